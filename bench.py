@@ -1,0 +1,232 @@
+"""Benchmark of the weight-only 4-bit dequantize-and-multiply hot path on one MI355X.
+
+Headline line: the decode GEMV (affine INT4 group 32, M=1, K=4096, N=14336),
+one step = one qmv_affine4 launch; value = weight bytes streamed per second.
+Weight copies are rotated (>= 512 MiB in total) so the 256 MB Infinity Cache
+cannot serve them. The same JSON line carries the other kernels of the path,
+each timed over its own back-to-back launches: the prefill GEMM (M=2048,
+K=N=4096, TFLOP/s), the lookup-codebook GEMM (M=512, K=4096, N=11008) and the
+expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8), each
+with its roofline fraction, plus the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
+MALL_BYTES = 256 * 2**20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="time one kernel only: decode|prefill|lut|moe")
+    return ap.parse_args()
+
+
+def rotation(bytes_per_copy: int, min_total: int = 512 * 2**20) -> int:
+    return max(2, -(-min_total // bytes_per_copy))
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def run(self, launch, steps: int, warmup: int) -> float:
+        torch = self.torch
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(self.stream)
+        for i in range(steps):
+            launch(i)
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps  # ms per launch
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not part of it", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from weight_only_bit_w4_amd import binding as B
+    from weight_only_bit_w4_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    B.lib()  # fail loudly before anything else if the library is missing
+    dev = "cuda"
+    timer = Timer(torch)
+    steps, warmup = args.steps, args.warmup
+
+    def to_dev(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(dtype) if dtype is not None else t).to(dev)
+
+    result = {}
+
+    # ------------------------------------------------------------ decode GEMV (headline)
+    c2 = synth.decode_affine()
+    M, K, N = c2["M"], c2["K"], c2["N"]
+    wbytes2 = N * K // 2 + 2 * (N * K // 32) * 2
+    ncopy = rotation(wbytes2)
+    ws = [to_dev(c2["w"].view(np.int32))]
+    ss = [to_dev(c2["scales"].view(np.int16), torch.bfloat16)]
+    bs = [to_dev(c2["biases"].view(np.int16), torch.bfloat16)]
+    for _ in range(ncopy - 1):
+        ws.append(ws[0].clone()); ss.append(ss[0].clone()); bs.append(bs[0].clone())
+    x2 = to_dev(c2["x"].view(np.int16), torch.bfloat16)
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def decode_step(i):
+        j = i % ncopy
+        B.qmv_affine4(ws[j], ss[j], bs[j], x2, y2)
+
+    if args.only in (None, "decode"):
+        ms = timer.run(decode_step, steps, warmup)
+        gbs = wbytes2 / (ms * 1e-3) / 1e9
+        result["decode"] = {"ms": ms, "GBps": gbs, "weight_bytes": wbytes2, "copies": ncopy}
+    del ws, ss, bs
+
+    # ------------------------------------------------------------ prefill GEMM
+    if args.only in (None, "prefill"):
+        c3 = synth.prefill_affine()
+        M3, K3, N3 = c3["M"], c3["K"], c3["N"]
+        w3 = to_dev(c3["w"].view(np.int32))
+        s3 = to_dev(c3["scales"].view(np.int16), torch.bfloat16)
+        b3 = to_dev(c3["biases"].view(np.int16), torch.bfloat16)
+        x3 = to_dev(c3["x"].view(np.int16), torch.bfloat16)
+        y3 = torch.empty((M3, N3), dtype=torch.bfloat16, device=dev)
+        n3 = max(20, steps // 20)
+        ms = timer.run(lambda i: B.qmm_affine4(w3, s3, b3, x3, y3), n3, max(5, warmup // 5))
+        flops = 2.0 * M3 * N3 * K3
+        result["prefill"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "flops": flops, "launches": n3}
+        del w3, s3, b3, x3, y3
+
+    # ------------------------------------------------------------ lookup-codebook GEMM
+    if args.only in (None, "lut"):
+        c4 = synth.lut_matmul_case()
+        M4, K4, N4, blk = c4["M"], c4["K"], c4["N"], c4["block"]
+        x4 = to_dev(c4["x"].view(np.int16), torch.float16)
+        p4 = to_dev(c4["packed"])
+        s4 = to_dev(c4["scales"].view(np.int16), torch.float16)
+        y4 = torch.empty((M4, N4), dtype=torch.float16, device=dev)
+        n4 = max(20, steps // 20)
+        ms = timer.run(lambda i: B.qmm_lut4(x4, p4, s4, c4["book"], N4, blk, y=y4), n4, max(5, warmup // 5))
+        flops = 2.0 * M4 * N4 * K4
+        result["lut"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "flops": flops, "launches": n4}
+        del x4, p4, s4, y4
+
+    # ------------------------------------------------------------ expert-routed Q4_0
+    if args.only in (None, "moe"):
+        c5 = synth.moe_q4_0_case()
+        E, N5, K5, T, top_k = c5["n_experts"], c5["N"], c5["K"], c5["n_tokens"], c5["top_k"]
+        wbytes5 = c5["w"].size
+        ncopy5 = rotation(wbytes5)
+        w5 = [to_dev(c5["w"])]
+        for _ in range(ncopy5 - 1):
+            w5.append(w5[0].clone())
+        x5 = to_dev(c5["x"])
+        ids5 = to_dev(c5["ids"].view(np.int32))
+        out5 = torch.empty((T * top_k, N5), dtype=torch.float32, device=dev)
+        scratch5 = torch.empty(B.qmm_id_q4_0_scratch_bytes(E, T, top_k, K5), dtype=torch.uint8, device=dev)
+        n5 = max(50, steps // 4)
+        ms = timer.run(lambda i: B.qmm_id_q4_0(x5, w5[i % ncopy5], ids5, T, top_k, N5, K5, E, c5["expert_stride"],
+                                               out=out5, scratch=scratch5), n5, max(5, warmup // 2))
+        result["moe"] = {"ms": ms, "GBps": wbytes5 / (ms * 1e-3) / 1e9, "weight_bytes": int(wbytes5),
+                         "flops": 2.0 * T * top_k * N5 * K5, "copies": ncopy5, "launches": n5}
+        del w5, x5, ids5, out5, scratch5
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu and args.only in (None, "decode"):
+        import oracle
+        c = c2
+        oracle.affine(c["w"], c["scales"], c["biases"], c["x"], 1, K, N)  # warm (build, page-in)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.affine(c["w"], c["scales"], c["biases"], c["x"], 1, K, N)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 10.0 or reps >= 200:
+                break
+        cpu = {"value": round(wbytes2 * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+               "kind": "oracle",
+               "sample": f"{reps} full decode GEMVs (M=1, K={K}, N={N}) in {el:.1f} s, weight bytes per second"}
+
+    # ------------------------------------------------------------ report
+    out = {
+        "metric": "W4 qmm TFLOP/s (prefill) + weight GB/s (decode GEMV), % of MI355X roofline",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws, the decode GEMV workload's distributions)",
+    }
+    if "decode" in result:
+        d = result["decode"]
+        out.update({
+            "value": round(d["GBps"], 2),
+            "unit": "GB/s",
+            "ms_per_step": round(d["ms"], 6),
+            "config": {"workload": "decode GEMV, affine INT4 group 32: x bf16 [1, 4096] . W[14336, 4096]^T",
+                       "M": 1, "K": K, "N": N, "group_size": 32, "weight_copies_rotated": d["copies"]},
+            "roofline": {"bound": "hbm", "achieved": round(d["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+        })
+    comps = {}
+    if "prefill" in result:
+        p = result["prefill"]
+        comps["prefill_gemm"] = {
+            "workload": "qmm_affine4 M=2048 K=4096 N=4096", "ms": round(p["ms"], 5),
+            "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(p["TFLOPs"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+    if "lut" in result:
+        p = result["lut"]
+        comps["lut_gemm"] = {
+            "workload": "qmm_lut4 M=512 K=4096 N=11008 block 64", "ms": round(p["ms"], 5),
+            "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(p["TFLOPs"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+    if "moe" in result:
+        p = result["moe"]
+        comps["moe_q4_0"] = {
+            "workload": "qmm_id_q4_0 E=64 N=1408 K=2048 tokens=128 top_k=8 (group + grouped GEMM)",
+            "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": None}}
+    if comps:
+        out["components"] = comps
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * w4mi - weight-only 4-bit dequantize-and-multiply, y = x . dequant(W)^T,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument named as "device" is a device pointer the
+ * caller owns (a hipMalloc'd buffer, e.g. a torch-ROCm tensor's data_ptr);
+ * "host" pointers are read during the call only. All tensors are dense and
+ * row-major. Every entry point validates its arguments on the host before it
+ * touches the GPU, enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without synchronising; the library never
+ * allocates device memory. On failure nothing is enqueued (W4_EINVAL,
+ * W4_EUNSUPPORTED) or the launch error is reported (W4_ELAUNCH); the message
+ * is available from w4_last_error() on the calling thread. There is no
+ * fallback path: a status other than W4_OK means no result was produced.
+ *
+ * Sources of each operation:
+ *   [P1] onnxruntime-ep-mlx 0.27.4, src/ops/quant_fastkernel.rs: INT4
+ *        group-32 affine MatMulNBits (module doc "Algorithm", the kernel's
+ *        W load, `eligible`, the tests' make_case);
+ *   [P2] onnxruntime-ep-mlx 0.31.1, src/ops/lut4.rs: frozen 16-entry lookup
+ *        decode (LookupMatMul, the decode kernel, rounded_weight, execute);
+ *   [P3] mlx-native 0.9.0, src/ops/quantized_matmul_id_ggml.rs:
+ *        expert-routed GGML block matmul (module doc,
+ *        quantized_matmul_id_ggml validation, IdMmScratch, the map0 + mm
+ *        two-stage dispatch).
+ */
+#ifndef W4MI_H
+#define W4MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4_OK = 0,
+    W4_EINVAL = 1,       /* an argument violates the operation's contract */
+    W4_EUNSUPPORTED = 2, /* a valid request this library does not implement */
+    W4_ELAUNCH = 3       /* the HIP runtime rejected a launch */
+} w4_status;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* w4_last_error(void);
+
+/* Library version string. */
+const char* w4_version(void);
+
+/* ------------------------------------------------------------------------
+ * Affine INT4, group size 32 [P1].
+ *
+ * w       device uint32 [N, K/8]: the weight at (n, k) is nibble k % 8 of
+ *         word (n, k / 8), least significant nibble first (bits 4j..4j+3).
+ * scales  device bf16 bits [N, K/32]; biases device bf16 bits [N, K/32],
+ *         bias = -zero_point * scale. Weight w[n][k] = q * scale + bias of
+ *         group k / 32.
+ * x       device bf16 bits [M, K]; y device bf16 bits [M, N] (written).
+ * Contract: bits == 4, group_size == 32, K % 32 == 0, N % 32 == 0, K > 0,
+ * N > 0 ([P1] `eligible`). M == 0 is a no-op. Accumulation is f32; y is the
+ * round-to-nearest-even bf16 of the accumulator.
+ *
+ * qmm_affine4 is the prefill form and requires M > 1 ([P1] `eligible`:
+ * the kernel is only used for M > 1). qmv_affine4 is the decode GEMV and
+ * requires M == 1 ([P1]: single-row decode takes the library qmv path).
+ * ---------------------------------------------------------------------- */
+w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
+                      int32_t group_size, int32_t bits, void* stream);
+
+w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
+                      int32_t group_size, int32_t bits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Lookup-codebook 4-bit matmul [P2], half-precision path.
+ *
+ * The decoded weight is the [rows, cols] matrix with flat index i: its code
+ * is the HIGH nibble of packed[i / 2] when i is even and the LOW nibble when
+ * i is odd, and value(i) = fp16(book[code] * scale[i / block]) (the product
+ * in f32, rounded to binary16 because the graph casts the decoded weight to
+ * half before the MatMul). With transpose != 0 the weight is [N, K]
+ * (rows = N, cols = K) and y = x . W^T.
+ *
+ * x       device fp16 bits [M, K]; y device fp16 bits [M, N] (written).
+ * packed  device uint8 [ceil(N*K/block) * block / 2].
+ * scales  device fp16 bits [ceil(N*K/block)].
+ * book    HOST pointer to 16 f32 codebook values (copied at the call).
+ * Contract: M >= 0, K > 0, N > 0, block > 0 and even ([P2] recognize).
+ * This library implements transpose != 0 with K % 32 == 0, K % block == 0 and
+ * block % 8 == 0; other valid shapes return W4_EUNSUPPORTED. M == 0 is a no-op.
+ * Accumulation is f32; y is the round-to-nearest-even fp16 of it.
+ * ---------------------------------------------------------------------- */
+w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
+                   const float* book, uint16_t* y, int64_t M, int64_t K, int64_t N,
+                   int32_t block, int32_t transpose, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-routed matmul over GGML Q4_0 blocks [P3].
+ *
+ * For every routed row r = token * top_k + slot, e = ids[r] and
+ *   out[r][n] = sum_k dequant(W[e][n][k]) * x[token][k].
+ * A Q4_0 block holds 32 consecutive k of one weight row in 18 bytes: a
+ * little-endian binary16 scale d, then 16 bytes qs; element i < 16 is the
+ * low nibble of qs[i], element i + 16 its high nibble; value = (q - 8) * d.
+ * Expert e's [N, K/32] blocks start at byte e * expert_stride of w.
+ *
+ * x       device f32 [n_tokens, K] (one row per token, shared by its slots).
+ * w       device bytes, at least n_experts * N * (K/32) * 18 long.
+ * ids     device uint32 [n_tokens * top_k].
+ * out     device f32 [n_tokens * top_k, N] (written).
+ * scratch device buffer of at least qmm_id_q4_0_scratch_bytes(...) bytes; the
+ *         call groups the routed rows by expert into it (and stores x as
+ *         binary16 there) before the grouped GEMM reads it ([P3] map0 + mm,
+ *         caller-owned scratch as in IdMmScratch). Its contents need no
+ *         initialisation. Calls that share one scratch buffer must be ordered
+ *         (same stream). The binary16 copy of x bounds |x| by 65504.
+ * Contract ([P3] quantized_matmul_id_ggml): n_tokens, K, N, top_k and
+ * n_experts > 0; K % 32 == 0; expert_stride >= N * (K/32) * 18; each byte
+ * length in p at least what the shapes need. Ids must be < n_experts: a row
+ * whose id is not is written as zeros, and the number of such rows is left
+ * as a uint32 at byte offset W4_ID_SCRATCH_BAD_IDS of scratch.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    uint32_t n_tokens;      /* input tokens */
+    uint32_t top_k;         /* experts per token */
+    uint32_t n;             /* output columns = weight rows per expert */
+    uint32_t k;             /* reduction length, multiple of 32 */
+    uint32_t n_experts;     /* experts in the stacked weight buffer */
+    uint32_t reserved;      /* must be 0 */
+    uint64_t expert_stride; /* bytes between consecutive experts' weights */
+    uint64_t x_bytes;       /* byte length of x */
+    uint64_t w_bytes;       /* byte length of w */
+    uint64_t ids_bytes;     /* byte length of ids */
+    uint64_t out_bytes;     /* byte length of out */
+} w4_id_params;
+
+#define W4_ID_SCRATCH_BAD_IDS 0
+
+/* Scratch bytes qmm_id_q4_0 needs: the per-expert row grouping and a copy of
+ * x in the matrix-core operand type (binary16). */
+size_t qmm_id_q4_0_scratch_bytes(uint32_t n_experts, uint32_t n_tokens, uint32_t top_k, uint32_t k);
+
+w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_t* ids, float* out,
+                      const w4_id_params* p, void* scratch, size_t scratch_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host-only argument checks: the exact validation the entry points above
+ * run before launching (no device access; callable without a GPU).
+ * decode != 0 checks the qmv_affine4 contract, else qmm_affine4's.
+ * ---------------------------------------------------------------------- */
+w4_status w4_check_affine(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t bits,
+                          int32_t decode);
+w4_status w4_check_lut(int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose);
+w4_status w4_check_id(const w4_id_params* p, size_t scratch_bytes);
+
+/* ------------------------------------------------------------------------
+ * Unpack exports: the codes the hot kernels decode, written out one byte
+ * per weight by the same device decode routines the kernels use, so that a
+ * caller can check them bit for bit. All pointers are device pointers.
+ *   w4_unpack_affine: q [N, K] from w [N, K/8] ([P1] nibble order).
+ *   w4_unpack_lut:    codes [count] from packed ([P2] high nibble first).
+ *   w4_unpack_q4_0:   q [rows, K] codes and d [rows, K/32] binary16 bits
+ *                     from `rows` consecutive Q4_0 weight rows.
+ * ---------------------------------------------------------------------- */
+w4_status w4_unpack_affine(const uint32_t* w, uint8_t* q, int64_t N, int64_t K, void* stream);
+w4_status w4_unpack_lut(const uint8_t* packed, uint8_t* codes, int64_t count, void* stream);
+w4_status w4_unpack_q4_0(const uint8_t* w, uint8_t* q, uint16_t* d, int64_t rows, int64_t K,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4MI_H */

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol include/w4mi.h declares, and its argument contracts reject what the
+pages' validation rejects, before any device work."""
+import os
+import re
+
+import pytest
+
+from weight_only_bit_w4_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4mi.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(B.LIB_PATH):
+        from weight_only_bit_w4_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([A-Za-z_]\w*)\s*\(", text)) - {"if", "sizeof", "return"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"qmm_affine4", "qmv_affine4", "qmm_lut4", "qmm_id_q4_0"} <= set(names)
+    lib = B.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in B.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version():
+    assert "gfx950" in B.version()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((4, 256, 256, 32, 4, 0), B.W4_OK, ""),
+    ((1, 4096, 14336, 32, 4, 1), B.W4_OK, ""),
+    ((0, 64, 64, 32, 4, 0), B.W4_OK, ""),
+    ((1, 256, 256, 32, 4, 0), B.W4_EINVAL, "M > 1"),          # prefill kernel is M > 1 only
+    ((2, 256, 256, 32, 4, 1), B.W4_EINVAL, "M == 1"),         # decode GEMV is M == 1 only
+    ((4, 256, 256, 64, 4, 0), B.W4_EINVAL, "group_size"),
+    ((4, 256, 256, 32, 8, 0), B.W4_EINVAL, "bits"),
+    ((4, 250, 256, 32, 4, 0), B.W4_EINVAL, "K (250)"),
+    ((4, 256, 250, 32, 4, 0), B.W4_EINVAL, "N (250)"),
+    ((4, 0, 256, 32, 4, 0), B.W4_EINVAL, "K, N > 0"),
+    ((-1, 64, 64, 32, 4, 0), B.W4_EINVAL, "M >= 0"),
+])
+def test_affine_contract(args, status, needle):
+    assert B.w4_check_affine(*args) == status
+    if status != B.W4_OK:
+        assert needle in B.last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((512, 4096, 11008, 64, 1), B.W4_OK),
+    ((0, 4096, 11008, 64, 1), B.W4_OK),
+    ((5, 128, 48, 63, 1), B.W4_EINVAL),          # block must be even
+    ((5, 128, 48, 0, 1), B.W4_EINVAL),
+    ((5, 0, 48, 64, 1), B.W4_EINVAL),
+    ((5, 128, 48, 64, 0), B.W4_EUNSUPPORTED),    # non-transposed layout
+    ((5, 96, 48, 64, 1), B.W4_EUNSUPPORTED),     # K not a multiple of the block
+    ((5, 128, 48, 2, 1), B.W4_EUNSUPPORTED),     # block not a multiple of 8
+])
+def test_lut_contract(args, status):
+    assert B.w4_check_lut(*args) == status
+
+
+def _params(**kw):
+    base = dict(n_tokens=128, top_k=8, n=1408, k=2048, n_experts=64, expert_stride=1408 * 64 * 18)
+    base.update(kw)
+    rows = base["n_tokens"] * base["top_k"]
+    p = B.IdParams(base["n_tokens"], base["top_k"], base["n"], base["k"], base["n_experts"], 0,
+                   base["expert_stride"], base["n_tokens"] * base["k"] * 4,
+                   base["n_experts"] * base["expert_stride"], rows * 4, rows * base["n"] * 4)
+    for f in ("x_bytes", "w_bytes", "ids_bytes", "out_bytes", "reserved"):
+        if f in kw:
+            setattr(p, f, kw[f])
+    return p, B.qmm_id_q4_0_scratch_bytes(base["n_experts"], base["n_tokens"], base["top_k"], base["k"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    ({}, B.W4_OK, ""),
+    ({"n_tokens": 0}, B.W4_EINVAL, "must all be > 0"),
+    ({"top_k": 0}, B.W4_EINVAL, "top_k"),
+    ({"n_experts": 0}, B.W4_EINVAL, "n_experts"),
+    ({"k": 2047}, B.W4_EINVAL, "divisible"),
+    ({"expert_stride": 1000}, B.W4_EINVAL, "expert_stride"),
+    ({"x_bytes": 16}, B.W4_EINVAL, "input buffer too small"),
+    ({"w_bytes": 1}, B.W4_EINVAL, "weight buffer too small"),
+    ({"ids_bytes": 4}, B.W4_EINVAL, "ids buffer too small"),
+    ({"out_bytes": 4}, B.W4_EINVAL, "output buffer too small"),
+    ({"reserved": 1}, B.W4_EINVAL, "reserved"),
+])
+def test_id_contract(kw, status, needle):
+    p, scratch = _params(**kw)
+    assert B.w4_check_id(p, scratch) == status
+    if status != B.W4_OK:
+        assert needle in B.last_error()
+
+
+def test_id_scratch_too_small():
+    p, scratch = _params()
+    assert B.w4_check_id(p, scratch - 1) == B.W4_EINVAL
+    assert "scratch" in B.last_error()
+
+
+def test_id_stride_padding_counts_last_expert_only():
+    # the last expert's slab need not be padded to the full stride
+    p, scratch = _params(expert_stride=1408 * 64 * 18 + 64)
+    p.w_bytes = 63 * (1408 * 64 * 18 + 64) + 1408 * 64 * 18
+    assert B.w4_check_id(p, scratch) == B.W4_OK
+    p.w_bytes -= 1
+    assert B.w4_check_id(p, scratch) == B.W4_EINVAL

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP library against the CPU oracle on identical seeded inputs.
+
+Bar: unpacked nibbles / codebook indices / Q4_0 codes and scales bit-exact;
+outputs within |y - ref| <= 1e-2 |ref| + 1e-2 sqrt(K) max|x| max|scale|, with
+ref the oracle's fp64 accumulator. Small shapes are compared element by
+element (spanning several tiles and ragged tails); the full-size workloads in
+the launch configuration the benchmark times are compared at sampled outputs
+the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from weight_only_bit_w4_amd import binding as B
+from weight_only_bit_w4_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _t(a: np.ndarray, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def _affine_dev(c):
+    return (_t(c["w"].view(np.int32)), _t(c["scales"].view(np.int16), torch.bfloat16),
+            _t(c["biases"].view(np.int16), torch.bfloat16), _t(c["x"].view(np.int16), torch.bfloat16))
+
+
+def _bf16_to_f64(y: torch.Tensor) -> np.ndarray:
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def _assert_within(got, ref, K, max_x, max_s, what):
+    tol = oracle.tolerance(ref, K, max_x, max_s)
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst err {err.max():.3g} "
+                           f"(tol there {tol.reshape(-1)[np.argmax(err)]:.3g})")
+
+
+def _affine_scales(c):
+    return float(np.abs(oracle.bf16_to_f32(c["scales"])).max()), float(np.abs(oracle.bf16_to_f32(c["x"])).max())
+
+
+# ---------------------------------------------------------------- unpack, bit-exact
+@pytest.mark.parametrize("N,K", [(256, 256), (96, 40), (14336, 4096)])
+def test_unpack_affine_bit_exact(N, K):
+    c = synth.affine_case(1, K, N, seed=11)
+    q = B.w4_unpack_affine(_t(c["w"].view(np.int32)), N, K).cpu().numpy()
+    assert np.array_equal(q, oracle.unpack_affine(c["w"], N, K))
+
+
+@pytest.mark.parametrize("N,K", [(48, 128), (11008, 4096)])
+def test_unpack_lut_bit_exact(N, K):
+    c = synth.lut_case(1, K, N, seed=12)
+    codes = B.w4_unpack_lut(_t(c["packed"]), N * K).cpu().numpy()
+    assert np.array_equal(codes, oracle.unpack_lut(c["packed"], N * K))
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 20, 128), (64, 1408, 2048)])
+def test_unpack_q4_0_bit_exact(E, N, K):
+    c = synth.moe_case(E, N, K, 1, 1, seed=13)
+    q, d = B.w4_unpack_q4_0(_t(c["w"]), E * N, K)
+    q_ref, d_ref = oracle.unpack_q4_0(c["w"], E * N, K)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(oracle.f16_to_f32(d.cpu().numpy().view(np.uint16)), d_ref)
+
+
+# ---------------------------------------------------------------- decode GEMV
+@pytest.mark.parametrize("K,N,seed", [
+    (256, 256, 0),        # the tiny workload's weights, one row of x
+    (96, 64, 1),          # fewer groups than lanes
+    (4096 + 32, 96, 2),   # a ragged second chunk of groups
+    (10240, 64, 3),       # more chunks than the unrolled forms (runtime loop)
+    (4096, 14336, 0),     # the decode workload at full size
+])
+def test_qmv_affine4(K, N, seed):
+    c = synth.affine_case(1, K, N, seed=seed)
+    w, s, b, x = _affine_dev(c)
+    y = B.qmv_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], 1, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"qmv K={K} N={N}")
+
+
+# ---------------------------------------------------------------- prefill GEMM
+@pytest.mark.parametrize("M,K,N", [
+    (4, 256, 256),                        # the tiny workload
+    (32, 32, 32), (4, 32, 32), (7, 64, 64), (64, 32, 32), (64, 128, 256), (100, 256, 512),  # page's test shapes
+    (300, 160, 224),                      # ragged M, N not a multiple of the 128 tile
+    (65, 96, 160),                        # just past the small-M tile
+])
+def test_qmm_affine4_small(M, K, N):
+    c = synth.affine_case(M, K, N, seed=M + K + N)
+    w, s, b, x = _affine_dev(c)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"qmm M={M} K={K} N={N}")
+
+
+def _sample_points(M, N, count, seed, tile_m=256, tile_n=128):
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, count)
+    ns = rng.integers(0, N, count)
+    corners_m = np.array([0, M - 1, tile_m - 1, tile_m, min(M - 1, 2 * tile_m + 17)])
+    corners_n = np.array([0, N - 1, tile_n - 1, tile_n, min(N - 1, 3 * tile_n + 5)])
+    cm, cn = np.meshgrid(corners_m, corners_n)
+    return np.concatenate([ms, cm.reshape(-1)]), np.concatenate([ns, cn.reshape(-1)])
+
+
+def test_qmm_affine4_prefill_full_size_sampled():
+    c = synth.prefill_affine()
+    M, K, N = c["M"], c["K"], c["N"]
+    w, s, b, x = _affine_dev(c)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    ms, ns = _sample_points(M, N, 3000, seed=21)
+    acc, _ = oracle.affine_points(c["w"], c["scales"], c["biases"], c["x"], K, ms, ns)
+    got = _bf16_to_f64(y)[ms, ns]
+    msc, mx = _affine_scales(c)
+    _assert_within(got, acc, K, mx, msc, "qmm prefill sampled")
+    assert torch.isfinite(y.float()).all()
+
+
+def test_affine_m_zero_is_noop():
+    c = synth.affine_case(2, 64, 32, seed=5)
+    w, s, b, _ = _affine_dev(c)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    y = B.qmm_affine4(w, s, b, x)
+    assert y.shape == (0, 32)
+
+
+# ---------------------------------------------------------------- lookup codebook
+def _lut_dev(c):
+    return _t(c["x"].view(np.int16), torch.float16), _t(c["packed"]), _t(c["scales"].view(np.int16), torch.float16)
+
+
+@pytest.mark.parametrize("M,K,N,block", [(5, 128, 48, 64), (70, 256, 200, 64), (300, 64, 130, 32), (3, 64, 16, 8)])
+def test_qmm_lut4_small(M, K, N, block):
+    c = synth.lut_case(M, K, N, seed=M + N, block=block)
+    x, p, s = _lut_dev(c)
+    y = B.qmm_lut4(x, p, s, c["book"], N, block)
+    torch.cuda.synchronize()
+    acc, _ = oracle.lut4(c["x"], c["packed"], c["scales"], c["book"], M, K, N, block)
+    got = y.float().cpu().numpy().astype(np.float64)
+    _assert_within(got, acc, K, float(np.abs(oracle.f16_to_f32(c["x"])).max()),
+                   float(np.abs(oracle.f16_to_f32(c["scales"])).max()), f"lut M={M} K={K} N={N}")
+
+
+def test_qmm_lut4_full_size_sampled():
+    c = synth.lut_matmul_case()
+    M, K, N, block = c["M"], c["K"], c["N"], c["block"]
+    x, p, s = _lut_dev(c)
+    y = B.qmm_lut4(x, p, s, c["book"], N, block)
+    torch.cuda.synchronize()
+    ms, ns = _sample_points(M, N, 3000, seed=22)
+    acc = oracle.lut4_points(c["x"], c["packed"], c["scales"], c["book"], K, block, ms, ns)
+    got = y.float().cpu().numpy().astype(np.float64)[ms, ns]
+    _assert_within(got, acc, K, float(np.abs(oracle.f16_to_f32(c["x"])).max()),
+                   float(np.abs(oracle.f16_to_f32(c["scales"])).max()), "lut full sampled")
+
+
+# ---------------------------------------------------------------- expert-routed Q4_0
+def _moe_run(c, ids=None):
+    ids = c["ids"] if ids is None else ids
+    x, w, idt = _t(c["x"]), _t(c["w"]), _t(ids.view(np.int32))
+    scratch = torch.empty(B.qmm_id_q4_0_scratch_bytes(c["n_experts"], c["n_tokens"], c["top_k"], c["K"]),
+                          dtype=torch.uint8, device=DEV)
+    out = B.qmm_id_q4_0(x, w, idt, c["n_tokens"], c["top_k"], c["N"], c["K"], c["n_experts"], c["expert_stride"],
+                        scratch=scratch)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), scratch
+
+
+def _max_d(c):
+    E, N, K = c["n_experts"], c["N"], c["K"]
+    _, d = oracle.unpack_q4_0(c["w"], E * N, K)
+    return float(np.abs(d).max())
+
+
+@pytest.mark.parametrize("E,N,K,T,top_k", [
+    (4, 40, 128, 3, 2),      # tiny, N not a multiple of the 128-row tile
+    (2, 64, 64, 100, 2),     # 100 routed rows per expert: two passes of 64
+    (8, 200, 320, 9, 3),     # K not a multiple of the 256 window
+])
+def test_qmm_id_q4_0_small(E, N, K, T, top_k):
+    c = synth.moe_case(E, N, K, T, top_k, seed=E + N + T)
+    got, scratch = _moe_run(c)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], T, top_k, N, K, E, c["expert_stride"])
+    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(c), f"moe E={E} N={N} K={K}")
+    assert scratch[:4].view(torch.int32).item() == 0
+
+
+def test_qmm_id_q4_0_duplicate_and_out_of_range_ids():
+    c = synth.moe_case(4, 32, 64, 5, 3, seed=31)
+    ids = c["ids"].copy()
+    ids[1] = ids[0]          # the same expert twice for token 0
+    ids[4] = 9               # no such expert
+    ids[10] = 0xFFFFFFFF
+    got, scratch = _moe_run(c, ids)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], ids, 5, 3, 32, 64, 4, c["expert_stride"])
+    _assert_within(got, acc, 64, float(np.abs(c["x"]).max()), _max_d(c), "moe odd ids")
+    assert np.all(got[4] == 0) and np.all(got[10] == 0)
+    assert scratch[:4].view(torch.int32).item() == 2
+
+
+def test_qmm_id_q4_0_full_size_sampled():
+    c = synth.moe_q4_0_case()
+    got, scratch = _moe_run(c)
+    rng = np.random.default_rng(23)
+    rows = c["n_tokens"] * c["top_k"]
+    rs = np.concatenate([rng.integers(0, rows, 3000), [0, rows - 1]])
+    ns = np.concatenate([rng.integers(0, c["N"], 3000), [c["N"] - 1, 0]])
+    acc = oracle.moe_q4_0_points(c["x"], c["w"], c["ids"], c["top_k"], c["K"], c["n_experts"], c["expert_stride"],
+                                 rs, ns)
+    _assert_within(got[rs, ns], acc, c["K"], float(np.abs(c["x"]).max()), _max_d(c), "moe full sampled")
+    assert np.isfinite(got).all()

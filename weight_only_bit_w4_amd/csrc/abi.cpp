@@ -1,0 +1,148 @@
+// Host-side part of the C ABI: error reporting and the argument contracts
+// each entry point checks before it enqueues work.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "w4mi_host.hpp"
+
+namespace w4mi {
+
+static thread_local std::string g_error;
+
+w4_status fail(w4_status status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return status;
+}
+
+void clear_error() { g_error.clear(); }
+
+w4_status launch_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(W4_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    clear_error();
+    return W4_OK;
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+IdScratchLayout id_scratch_layout(uint32_t n_experts, uint32_t n_tokens, uint32_t top_k, uint32_t k) {
+    IdScratchLayout l;
+    size_t off = 0;
+    l.bad_ids = off;
+    off = align_up(off + 4, 256);
+    l.counts = off;
+    off = align_up(off + 4ull * n_experts, 256);
+    l.offsets = off;
+    off = align_up(off + 4ull * (n_experts + 1ull), 256);
+    l.rows = off;
+    off = align_up(off + 4ull * n_tokens * top_k, 256);
+    l.xh = off;
+    off = align_up(off + 2ull * n_tokens * k, 256);
+    l.total = off;
+    return l;
+}
+
+}  // namespace w4mi
+
+using namespace w4mi;
+
+extern "C" {
+
+const char* w4_last_error(void) { return g_error.c_str(); }
+
+const char* w4_version(void) { return "w4mi 0.1 (gfx950)"; }
+
+// INT4 MatMulNBits page, `eligible`: bits 4, group size 32, M > 1 for the
+// prefill kernel, K and N multiples of 32; single-row decode is the GEMV.
+w4_status w4_check_affine(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t bits,
+                          int32_t decode) {
+    const char* fn = decode ? "qmv_affine4" : "qmm_affine4";
+    if (bits != 4) return fail(W4_EINVAL, "%s: bits must be 4, got %d", fn, bits);
+    if (group_size != 32) return fail(W4_EINVAL, "%s: group_size must be 32, got %d", fn, group_size);
+    if (M < 0 || K <= 0 || N <= 0)
+        return fail(W4_EINVAL, "%s: need M >= 0 and K, N > 0 (M=%lld K=%lld N=%lld)", fn, (long long)M,
+                    (long long)K, (long long)N);
+    if (K % 32 != 0) return fail(W4_EINVAL, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+    if (N % 32 != 0) return fail(W4_EINVAL, "%s: N (%lld) must be a multiple of 32", fn, (long long)N);
+    if (M > INT32_MAX || K > INT32_MAX || N > INT32_MAX)
+        return fail(W4_EINVAL, "%s: each dimension must fit in int32", fn);
+    if (decode && M > 1) return fail(W4_EINVAL, "%s: the decode GEMV takes M == 1, got %lld", fn, (long long)M);
+    if (!decode && M == 1)
+        return fail(W4_EINVAL, "%s: the prefill GEMM takes M > 1; use qmv_affine4 for M == 1", fn);
+    clear_error();
+    return W4_OK;
+}
+
+// lut4 page, recognize/execute: block positive and even; K and N positive; M
+// flattened. This library runs the transposed layout with whole blocks per
+// row segment of 8.
+w4_status w4_check_lut(int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose) {
+    if (M < 0 || K <= 0 || N <= 0)
+        return fail(W4_EINVAL, "qmm_lut4: need M >= 0 and K, N > 0 (M=%lld K=%lld N=%lld)", (long long)M,
+                    (long long)K, (long long)N);
+    if (block <= 0 || block % 2 != 0) return fail(W4_EINVAL, "qmm_lut4: block must be positive and even, got %d", block);
+    if (M > INT32_MAX || K > INT32_MAX || N > INT32_MAX || N * K > (int64_t)1 << 40)
+        return fail(W4_EINVAL, "qmm_lut4: dimensions too large");
+    if (!transpose) return fail(W4_EUNSUPPORTED, "qmm_lut4: only the transposed weight layout ([N, K]) is implemented");
+    if (K % 32 != 0 || K % block != 0 || block % 8 != 0)
+        return fail(W4_EUNSUPPORTED, "qmm_lut4: implemented for K %% 32 == 0, K %% block == 0, block %% 8 == 0 "
+                                     "(K=%lld block=%d)", (long long)K, block);
+    clear_error();
+    return W4_OK;
+}
+
+// mlx-native MoE page, quantized_matmul_id_ggml: every dimension positive,
+// K a multiple of the block size, expert stride and buffer lengths large
+// enough; plus the scratch the grouping needs.
+w4_status w4_check_id(const w4_id_params* p, size_t scratch_bytes) {
+    if (!p) return fail(W4_EINVAL, "qmm_id_q4_0: params is null");
+    if (p->n_tokens == 0 || p->k == 0 || p->n == 0)
+        return fail(W4_EINVAL, "qmm_id_q4_0: n_tokens, K, and N must all be > 0");
+    if (p->top_k == 0) return fail(W4_EINVAL, "qmm_id_q4_0: top_k must be > 0");
+    if (p->n_experts == 0) return fail(W4_EINVAL, "qmm_id_q4_0: n_experts must be > 0");
+    if (p->reserved != 0) return fail(W4_EINVAL, "qmm_id_q4_0: reserved field must be 0");
+    if (p->k % 32 != 0) return fail(W4_EINVAL, "qmm_id_q4_0: K (%u) must be divisible by block QK (32)", p->k);
+    const uint64_t row_bytes = (uint64_t)(p->k / 32) * 18u;
+    const uint64_t per_expert = (uint64_t)p->n * row_bytes;
+    if (p->expert_stride < per_expert)
+        return fail(W4_EINVAL, "qmm_id_q4_0: expert_stride (%llu) < per_expert_bytes (%llu)",
+                    (unsigned long long)p->expert_stride, (unsigned long long)per_expert);
+    const uint64_t need_x = (uint64_t)p->n_tokens * p->k * 4u;
+    if (p->x_bytes < need_x)
+        return fail(W4_EINVAL, "qmm_id_q4_0: input buffer too small: expected %llu bytes for [%u x %u] f32, got %llu",
+                    (unsigned long long)need_x, p->n_tokens, p->k, (unsigned long long)p->x_bytes);
+    const uint64_t need_w = (uint64_t)(p->n_experts - 1) * p->expert_stride + per_expert;
+    if (p->w_bytes < need_w)
+        return fail(W4_EINVAL, "qmm_id_q4_0: weight buffer too small: expected %llu bytes for %u experts, got %llu",
+                    (unsigned long long)need_w, p->n_experts, (unsigned long long)p->w_bytes);
+    const uint64_t rows = (uint64_t)p->n_tokens * p->top_k;
+    if (rows > INT32_MAX) return fail(W4_EINVAL, "qmm_id_q4_0: n_tokens * top_k must fit in int32");
+    if (p->ids_bytes < rows * 4u)
+        return fail(W4_EINVAL, "qmm_id_q4_0: ids buffer too small: expected %llu bytes for [%u * %u] u32, got %llu",
+                    (unsigned long long)(rows * 4u), p->n_tokens, p->top_k, (unsigned long long)p->ids_bytes);
+    if (p->out_bytes < rows * p->n * 4u)
+        return fail(W4_EINVAL, "qmm_id_q4_0: output buffer too small: expected %llu bytes for [%llu x %u] f32, got %llu",
+                    (unsigned long long)(rows * p->n * 4u), (unsigned long long)rows, p->n,
+                    (unsigned long long)p->out_bytes);
+    if (p->n_experts > kMaxExperts)
+        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: at most %u experts are supported, got %u", kMaxExperts,
+                    p->n_experts);
+    const size_t need_s = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k).total;
+    if (scratch_bytes < need_s)
+        return fail(W4_EINVAL, "qmm_id_q4_0: scratch too small: expected %zu bytes, got %zu", need_s, scratch_bytes);
+    clear_error();
+    return W4_OK;
+}
+
+size_t qmm_id_q4_0_scratch_bytes(uint32_t n_experts, uint32_t n_tokens, uint32_t top_k, uint32_t k) {
+    return id_scratch_layout(n_experts, n_tokens, top_k, k).total;
+}
+
+}  // extern "C"

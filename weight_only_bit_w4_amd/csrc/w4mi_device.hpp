@@ -1,0 +1,115 @@
+// Device-side building blocks shared by the w4mi kernels (gfx950 only).
+//
+// Operand types for the CDNA4 matrix cores, the 4-bit decode routines every
+// kernel and the unpack exports share, and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4mi {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+
+// Reinterpret a 32-bit value as a packed pair. Always pass a plain scalar:
+// hipcc (ROCm 7.2) mis-reads __builtin_bit_cast applied directly to a
+// vector-element expression such as v[e] (it reads element 0).
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// ---------------------------------------------------------------- 16-bit floats
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// Round-to-nearest-even narrowing (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 r;
+    r[0] = (_Float16)lo;
+    r[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// ---------------------------------------------------------------- 4-bit decode
+// Affine INT4 word (INT4 MatMulNBits page, kernel W load): eight weights
+// k0..k0+7 of one row, nibble j at bits 4j..4j+3 (least significant first).
+__device__ __forceinline__ uint32_t affine_nibble(uint32_t word, int j) { return (word >> (4 * j)) & 0xFu; }
+
+// Eight nibbles of an affine word as f32 values 0..15, in k order.
+__device__ __forceinline__ void affine_word_to_f32(uint32_t word, float (&q)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = (float)affine_nibble(word, j);
+}
+
+// Pair form used by the decode GEMV: bf16 pairs holding 128 + q for nibbles
+// (i, i + 4), i = 0..3, of an affine word. 128 + q (q <= 15) is exact in bf16
+// (8 significant bits), so a bf16 dot product with these pairs yields
+// sum (128 + q) x exactly up to f32 accumulation.
+__device__ __forceinline__ uint32_t affine_pair_biased_bf16(uint32_t word, int i) {
+    return ((word >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Lookup-codebook index order (lut4 page, decode kernel): flat index i uses
+// the HIGH nibble of byte i/2 when i is even, the LOW nibble when i is odd.
+__device__ __forceinline__ uint32_t lut_code(uint32_t byte, uint32_t i) {
+    return (i & 1u) ? (byte & 0xFu) : (byte >> 4);
+}
+
+// GGML Q4_0 block: element i < 16 is the low nibble of qs[i], element i + 16
+// its high nibble. From one qs dword (bytes 4i..4i+3 of a block) this yields
+// four fp16 pairs holding 1024 + q (exact in binary16) for the elements
+//   out[0] = (4i, 4i+1)  out[1] = (4i+2, 4i+3)     (low nibbles)
+//   out[2] = (16+4i, 16+4i+1)  out[3] = (16+4i+2, 16+4i+3)  (high nibbles).
+__device__ __forceinline__ void q4_0_biased_pairs(uint32_t qs, uint32_t (&out)[4]) {
+    const uint32_t t0 = __builtin_amdgcn_perm(0u, qs, 0x0C010C00u);  // [b0, 0, b1, 0]
+    const uint32_t t1 = __builtin_amdgcn_perm(0u, qs, 0x0C030C02u);  // [b2, 0, b3, 0]
+    out[0] = (t0 & 0x000F000Fu) | 0x64006400u;
+    out[1] = (t1 & 0x000F000Fu) | 0x64006400u;
+    out[2] = ((t0 >> 4) & 0x000F000Fu) | 0x64006400u;
+    out[3] = ((t1 >> 4) & 0x000F000Fu) | 0x64006400u;
+}
+
+// Two consecutive Q4_0 blocks (36 bytes, read as nine 4-byte-aligned dwords):
+// block A is bytes 0..17 (d at 0, qs at 2), block B bytes 18..35 (d at 18,
+// qs at 20). Returns both scales' binary16 bits and both qs as aligned dwords.
+__device__ __forceinline__ void q4_0_split_pair(const uint32_t (&raw)[9], uint32_t& dA, uint32_t& dB,
+                                                uint32_t (&qsA)[4], uint32_t (&qsB)[4]) {
+    dA = raw[0] & 0xFFFFu;
+    dB = raw[4] >> 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qsA[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], 2);
+        qsB[i] = raw[5 + i];
+    }
+}
+
+// ---------------------------------------------------------------- reductions
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+}  // namespace w4mi

@@ -1,0 +1,36 @@
+// Host-side helpers shared by the w4mi entry points: the per-thread error
+// message and the launch-status check.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "w4mi.h"
+
+namespace w4mi {
+
+// Records a formatted message for w4_last_error() and returns `status`.
+w4_status fail(w4_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Clears the thread's message (called on success paths).
+void clear_error();
+
+// Checks the HIP runtime's launch status after enqueuing `what`.
+w4_status launch_status(const char* what);
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Internal layout of the expert-routed scratch buffer (see qmm_id_q4_0).
+struct IdScratchLayout {
+    size_t bad_ids;   // uint32 count of rows with an out-of-range id
+    size_t counts;    // uint32 [n_experts] routed rows per expert
+    size_t offsets;   // uint32 [n_experts + 1] exclusive prefix of counts
+    size_t rows;      // uint32 [n_tokens * top_k] routed rows grouped by expert
+    size_t xh;        // binary16 [n_tokens, k] activations in the MFMA operand type
+    size_t total;
+};
+IdScratchLayout id_scratch_layout(uint32_t n_experts, uint32_t n_tokens, uint32_t top_k, uint32_t k);
+
+// Largest expert count the grouping kernel keeps in its LDS histogram.
+constexpr uint32_t kMaxExperts = 8192;
+
+}  // namespace w4mi
