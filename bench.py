@@ -1,21 +1,28 @@
 """Benchmark of the weight-only 4-bit dequantize-and-multiply hot path on one MI355X.
 
-Headline line: the decode GEMV (affine INT4 group 32, M=1, K=4096, N=14336),
-one step = one qmv_affine4 launch; value = weight bytes streamed per second.
-Weight copies are rotated (>= 512 MiB in total) so the 256 MB Infinity Cache
-cannot serve them. The same JSON line carries the other kernels of the path,
-each timed over its own back-to-back launches: the prefill GEMM (M=2048,
+Headline line: the decode GEMV (affine INT4 group 32, M=1, K=4096, N=14336);
+one step = one qmv_affine4 launch (unpack, dequantize, contract, round: every
+step of the affine path); value = weight bytes streamed per second. Weight
+copies are rotated (>= 512 MiB in total) so the 256 MB Infinity Cache cannot
+serve them. The same JSON line carries the other kernels of the path, each
+timed over its own back-to-back launches: the prefill GEMM (M=2048,
 K=N=4096, TFLOP/s), the lookup-codebook GEMM (M=512, K=4096, N=11008) and the
 expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8), each
 with its roofline fraction, plus the CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
+Launches are captured in HIP graphs (torch.cuda.CUDAGraph over the library's
+own launches on the capture stream) and replayed, so the host-side cost of a
+call does not pace the GPU; --eager launches them one by one instead (used
+under counter collection). Times come from HIP events recorded on the stream
+the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--only decode|prefill|lut|moe] [--eager] [--calib]
 """
 from __future__ import annotations
 
 import argparse
 import json
-import os
 import sys
 import time
 
@@ -23,7 +30,32 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
-MALL_BYTES = 256 * 2**20
+
+# HBM bytes per launch (FETCH_SIZE + WRITE_SIZE) from rocprofv3 --pmc runs of
+# `bench.py --eager --calib`, each counter scaled by what it reads for a plain
+# 256 MiB copy (torch.neg on f32: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0). Each entry
+# is tied to the digest of the kernel sources it was measured on and reported
+# as null once those sources change.
+TRAFFIC = {
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "0e052583f6af1883", 36936526 + 57344),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "7cf3295ab42b119c", 144938159 + 16777245),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "7cf3295ab42b119c", 81733607 + 11272192),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "a21fb044e54fa8a9", 113704439 + 5768419),
+}
+
+
+def traffic(name: str):
+    """Measured HBM bytes per launch of `name`, or None if its sources changed since."""
+    import hashlib
+    import os
+
+    sources, digest, nbytes = TRAFFIC[name]
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_bit_w4_amd", "csrc")
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(csrc, src), "rb") as f:
+            h.update(f.read())
+    return nbytes if h.hexdigest()[:16] == digest else None
 
 
 def parse():
@@ -32,7 +64,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, help="time one kernel only: decode|prefill|lut|moe")
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "moe"],
+                    help="time one kernel only")
+    ap.add_argument("--eager", action="store_true", help="launch one by one instead of replaying graphs")
+    ap.add_argument("--calib", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (counter calibration)")
     return ap.parse_args()
 
 
@@ -41,23 +77,54 @@ def rotation(bytes_per_copy: int, min_total: int = 512 * 2**20) -> int:
 
 
 class Timer:
-    """HIP events on the stream the kernels are launched on (torch's current stream)."""
+    """Times `steps` launches of launch(i) with HIP events on torch's current
+    stream (the stream the binding enqueues on), after `warmup` launches."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, eager: bool):
         self.torch = torch
-        self.stream = torch.cuda.current_stream()
+        self.eager = eager
 
-    def run(self, launch, steps: int, warmup: int) -> float:
+    def _graph(self, launch, first: int, count: int):
         torch = self.torch
-        for i in range(warmup):
-            launch(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(first, first + count):
+                launch(i)
+        return g
+
+    def run(self, launch, steps: int, warmup: int, chunk: int = 60) -> float:
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        if self.eager:
+            for i in range(warmup):
+                launch(i)
+            plan = None
+        else:
+            # Eager warm-up on a side stream (default priority), then capture.
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for i in range(3):
+                    launch(i)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            chunk = max(1, min(chunk, steps))
+            full = self._graph(launch, 0, chunk)
+            rest = self._graph(launch, 0, steps % chunk) if steps % chunk else None
+            plan = [full] * (steps // chunk) + ([rest] if rest is not None else [])
+            for _ in range(max(1, warmup // chunk)):
+                full.replay()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
-        start.record(self.stream)
-        for i in range(steps):
-            launch(i)
-        end.record(self.stream)
+        start.record(stream)
+        if plan is None:
+            for i in range(steps):
+                launch(i)
+        else:
+            for g in plan:
+                g.replay()
+        end.record(stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps  # ms per launch
 
@@ -65,8 +132,8 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not part of it", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU (got --gpus {args.gpus}); "
+              "sharding across GPUs is a design note, not part of this benchmark", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -78,37 +145,51 @@ def main():
         sys.exit(1)
     B.lib()  # fail loudly before anything else if the library is missing
     dev = "cuda"
-    timer = Timer(torch)
+    timer = Timer(torch, args.eager)
     steps, warmup = args.steps, args.warmup
 
     def to_dev(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
         return (t.view(dtype) if dtype is not None else t).to(dev)
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     result = {}
+
+    if args.calib:
+        a = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log("calibration copy: torch.neg over 256 MiB f32 (reads 268435456 B, writes 268435456 B), 5 launches")
+        del a, b
 
     # ------------------------------------------------------------ decode GEMV (headline)
     c2 = synth.decode_affine()
     M, K, N = c2["M"], c2["K"], c2["N"]
     wbytes2 = N * K // 2 + 2 * (N * K // 32) * 2
-    ncopy = rotation(wbytes2)
-    ws = [to_dev(c2["w"].view(np.int32))]
-    ss = [to_dev(c2["scales"].view(np.int16), torch.bfloat16)]
-    bs = [to_dev(c2["biases"].view(np.int16), torch.bfloat16)]
-    for _ in range(ncopy - 1):
-        ws.append(ws[0].clone()); ss.append(ss[0].clone()); bs.append(bs[0].clone())
-    x2 = to_dev(c2["x"].view(np.int16), torch.bfloat16)
-    y2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-    def decode_step(i):
-        j = i % ncopy
-        B.qmv_affine4(ws[j], ss[j], bs[j], x2, y2)
-
     if args.only in (None, "decode"):
-        ms = timer.run(decode_step, steps, warmup)
-        gbs = wbytes2 / (ms * 1e-3) / 1e9
-        result["decode"] = {"ms": ms, "GBps": gbs, "weight_bytes": wbytes2, "copies": ncopy}
-    del ws, ss, bs
+        ncopy = rotation(wbytes2)
+        ws = [to_dev(c2["w"].view(np.int32))]
+        ss = [to_dev(c2["scales"].view(np.int16), torch.bfloat16)]
+        bs = [to_dev(c2["biases"].view(np.int16), torch.bfloat16)]
+        for _ in range(ncopy - 1):
+            ws.append(ws[0].clone())
+            ss.append(ss[0].clone())
+            bs.append(bs[0].clone())
+        x2 = to_dev(c2["x"].view(np.int16), torch.bfloat16)
+        y2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def decode_step(i):
+            j = i % ncopy
+            B.qmv_affine4(ws[j], ss[j], bs[j], x2, y2)
+
+        log(f"decode: qmv_affine4 M=1 K={K} N={N}, {ncopy} weight copies, {steps} launches")
+        ms = timer.run(decode_step, steps, warmup, chunk=ncopy * 4)
+        result["decode"] = {"ms": ms, "GBps": wbytes2 / (ms * 1e-3) / 1e9, "copies": ncopy}
+        del ws, ss, bs, x2, y2
 
     # ------------------------------------------------------------ prefill GEMM
     if args.only in (None, "prefill"):
@@ -119,10 +200,11 @@ def main():
         b3 = to_dev(c3["biases"].view(np.int16), torch.bfloat16)
         x3 = to_dev(c3["x"].view(np.int16), torch.bfloat16)
         y3 = torch.empty((M3, N3), dtype=torch.bfloat16, device=dev)
-        n3 = max(20, steps // 20)
-        ms = timer.run(lambda i: B.qmm_affine4(w3, s3, b3, x3, y3), n3, max(5, warmup // 5))
+        n3 = max(20, steps // 10)
+        log(f"prefill: qmm_affine4 M={M3} K={K3} N={N3}, {n3} launches")
+        ms = timer.run(lambda i: B.qmm_affine4(w3, s3, b3, x3, y3), n3, max(5, warmup // 5), chunk=20)
         flops = 2.0 * M3 * N3 * K3
-        result["prefill"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "flops": flops, "launches": n3}
+        result["prefill"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "launches": n3}
         del w3, s3, b3, x3, y3
 
     # ------------------------------------------------------------ lookup-codebook GEMM
@@ -133,10 +215,12 @@ def main():
         p4 = to_dev(c4["packed"])
         s4 = to_dev(c4["scales"].view(np.int16), torch.float16)
         y4 = torch.empty((M4, N4), dtype=torch.float16, device=dev)
-        n4 = max(20, steps // 20)
-        ms = timer.run(lambda i: B.qmm_lut4(x4, p4, s4, c4["book"], N4, blk, y=y4), n4, max(5, warmup // 5))
+        n4 = max(20, steps // 10)
+        log(f"lut: qmm_lut4 M={M4} K={K4} N={N4} block {blk}, {n4} launches")
+        ms = timer.run(lambda i: B.qmm_lut4(x4, p4, s4, c4["book"], N4, blk, y=y4), n4, max(5, warmup // 5),
+                       chunk=20)
         flops = 2.0 * M4 * N4 * K4
-        result["lut"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "flops": flops, "launches": n4}
+        result["lut"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "launches": n4}
         del x4, p4, s4, y4
 
     # ------------------------------------------------------------ expert-routed Q4_0
@@ -152,11 +236,12 @@ def main():
         ids5 = to_dev(c5["ids"].view(np.int32))
         out5 = torch.empty((T * top_k, N5), dtype=torch.float32, device=dev)
         scratch5 = torch.empty(B.qmm_id_q4_0_scratch_bytes(E, T, top_k, K5), dtype=torch.uint8, device=dev)
-        n5 = max(50, steps // 4)
+        n5 = max(60, steps // 4)
+        log(f"moe: qmm_id_q4_0 E={E} N={N5} K={K5} tokens={T} top_k={top_k}, {ncopy5} weight copies, {n5} launches")
         ms = timer.run(lambda i: B.qmm_id_q4_0(x5, w5[i % ncopy5], ids5, T, top_k, N5, K5, E, c5["expert_stride"],
-                                               out=out5, scratch=scratch5), n5, max(5, warmup // 2))
-        result["moe"] = {"ms": ms, "GBps": wbytes5 / (ms * 1e-3) / 1e9, "weight_bytes": int(wbytes5),
-                         "flops": 2.0 * T * top_k * N5 * K5, "copies": ncopy5, "launches": n5}
+                                               out=out5, scratch=scratch5), n5, max(5, warmup // 2),
+                       chunk=ncopy5 * 5)
+        result["moe"] = {"ms": ms, "GBps": wbytes5 / (ms * 1e-3) / 1e9, "copies": ncopy5, "launches": n5}
         del w5, x5, ids5, out5, scratch5
 
     # ------------------------------------------------------------ CPU oracle baseline
@@ -164,19 +249,21 @@ def main():
     if not args.no_cpu and args.only in (None, "decode"):
         import oracle
         c = c2
+        log("cpu baseline: oracle decode GEMVs on the host cores (about 10 s)")
         oracle.affine(c["w"], c["scales"], c["biases"], c["x"], 1, K, N)  # warm (build, page-in)
         reps, t0 = 0, time.perf_counter()
         while True:
             oracle.affine(c["w"], c["scales"], c["biases"], c["x"], 1, K, N)
             reps += 1
             el = time.perf_counter() - t0
-            if el > 10.0 or reps >= 200:
+            if el > 10.0 or reps >= 400:
                 break
         cpu = {"value": round(wbytes2 * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
                "kind": "oracle",
                "sample": f"{reps} full decode GEMVs (M=1, K={K}, N={N}) in {el:.1f} s, weight bytes per second"}
 
     # ------------------------------------------------------------ report
+    mode = "eager launches" if args.eager else "HIP-graph replays of back-to-back launches"
     out = {
         "metric": "W4 qmm TFLOP/s (prefill) + weight GB/s (decode GEMV), % of MI355X roofline",
         "n_gpus": 1,
@@ -186,8 +273,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded numpy draws, the decode GEMV workload's distributions)",
+        "data": "synthetic (seeded numpy draws with the workloads' shapes and distributions)",
+        "timing": mode,
     }
+
     if "decode" in result:
         d = result["decode"]
         out.update({
@@ -195,9 +284,10 @@ def main():
             "unit": "GB/s",
             "ms_per_step": round(d["ms"], 6),
             "config": {"workload": "decode GEMV, affine INT4 group 32: x bf16 [1, 4096] . W[14336, 4096]^T",
-                       "M": 1, "K": K, "N": N, "group_size": 32, "weight_copies_rotated": d["copies"]},
+                       "M": 1, "K": K, "N": N, "group_size": 32, "weight_bytes": wbytes2,
+                       "weight_copies_rotated": d["copies"]},
             "roofline": {"bound": "hbm", "achieved": round(d["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+                         "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("decode")},
         })
     comps = {}
     if "prefill" in result:
@@ -206,21 +296,23 @@ def main():
             "workload": "qmm_affine4 M=2048 K=4096 N=4096", "ms": round(p["ms"], 5),
             "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(p["TFLOPs"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic("prefill")}}
     if "lut" in result:
         p = result["lut"]
         comps["lut_gemm"] = {
             "workload": "qmm_lut4 M=512 K=4096 N=11008 block 64", "ms": round(p["ms"], 5),
             "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(p["TFLOPs"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic("lut")}}
     if "moe" in result:
         p = result["moe"]
         comps["moe_q4_0"] = {
             "workload": "qmm_id_q4_0 E=64 N=1408 K=2048 tokens=128 top_k=8 (group + grouped GEMM)",
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": None}}
+                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe")}}
     if comps:
         out["components"] = comps
     if cpu is not None:
