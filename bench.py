@@ -37,10 +37,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "0e052583f6af1883", 36936526 + 57344),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "7cf3295ab42b119c", 144938159 + 16777245),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "7cf3295ab42b119c", 81733607 + 11272192),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "a21fb044e54fa8a9", 113704439 + 5768419),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "a9670cebebdd79c1", 36838257 + 114688),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "55838a81b0d8fafa", 144938255 + 16777324),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "55838a81b0d8fafa", 81733639 + 11272192),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "2dd6faddd5f81754", 113850817 + 5768631),
 }
 
 
@@ -112,8 +112,16 @@ class Timer:
             full = self._graph(launch, 0, chunk)
             rest = self._graph(launch, 0, steps % chunk) if steps % chunk else None
             plan = [full] * (steps // chunk) + ([rest] if rest is not None else [])
-            for _ in range(max(1, warmup // chunk)):
+            # Warm-up: the requested launches, and at least ~0.2 s of
+            # back-to-back work so the clocks have settled before timing.
+            torch.cuda.synchronize()
+            t_end = time.perf_counter() + 0.2
+            n = 0
+            while n < max(1, warmup // chunk) or time.perf_counter() < t_end:
                 full.replay()
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)

@@ -1,22 +1,31 @@
 // qmv_affine4: decode GEMV y[1, N] = x[1, K] . dequant(W)^T for affine INT4
-// group-32 weights (INT4 MatMulNBits page: the M = 1 route).
+// group-32 weights (INT4 MatMulNBits page: the M = 1 route, which that page
+// leaves to the library mat-vec).
 //
 // HBM-bound: every weight byte is read once. Each wavefront (one per
 // workgroup, so the rows spread evenly over the CUs) owns R output rows; its
 // 64 lanes split K by quantisation group (lane l takes groups l, l + 64, ...),
 // so one 128-bit load per lane and row fetches exactly one group's 32 nibbles
 // and consecutive lanes read consecutive 16-byte pieces of the row. All loads
-// of a wavefront are issued before its first arithmetic; x stays in registers
-// for all R rows, and the R row sums are reduced across lanes together. The per-group dot product
-// uses bf16 pairs (128 + q) with v_dot2_f32_bf16, then
+// of a wavefront are issued before its first arithmetic, x first; rows are
+// then consumed in load order, so arithmetic on early rows overlaps the
+// arrival of later ones. x stays in registers for all R rows, and the R row
+// sums are reduced across lanes together, in the vector ALU (lane swaps and
+// DPP moves, no LDS round trips).
+//
+// Arithmetic per group, for the bf16 pairs (128 + q) that one AND-OR makes
+// from a shifted weight word (exact: 128 + q has 8 significant bits):
 //   sum_k x_k (q_k s + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k,
-// so the scale and bias are applied once per group, not per weight.
+// so the scale and bias are applied once per group, not per weight, and the
+// inner loop is 7 integer ops + 4 v_dot2_f32_bf16 per 8 weights.
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
 namespace w4mi {
 
-constexpr int kGemvRows = 8;  // output rows per wavefront (one wavefront per workgroup)
+constexpr int kGemvRows = 4;  // output rows per wavefront (one wavefront per workgroup)
+constexpr int kGemvAux = 2;   // non-temporal weight loads: each byte is read once
+constexpr int kGemvAcc = 2;   // independent partial sums per group dot product
 
 // Lane view of one quantisation group of x: bf16 pairs matching the nibble
 // pairs (i, i + 4) of each of the group's four words, and the group sum.
@@ -25,11 +34,15 @@ struct XGroup {
     float sum;
 };
 
-__device__ __forceinline__ void x_group_from_raw(const u32x4 (&v4)[4], XGroup& xg) {
+// Builds the pairs from the group's 32 bf16 values (four 16-byte pieces);
+// an idle lane (past the last group) gets zeros, so every row term it adds
+// is zero.
+__device__ __forceinline__ void x_group_from_raw(const u32x4 (&v4)[4], bool valid, XGroup& xg) {
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t v0 = v4[j][0], v1 = v4[j][1], v2 = v4[j][2], v3 = v4[j][3];
+        const uint32_t v0 = valid ? v4[j][0] : 0u, v1 = valid ? v4[j][1] : 0u;
+        const uint32_t v2 = valid ? v4[j][2] : 0u, v3 = valid ? v4[j][3] : 0u;
         // v0..v3: elements 8j .. 8j+7 as bf16 pairs (0,1) (2,3) (4,5) (6,7)
         xg.pair[j][0] = __builtin_amdgcn_perm(v2, v0, 0x05040100u);  // (8j+0, 8j+4)
         xg.pair[j][1] = __builtin_amdgcn_perm(v2, v0, 0x07060302u);  // (8j+1, 8j+5)
@@ -43,54 +56,127 @@ __device__ __forceinline__ void x_group_from_raw(const u32x4 (&v4)[4], XGroup& x
     xg.sum = s;
 }
 
-// sum over the group of x_k * (128 + q_k), f32 accumulation.
-__device__ __forceinline__ float group_dot_biased(const u32x4& words, const XGroup& xg) {
-    float d = 0.f;
+// sum over the group of x_k * (128 + q_k), f32 accumulation. `mask` and
+// `bias` hold kAffinePairMask and kAffinePairBias in vector registers, so
+// each pair is one shift and one v_and_or_b32. NA independent partial sums
+// (word j feeds sum j % NA) shorten the chain of dependent dot products.
+template <int NA>
+__device__ __forceinline__ float group_dot_biased(const u32x4& words, const XGroup& xg, uint32_t mask,
+                                                  uint32_t bias) {
+    float d[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) d[a] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t word = words[j];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(affine_pair_biased_bf16(word, i)), as_bf16x2(xg.pair[j][i]),
-                                                d, false);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t pair = affine_pair_biased_bf16(word, i, mask, bias);
+            d[j % NA] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pair), as_bf16x2(xg.pair[j][i]), d[j % NA], false);
+        }
     }
-    return d;
+#pragma unroll
+    for (int a = 1; a < NA; ++a) d[0] += d[a];
+    return d[0];
 }
 
-// Reduces R per-lane partial sums over the wavefront in log2(64) exchange
-// steps: each of the first log2(R) steps halves the values a lane holds (the
-// upper half of the lanes keeps the upper half of the rows), the rest add
-// lane pairs. Afterwards lane l holds the full sum of row (l >> (6 - log2 R)).
+// Reduces R per-lane partial sums over the wavefront, all in the vector ALU
+// (no LDS crossbar). The first log2(R) steps halve the values a lane holds,
+// exchanging with the lane at distance 32, 16, 8 (the upper lane keeps the
+// upper half of the rows); the rest add within the remaining lane group.
+// Afterwards lane l holds the full sum of row (l >> (6 - log2 R)).
+//  - distance 32 / 16: v_permlane32_swap / v_permlane16_swap with the pair
+//    (v[i], v[i + h]) returns, in both lanes of each exchanged pair, exactly
+//    the two values that lane must add;
+//  - distance 8: DPP row_ror:8 within 16-lane rows, on a per-lane selected
+//    value;
+//  - the closing sums: DPP row_ror 8/4/2/1 over 16 lanes, or quad_perm
+//    xor 1, xor 2 and row_half_mirror over 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowRor = 0x120;     // + 1..15: rotate right within 16 lanes
+constexpr int kDppHalfMirror = 0x141; // reverse within 8 lanes
+
 template <int R>
 __device__ __forceinline__ float wave_reduce_rows(float (&v)[R], int lane) {
-    int off = 32;
+    static_assert(R == 1 || R == 2 || R == 4 || R == 8, "rows per wavefront: 1, 2, 4 or 8");
+    if constexpr (R >= 2) {
 #pragma unroll
-    for (int cnt = R; cnt > 1; cnt >>= 1, off >>= 1) {
-        const bool upper = (lane & off) != 0;
+        for (int i = 0; i < R / 2; ++i) {
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + R / 2]), false, false);
+            v[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+    }
+    if constexpr (R >= 4) {
 #pragma unroll
-        for (int i = 0; i < cnt / 2; ++i) {
-            const float keep = upper ? v[i + cnt / 2] : v[i];
-            const float send = upper ? v[i] : v[i + cnt / 2];
-            v[i] = keep + __shfl_xor(send, off, kWave);
+        for (int i = 0; i < R / 4; ++i) {
+            const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + R / 4]), false, false);
+            v[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
         }
     }
     float t = v[0];
-    for (; off >= 1; off >>= 1) t += __shfl_xor(t, off, kWave);
+    if constexpr (R == 8) {
+        const bool upper = (lane & 8) != 0;
+        const float keep = upper ? v[1] : v[0];
+        const float send = upper ? v[0] : v[1];
+        t = keep + dpp_get<kDppRowRor + 8>(send);
+    }
+    if constexpr (R <= 4) {
+        // 16 lanes share a row (R = 4), or more (R = 1, 2: finish across rows).
+        t += dpp_get<kDppRowRor + 8>(t);
+        t += dpp_get<kDppRowRor + 4>(t);
+        t += dpp_get<kDppRowRor + 2>(t);
+        t += dpp_get<kDppRowRor + 1>(t);
+        if constexpr (R <= 2) {
+            const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+            t = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+        if constexpr (R == 1) {
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+            t = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+    } else {
+        t += dpp_get<kDppQuadXor1>(t);
+        t += dpp_get<kDppQuadXor2>(t);
+        t += dpp_get<kDppHalfMirror>(t);
+    }
     return t;
+}
+
+template <int R>
+constexpr int log2_rows() {
+    return R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : R == 8 ? 3 : R == 16 ? 4 : 5;
 }
 
 // One wavefront computes R rows. K is covered in chunks of 64 groups (one
 // group per lane); T chunks are loaded before any arithmetic so that every
 // load of the wavefront is in flight at once. T = 0 selects a runtime loop
-// over chunks (one chunk in flight at a time) for long K.
-template <int R, int T>
+// over chunks (one chunk in flight at a time) for long K. Loads go through
+// buffer resources over the wave's R rows: the row offset is a scalar
+// register and the lane offset a 32-bit vector register, so addressing costs
+// no vector ALU work. AUX is the load cache policy (0, or 2 = non-temporal);
+// NA the number of independent partial sums per group dot product.
+template <int R, int T, int AUX, int NA = 1>
 __global__ __launch_bounds__(kWave) void qmv_affine4_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int K, int N, int chunks) {
     const int lane = threadIdx.x;
     const int n0 = blockIdx.x * R;  // N % 32 == 0 and R | 32: rows n0 .. n0+R-1 exist
     const int G = K / 32;
-    const size_t wrow = (size_t)(K / 8);
+    const uint32_t mask = vreg(kAffinePairMask), bias = vreg(kAffinePairBias);
+    const int wrow = K / 2;  // bytes per packed weight row
+    const int srow = G * 2;  // bytes per scale (bias) row
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * wrow, (uint32_t)(R * wrow));
+    const __amdgpu_buffer_rsrc_t ssrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow, (uint32_t)(R * srow));
+    const __amdgpu_buffer_rsrc_t bsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow, (uint32_t)(R * srow));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)(K * 2));
 
     float acc[R];
 #pragma unroll
@@ -102,46 +188,51 @@ __global__ __launch_bounds__(kWave) void qmv_affine4_kernel(
         u32x4 xr[TB][4];
         u32x4 wv[TB][R];
         uint32_t sv[TB][R], bv[TB][R];
-        bool valid[TB];
-        // x first (shared by all rows), then the weights, scales and biases.
+        // Issue order = consumption order, because loads complete in issue
+        // order for the wait counter: x and the (small) scales and biases
+        // first, then the weights row by row, each pinned in place so the
+        // arithmetic on row r waits only for loads up to row r. Idle lanes
+        // (past the last group) read the last group again.
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
             const int g = (t0 + t) * kWave + lane;
-            valid[t] = g < G;
-            const int gc = valid[t] ? g : G - 1;  // in-bounds address for idle lanes
-            const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)gc * 32);
+            const uint32_t gc = (uint32_t)(g < G ? g : G - 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xr[t][j] = xp[j];
-        }
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            const int g = (t0 + t) * kWave + lane;
-            const int gc = g < G ? g : G - 1;
+            for (int j = 0; j < 4; ++j) xr[t][j] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, gc * 64u + 16u * j, 0, 0);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const size_t row = (size_t)(n0 + r);
-                wv[t][r] = *reinterpret_cast<const u32x4*>(w + row * wrow + (size_t)gc * 4);
-                sv[t][r] = scales[row * G + gc];
-                bv[t][r] = biases[row * G + gc];
+                sv[t][r] = __builtin_amdgcn_raw_buffer_load_b16(ssrc, gc * 2u, r * srow, AUX);
+                bv[t][r] = __builtin_amdgcn_raw_buffer_load_b16(bsrc, gc * 2u, r * srow, AUX);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            const int g = (t0 + t) * kWave + lane;
+            const uint32_t gc = (uint32_t)(g < G ? g : G - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                wv[t][r] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, gc * 16u, r * wrow, AUX);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
             XGroup xg;
-            x_group_from_raw(xr[t], xg);
+            x_group_from_raw(xr[t], (t0 + t) * kWave + lane < G, xg);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float s = bf16_bits_to_f32(sv[t][r]);
                 const float b = bf16_bits_to_f32(bv[t][r]);
-                const float d = group_dot_biased(wv[t][r], xg);
-                const float part = __builtin_fmaf(s, d, __builtin_fmaf(-128.f, s, b) * xg.sum);
-                acc[r] += valid[t] ? part : 0.f;
+                const float d = group_dot_biased<NA>(wv[t][r], xg, mask, bias);
+                acc[r] = __builtin_fmaf(s, d, acc[r]);
+                acc[r] = __builtin_fmaf(__builtin_fmaf(-128.f, s, b), xg.sum, acc[r]);
             }
         }
     }
 
     const float total = wave_reduce_rows<R>(acc, lane);
-    constexpr int shift = 6 - (R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : R == 8 ? 3 : R == 16 ? 4 : 5);
+    constexpr int shift = 6 - log2_rows<R>();
     if ((lane & ((1 << shift) - 1)) == 0) y[n0 + (lane >> shift)] = f32_to_bf16_bits(total);
 }
 
@@ -163,11 +254,11 @@ extern "C" w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, cons
     const int chunks = (G + kWave - 1) / kWave;
     hipStream_t s = as_stream(stream);
     switch (chunks) {
-        case 1: hipLaunchKernelGGL((qmv_affine4_kernel<R, 1>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        case 2: hipLaunchKernelGGL((qmv_affine4_kernel<R, 2>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        case 3: hipLaunchKernelGGL((qmv_affine4_kernel<R, 3>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        case 4: hipLaunchKernelGGL((qmv_affine4_kernel<R, 4>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        default: hipLaunchKernelGGL((qmv_affine4_kernel<R, 0>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
+        case 1: hipLaunchKernelGGL((qmv_affine4_kernel<R, 1, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
+        case 2: hipLaunchKernelGGL((qmv_affine4_kernel<R, 2, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
+        case 3: hipLaunchKernelGGL((qmv_affine4_kernel<R, 3, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
+        case 4: hipLaunchKernelGGL((qmv_affine4_kernel<R, 4, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
+        default: hipLaunchKernelGGL((qmv_affine4_kernel<R, 0, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
     }
     return launch_status("qmv_affine4");
 }

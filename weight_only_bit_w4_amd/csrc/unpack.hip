@@ -15,10 +15,11 @@ __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __
     const int64_t i = (int64_t)blockIdx.x * kUnpackThreads + threadIdx.x;
     if (i >= words) return;
     const uint32_t word = w[i];
+    const uint32_t mask = vreg(kAffinePairMask), bias = vreg(kAffinePairBias);
     uint8_t out[8];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const uint32_t pair = affine_pair_biased_bf16(word, p);  // nibbles p (low half) and p + 4 (high half)
+        const uint32_t pair = affine_pair_biased_bf16(word, p, mask, bias);  // nibbles p (low half) and p + 4 (high half)
         out[p] = (uint8_t)(pair & 0xFu);
         out[p + 4] = (uint8_t)((pair >> 16) & 0xFu);
     }

@@ -62,13 +62,38 @@ __device__ __forceinline__ void affine_word_to_f32(uint32_t word, float (&q)[8])
     for (int j = 0; j < 8; ++j) q[j] = (float)affine_nibble(word, j);
 }
 
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer resource over [base, base + bytes): loads through it take a
+// scalar offset per instruction and a 32-bit lane offset, and return zero
+// past the end. The third descriptor word is the gfx9 raw-buffer setting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------- integer helpers
+// A 32-bit constant held in a vector register (gfx9 VOP3 encodings take no
+// literal and read at most one scalar register, so a three-operand integer
+// op with two constants needs one of them in a VGPR).
+__device__ __forceinline__ uint32_t vreg(uint32_t c) {
+    uint32_t r = c;
+    asm("" : "+v"(r));
+    return r;
+}
+
+// (a & m) | c; with m and c in vector registers (vreg) the compiler selects
+// one v_and_or_b32.
+__device__ __forceinline__ uint32_t and_or_u32(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
+
 // Pair form used by the decode GEMV: bf16 pairs holding 128 + q for nibbles
 // (i, i + 4), i = 0..3, of an affine word. 128 + q (q <= 15) is exact in bf16
 // (8 significant bits), so a bf16 dot product with these pairs yields
-// sum (128 + q) x exactly up to f32 accumulation.
-__device__ __forceinline__ uint32_t affine_pair_biased_bf16(uint32_t word, int i) {
-    return ((word >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+// sum (128 + q) x exactly up to f32 accumulation. mask = 0x000F000F and
+// bias = 0x43004300 (bf16 128.0 twice), passed in vector registers.
+__device__ __forceinline__ uint32_t affine_pair_biased_bf16(uint32_t word, int i, uint32_t mask, uint32_t bias) {
+    return and_or_u32(i == 0 ? word : word >> (4 * i), mask, bias);
 }
+constexpr uint32_t kAffinePairMask = 0x000F000Fu;
+constexpr uint32_t kAffinePairBias = 0x43004300u;
 
 // Lookup-codebook index order (lut4 page, decode kernel): flat index i uses
 // the HIGH nibble of byte i/2 when i is even, the LOW nibble when i is odd.
