@@ -96,6 +96,9 @@ def test_qmv_affine4(K, N, seed):
     (32, 32, 32), (4, 32, 32), (7, 64, 64), (64, 32, 32), (64, 128, 256), (100, 256, 512),  # page's test shapes
     (300, 160, 224),                      # ragged M, N not a multiple of the 128 tile
     (65, 96, 160),                        # just past the small-M tile
+    (260, 192, 96),                       # K % 64 == 0 prefill path: 3 K steps (ring wrap), ragged M and N
+    (513, 320, 416),                      # 5 K steps, M one past two 256-row tiles
+    (256, 64, 128),                       # a single K step, exact tiles
 ])
 def test_qmm_affine4_small(M, K, N):
     c = synth.affine_case(M, K, N, seed=M + K + N)

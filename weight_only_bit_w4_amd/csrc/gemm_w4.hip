@@ -223,6 +223,399 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_affine4_kernel(const uint32_
     gemm_w4_body<WM, WN, FM, FN, false>(x, y, M, K, N, dec, As, Bs);
 }
 
+// ---------------------------------------------------------------- prefill GEMM (affine)
+// qmm_affine4 for the prefill shapes: a 256 x 128 output tile per workgroup
+// (one workgroup per CU at M = 2048, N = 4096) of 8 wavefronts in a 4 x 2
+// grid, two per SIMD so one's vector-ALU and LDS work fills the other's
+// matrix-core time. Each wavefront owns a 64 x 64 sub-tile as 2 x 2
+// accumulators of v_mfma_f32_32x32x16_bf16 (the full-rate matrix instruction
+// on gfx950). K advances 64 (two quantisation groups) per step. Global loads
+// run two steps ahead into registers and the LDS tiles are double buffered,
+// so a step's loads have two steps of matrix-core work to arrive. Each
+// thread decodes half a (weight row, group) per step: 16 nibbles into bf16
+// w = q s + b, via one AND-OR per nibble pair into binary16 1024 + q (or
+// 1024 + 16 q for the odd nibbles) and one v_fma_mix_f32 per weight with the
+// scale and the offset b - 1024 s (or s / 16 and b - 64 s) held in f32, then
+// v_cvt_pk_bf16_f32. LDS rows are 144 bytes (64 bf16 + 16 bytes), which keeps
+// the 16-byte operand reads of 16 consecutive rows conflict-free. Workgroups
+// are assigned to tiles so that the 32 workgroups one XCD runs share one x
+// tile in that XCD's L2.
+constexpr int kPBM = 256, kPBN = 128, kPBK = 64;
+constexpr int kPThreads = 512;
+constexpr int kPLd = kPBK + 8;  // LDS row stride in 16-bit elements (144 bytes)
+constexpr int kPTM = 2, kPTN = 2;  // 32 x 32 accumulator tiles per wavefront
+
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+struct PrefillRegs {
+    u32x4 x[4];       // x tile pieces i: row (tid / 8) + 64 i, 16-byte chunk tid % 8
+    u32x2 w;          // two words (16 nibbles) of one quantisation group of one weight row
+    uint32_t s, b;    // the group's scale and bias (bf16 bits)
+};
+
+// Offsets past a buffer's end read as zero (and stores there are dropped);
+// kOob is far past any tile.
+constexpr uint32_t kOob = 0x80000000u;
+
+// Per-thread load offsets that stay fixed over the K loop; each step adds a
+// wave-uniform (scalar register) offset. Thread t decodes weight row t / 4,
+// group (t / 2) % 2 of the step, words 2 (t % 2), 2 (t % 2) + 1.
+struct PrefillOffsets {
+    uint32_t x, w, s;
+};
+
+template <bool kTail>
+__device__ __forceinline__ void prefill_load(PrefillRegs& R, int kt, bool live, const PrefillOffsets& o, int tid, int K, int G,
+                                             const __amdgpu_buffer_rsrc_t& xsrc, const __amdgpu_buffer_rsrc_t& wsrc,
+                                             const __amdgpu_buffer_rsrc_t& ssrc, const __amdgpu_buffer_rsrc_t& bsrc) {
+    // K % 64 == 32 (kTail): the last step holds one group; its other half is
+    // read as zeros (x chunk past K, weight group past K / 32).
+    // live == false (steps past the end): every offset is out of range, so
+    // the loads fetch nothing and no branch splits the wait-counter state.
+    const bool xv = live && (!kTail || kt * kPBK + 8 * (tid & 7) < K);
+    const bool gv = live && (!kTail || 2 * kt + ((tid >> 1) & 1) < G);
+    // Step offsets are wave-uniform; readfirstlane keeps them in scalar
+    // registers (the buffer instructions' soffset operand).
+    const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK), kw = __builtin_amdgcn_readfirstlane(kt * 32);
+    const int ks = __builtin_amdgcn_readfirstlane(kt * 4), xrow = __builtin_amdgcn_readfirstlane(128 * K);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        R.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xv ? o.x : kOob, i * xrow + kx, 0);
+    R.w = __builtin_amdgcn_raw_buffer_load_b64(wsrc, gv ? o.w : kOob, kw, 0);
+    R.s = __builtin_amdgcn_raw_buffer_load_b16(ssrc, gv ? o.s : kOob, ks, 0);
+    R.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, gv ? o.s : kOob, ks, 0);
+}
+
+// Eight affine weights of one word (k = 8j .. 8j + 7) as bf16 pairs in k order.
+__device__ __forceinline__ u32x4 affine_word_bf16(uint32_t word, float s, float c, float s16, float c16,
+                                                  uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    const uint32_t w8 = word >> 8;
+    const f16x2 p0 = as_f16x2(and_or_u32(word, m_lo, magic));  // 1024 + n0, 1024 + n4
+    const f16x2 p1 = as_f16x2(and_or_u32(word, m_hi, magic));  // 1024 + 16 n1, 1024 + 16 n5
+    const f16x2 p2 = as_f16x2(and_or_u32(w8, m_lo, magic));    // 1024 + n2, 1024 + n6
+    const f16x2 p3 = as_f16x2(and_or_u32(w8, m_hi, magic));    // 1024 + 16 n3, 1024 + 16 n7
+    const float f0 = __builtin_fmaf((float)p0[0], s, c), f4 = __builtin_fmaf((float)p0[1], s, c);
+    const float f1 = __builtin_fmaf((float)p1[0], s16, c16), f5 = __builtin_fmaf((float)p1[1], s16, c16);
+    const float f2 = __builtin_fmaf((float)p2[0], s, c), f6 = __builtin_fmaf((float)p2[1], s, c);
+    const float f3 = __builtin_fmaf((float)p3[0], s16, c16), f7 = __builtin_fmaf((float)p3[1], s16, c16);
+    return u32x4{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3), pack_bf16x2(f4, f5), pack_bf16x2(f6, f7)};
+}
+
+__device__ __forceinline__ void prefill_store(const PrefillRegs& R, int tid, uint16_t* As, uint16_t* Bs,
+                                              uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    uint16_t* xa = As + (tid >> 3) * kPLd + 8 * (tid & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xa + 64 * i * kPLd) = R.x[i];
+    const float s = bf16_bits_to_f32(R.s), b = bf16_bits_to_f32(R.b);
+    const float c = __builtin_fmaf(-1024.f, s, b), s16 = 0.0625f * s, c16 = __builtin_fmaf(-64.f, s, b);
+    uint16_t* dst = Bs + (tid >> 2) * kPLd + 16 * (tid & 3);
+    *reinterpret_cast<u32x4*>(dst) = affine_word_bf16(R.w[0], s, c, s16, c16, m_lo, m_hi, magic);
+    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_bf16(R.w[1], s, c, s16, c16, m_lo, m_hi, magic);
+}
+
+// One step (64 of K) of the wavefront's 64 x 64 sub-tile: per 16 of K, two
+// A fragments (rows lane % 32 of each 32-row tile, k = 8 (lane / 32) .. +7)
+// and two B fragments, four v_mfma_f32_32x32x16_bf16.
+__device__ __forceinline__ void prefill_mma(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
+                                            f32x16 (&acc)[kPTM][kPTN]) {
+    const uint16_t* ab = As + (wm * 64 + (lane & 31)) * kPLd + 8 * (lane >> 5);
+    const uint16_t* bb = Bs + (wn * 64 + (lane & 31)) * kPLd + 8 * (lane >> 5);
+#pragma unroll
+    for (int sub = 0; sub < kPBK / 16; ++sub) {
+        u32x4 a[kPTM], b[kPTN];
+#pragma unroll
+        for (int f = 0; f < kPTM; ++f) a[f] = *reinterpret_cast<const u32x4*>(ab + f * 32 * kPLd + sub * 16);
+#pragma unroll
+        for (int g = 0; g < kPTN; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+#pragma unroll
+        for (int f = 0; f < kPTM; ++f)
+#pragma unroll
+            for (int g = 0; g < kPTN; ++g)
+                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[f]),
+                                                                   __builtin_bit_cast(bf16x8, b[g]), acc[f][g], 0, 0, 0);
+    }
+}
+
+template <bool kTail>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_kernel(
+    const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kPBM * kPLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
+    const int tiles = tiles_m * tiles_n;
+    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
+    // contiguous run of tiles (n fastest), so it shares one x tile.
+    int t = blockIdx.x;
+    if (tiles % 8 == 0) t = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+    const int m0 = (t / tiles_n) * kPBM, n0 = (t % tiles_n) * kPBN;
+    const int G = K / 32, steps = (K + kPBK - 1) / kPBK;
+
+    const int mrows = min(kPBM, M - m0), nrows = min(kPBN, N - n0);
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * (K / 2), (uint32_t)(nrows * (K / 2)));
+    const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
+    const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
+    const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
+    PrefillOffsets o;
+    o.x = (uint32_t)((tid >> 3) * K * 2 + 16 * (tid & 7));
+    o.w = (uint32_t)((tid >> 2) * (K / 2) + 16 * ((tid >> 1) & 1) + 8 * (tid & 1));
+    o.s = (uint32_t)(((tid >> 2) * G + ((tid >> 1) & 1)) * 2);
+
+    f32x16 acc[kPTM][kPTN];
+#pragma unroll
+    for (int f = 0; f < kPTM; ++f)
+#pragma unroll
+        for (int g = 0; g < kPTN; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][g][e] = 0.f;
+
+    PrefillRegs R0, R1;
+    prefill_load<kTail>(R0, 0, true, o, tid, K, G, xsrc, wsrc, ssrc, bsrc);
+    prefill_load<kTail>(R1, 1, steps > 1, o, tid, K, G, xsrc, wsrc, ssrc, bsrc);
+    prefill_store(R0, tid, As[0], Bs[0], m_lo, m_hi, magic);
+    __syncthreads();
+    for (int kt = 0; kt < steps; kt += 2) {
+        // even step: buffer 0 holds step kt; R1 holds step kt + 1
+        prefill_load<kTail>(R0, kt + 2, kt + 2 < steps, o, tid, K, G, xsrc, wsrc, ssrc, bsrc);
+        __builtin_amdgcn_sched_barrier(0);
+        prefill_mma(As[0], Bs[0], wm, wn, lane, acc);
+        if (kt + 1 < steps) prefill_store(R1, tid, As[1], Bs[1], m_lo, m_hi, magic);
+        __syncthreads();
+        if (kt + 1 >= steps) break;
+        // odd step: buffer 1 holds step kt + 1; R0 holds step kt + 2
+        prefill_load<kTail>(R1, kt + 3, kt + 3 < steps, o, tid, K, G, xsrc, wsrc, ssrc, bsrc);
+        __builtin_amdgcn_sched_barrier(0);
+        prefill_mma(As[1], Bs[1], wm, wn, lane, acc);
+        if (kt + 2 < steps) prefill_store(R0, tid, As[0], Bs[0], m_lo, m_hi, magic);
+        __syncthreads();
+    }
+
+    // Epilogue. Lane holds column lane % 32 of each 32 x 32 tile and, in
+    // register e, row 8 (e / 4) + 4 (lane / 32) + e % 4. Stores go through a
+    // buffer resource over the tile's rows, so rows past M are dropped by the
+    // hardware; columns past N are sent out of range.
+    const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
+#pragma unroll
+    for (int g = 0; g < kPTN; ++g) {
+        const int n = n0 + wn * 64 + g * 32 + (lane & 31);
+        const uint32_t voff = n < N ? (uint32_t)((4 * (lane >> 5)) * N + n) * 2u : kOob;
+#pragma unroll
+        for (int f = 0; f < kPTM; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = wm * 64 + f * 32 + 8 * (e >> 2) + (e & 3);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[f][g][e]), ysrc, voff, row * N * 2, 0);
+            }
+    }
+}
+
+// ---------------------------------------------------------------- prefill GEMM, LDS-DMA form
+// The same tile (256 x 128, 8 wavefronts of 64 x 64, K step 64) for
+// K % 64 == 0, fed by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) so the
+// data in flight does not occupy registers and the prefetch can run two
+// steps ahead of the matrix-core work:
+//   x ring   3 x [256 rows x 128 B]: row r's 16-byte chunk c at slot
+//            c ^ ((r / 2) % 8), which keeps the 32x32x16 A-operand reads
+//            (32 rows x 2 chunks per instruction) conflict-free;
+//   W ring   3 x [128 rows x 32 B] packed nibbles of the step's two groups,
+//            plus 3 x [128] scale pairs and 3 x [128] bias pairs;
+//   W tiles  2 x [128 rows x 144 B] decoded bf16 operands.
+// Iteration j: wait for this wavefront's DMA of step j (x) and j + 1 (packed
+// W), barrier, issue the DMA of steps j + 2 / j + 3, decode step j + 1's
+// weights into the free W tile, and run step j's 16 matrix instructions per
+// wavefront. Every wavefront issues exactly 5 DMA instructions per
+// iteration (4 for x and one for packed weights, scales or biases), so one
+// s_waitcnt vmcnt(5) covers the data two iterations old. Waits are explicit
+// (the compiler does not count LDS DMA against LDS reads) and the barrier
+// carries no memory fence, which would wait for all DMA in flight.
+constexpr int kDStages = 3;
+constexpr int kDXBytes = kPBM * 128;           // x ring slot
+constexpr int kDWBytes = kPBN * 32;            // packed W ring slot
+constexpr int kDSBytes = kPBN * 4;             // scale (or bias) pairs ring slot
+constexpr int kDPerIter = 5;                   // DMA instructions per wavefront per iteration
+
+// Byte address of an LDS object, for inline-asm LDS instructions.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Buffer-to-LDS DMA of 16 (or 4) bytes per lane: lane l's bytes land at
+// lds + 16 l (or 4 l); M0 carries the wave-uniform LDS base. Issued as inline
+// asm so that the compiler, which cannot tell DMA targets apart, does not
+// wait for all DMA in flight before every LDS access; completion is awaited
+// explicitly (wait_vmcnt) before the data is read. Nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void lds_dma16(const __amdgpu_buffer_rsrc_t& rsrc, void* lds, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff));
+}
+__device__ __forceinline__ void lds_dma4(const __amdgpu_buffer_rsrc_t& rsrc, void* lds, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 ::"s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff));
+}
+// s_barrier with a compiler-only memory clobber (no hardware wait).
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt with only vmcnt (N <= 15) or only lgkmcnt(0) constrained. gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
+
+struct DmaPlan {
+    uint32_t x[4];  // per-lane x offsets of this wavefront's 4 blocks (row r, swizzled chunk)
+    uint32_t w;     // packed W / scale / bias offset
+};
+
+// Issues step kt's x DMA into xring slot and step kw's packed-weight-side DMA
+// (wavefronts 0-3: packed words; 4-5: scales; 6-7: biases). Steps past the
+// end use out-of-range offsets, which fetch nothing.
+__device__ __forceinline__ void dma_issue(const DmaPlan& d, int wave, int kt, int kw, int steps, uint8_t* xslot,
+                                          uint8_t* wslot, uint8_t* sslot, uint8_t* bslot,
+                                          const __amdgpu_buffer_rsrc_t& xsrc, const __amdgpu_buffer_rsrc_t& wsrc,
+                                          const __amdgpu_buffer_rsrc_t& ssrc, const __amdgpu_buffer_rsrc_t& bsrc) {
+    const bool xl = kt < steps, wl = kw < steps;
+    const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_dma16(xsrc, xslot + (4 * wave + j) * 1024, xl ? d.x[j] : kOob, kx);
+    if (wave < 4) {
+        lds_dma16(wsrc, wslot + wave * 1024, wl ? d.w : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
+    } else if (wave < 6) {
+        lds_dma4(ssrc, sslot + (wave - 4) * 256, wl ? d.w : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+    } else {
+        lds_dma4(bsrc, bslot + (wave - 6) * 256, wl ? d.w : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+    }
+}
+
+// Decodes one step's weights from the packed ring slot into a W tile: thread
+// t takes row t / 4, group (t / 2) % 2, words 2 (t % 2), 2 (t % 2) + 1.
+__device__ __forceinline__ void dma_decode(int tid, const uint8_t* wslot, const uint8_t* sslot, const uint8_t* bslot,
+                                           uint16_t* Bs, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    const int r = tid >> 2, g = (tid >> 1) & 1, h = tid & 1;
+    const u32x2 words = *reinterpret_cast<const u32x2*>(wslot + r * 32 + 16 * g + 8 * h);
+    const uint32_t sp = *reinterpret_cast<const uint32_t*>(sslot + 4 * r);
+    const uint32_t bp = *reinterpret_cast<const uint32_t*>(bslot + 4 * r);
+    const float s = bf16_bits_to_f32(g ? (sp >> 16) : (sp & 0xFFFFu));
+    const float b = bf16_bits_to_f32(g ? (bp >> 16) : (bp & 0xFFFFu));
+    const float c = __builtin_fmaf(-1024.f, s, b), s16 = 0.0625f * s, c16 = __builtin_fmaf(-64.f, s, b);
+    uint16_t* dst = Bs + r * kPLd + 32 * g + 16 * h;
+    *reinterpret_cast<u32x4*>(dst) = affine_word_bf16(words[0], s, c, s16, c16, m_lo, m_hi, magic);
+    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_bf16(words[1], s, c, s16, c16, m_lo, m_hi, magic);
+}
+
+// Step j's matrix work on the swizzled x slot and the W tile.
+__device__ __forceinline__ void dma_mma(const uint8_t* xslot, const uint16_t* Bs, int wm, int wn, int lane,
+                                        f32x16 (&acc)[kPTM][kPTN]) {
+    const uint16_t* bb = Bs + (wn * 64 + (lane & 31)) * kPLd + 8 * (lane >> 5);
+#pragma unroll
+    for (int sub = 0; sub < kPBK / 16; ++sub) {
+        u32x4 a[kPTM], b[kPTN];
+        const int c = 2 * sub + (lane >> 5);
+#pragma unroll
+        for (int f = 0; f < kPTM; ++f) {
+            const int row = wm * 64 + f * 32 + (lane & 31);
+            a[f] = *reinterpret_cast<const u32x4*>(xslot + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
+        }
+#pragma unroll
+        for (int g = 0; g < kPTN; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+#pragma unroll
+        for (int f = 0; f < kPTM; ++f)
+#pragma unroll
+            for (int g = 0; g < kPTN; ++g)
+                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[f]),
+                                                                   __builtin_bit_cast(bf16x8, b[g]), acc[f][g], 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_dma_kernel(
+    const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
+    __shared__ __attribute__((aligned(1024))) uint8_t xring[kDStages][kDXBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t wring[kDStages][kDWBytes];
+    __shared__ __attribute__((aligned(256))) uint8_t sring[kDStages][kDSBytes];
+    __shared__ __attribute__((aligned(256))) uint8_t bring[kDStages][kDSBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
+    const int tiles = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if (tiles % 8 == 0) t = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+    const int m0 = (t / tiles_n) * kPBM, n0 = (t % tiles_n) * kPBN;
+    const int G = K / 32, steps = K / kPBK;
+
+    const int mrows = min(kPBM, M - m0), nrows = min(kPBN, N - n0);
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * (K / 2), (uint32_t)(nrows * (K / 2)));
+    const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
+    const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
+    const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
+
+    DmaPlan d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * (4 * wave + j) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        d.x[j] = (uint32_t)(row * K * 2 + 16 * c);
+    }
+    if (wave < 4) {
+        d.w = (uint32_t)((32 * wave + (lane >> 1)) * (K / 2) + 16 * (lane & 1));
+    } else {
+        d.w = (uint32_t)((64 * ((wave - 4) & 1) + lane) * G * 2);
+    }
+
+    f32x16 acc[kPTM][kPTN];
+#pragma unroll
+    for (int f = 0; f < kPTM; ++f)
+#pragma unroll
+        for (int g = 0; g < kPTN; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][g][e] = 0.f;
+
+    // Prologue: packed W of step 0 (with x of a nonexistent step, so every
+    // batch is 5 instructions), then steps (0, 1) and (1, 2).
+    dma_issue(d, wave, steps, 0, steps, xring[2], wring[0], sring[0], bring[0], xsrc, wsrc, ssrc, bsrc);
+    dma_issue(d, wave, 0, 1, steps, xring[0], wring[1], sring[1], bring[1], xsrc, wsrc, ssrc, bsrc);
+    dma_issue(d, wave, 1, 2, steps, xring[1], wring[2], sring[2], bring[2], xsrc, wsrc, ssrc, bsrc);
+    wait_vmcnt<2 * kDPerIter>();
+    raw_barrier();
+    dma_decode(tid, wring[0], sring[0], bring[0], Bs[0], m_lo, m_hi, magic);
+
+    for (int j = 0; j < steps; ++j) {
+        const int cur = j % kDStages, nxt = (j + 1) % kDStages, fut = (j + 2) % kDStages;
+        wait_vmcnt<kDPerIter>();  // this wavefront's DMA of x(j) and packed W(j + 1)
+        wait_lgkmcnt0();          // this wavefront's decode of W(j)
+        raw_barrier();
+        // x(j + 2) and packed W(j + 3): slot fut was last read in iteration j - 1.
+        dma_issue(d, wave, j + 2, j + 3, steps, xring[fut], wring[cur], sring[cur], bring[cur], xsrc, wsrc, ssrc,
+                  bsrc);
+        dma_decode(tid, wring[nxt], sring[nxt], bring[nxt], Bs[(j + 1) & 1], m_lo, m_hi, magic);
+        dma_mma(xring[cur], Bs[j & 1], wm, wn, lane, acc);
+    }
+
+    const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
+#pragma unroll
+    for (int g = 0; g < kPTN; ++g) {
+        const int n = n0 + wn * 64 + g * 32 + (lane & 31);
+        const uint32_t voff = n < N ? (uint32_t)((4 * (lane >> 5)) * N + n) * 2u : kOob;
+#pragma unroll
+        for (int f = 0; f < kPTM; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = wm * 64 + f * 32 + 8 * (e >> 2) + (e & 3);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[f][g][e]), ysrc, voff, row * N * 2, 0);
+            }
+    }
+}
+
 struct Book16 {
     float v[16];
 };
@@ -264,10 +657,13 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
         hipLaunchKernelGGL((qmm_affine4_kernel<1, 4, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, w, scales, biases,
                            x, y, (int)M, (int)K, (int)N);
     } else {
-        constexpr int BM = 256, BN = 128;
-        const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-        hipLaunchKernelGGL((qmm_affine4_kernel<2, 2, 8, 4>), dim3(tiles), dim3(kGemmThreads), 0, s, w, scales, biases,
-                           x, y, (int)M, (int)K, (int)N);
+        const unsigned tiles = (unsigned)(((M + kPBM - 1) / kPBM) * ((N + kPBN - 1) / kPBN));
+        if (K % kPBK == 0)
+            hipLaunchKernelGGL(qmm_affine4_prefill_dma_kernel, dim3(tiles), dim3(kPThreads), 0, s, w, scales, biases,
+                               x, y, (int)M, (int)K, (int)N);
+        else
+            hipLaunchKernelGGL(qmm_affine4_prefill_kernel<true>, dim3(tiles), dim3(kPThreads), 0, s, w, scales, biases,
+                               x, y, (int)M, (int)K, (int)N);
     }
     return launch_status("qmm_affine4");
 }
