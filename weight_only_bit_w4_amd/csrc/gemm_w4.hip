@@ -415,10 +415,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // ---------------------------------------------------------------- prefill GEMM, LDS-DMA form
-// The same tile (256 x 128, 8 wavefronts of 64 x 64, K step 64) for
-// K % 64 == 0, fed by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) so the
-// data in flight does not occupy registers and the prefetch can run two
-// steps ahead of the matrix-core work:
+// The same 256 x 128 tile and K step of 64 for K % 64 == 0, fed by
+// buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) so the data in flight does
+// not occupy registers and the prefetch can run two steps ahead of the
+// matrix-core work. WAVES = 8 (two per SIMD, 64 x 64 sub-tiles) or 4 (one
+// per SIMD, 128 x 64 sub-tiles, which cuts the LDS operand reads by a
+// quarter). LDS:
 //   x ring   3 x [256 rows x 128 B]: row r's 16-byte chunk c at slot
 //            c ^ ((r / 2) % 8), which keeps the 32x32x16 A-operand reads
 //            (32 rows x 2 chunks per instruction) conflict-free;
@@ -426,18 +428,16 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 //            plus 3 x [128] scale pairs and 3 x [128] bias pairs;
 //   W tiles  2 x [128 rows x 144 B] decoded bf16 operands.
 // Iteration j: wait for this wavefront's DMA of step j (x) and j + 1 (packed
-// W), barrier, issue the DMA of steps j + 2 / j + 3, decode step j + 1's
-// weights into the free W tile, and run step j's 16 matrix instructions per
-// wavefront. Every wavefront issues exactly 5 DMA instructions per
-// iteration (4 for x and one for packed weights, scales or biases), so one
-// s_waitcnt vmcnt(5) covers the data two iterations old. Waits are explicit
-// (the compiler does not count LDS DMA against LDS reads) and the barrier
-// carries no memory fence, which would wait for all DMA in flight.
+// W), barrier, run step j's matrix work, issue the DMA of steps j + 2 / j + 3
+// and decode step j + 1's weights into the free W tile (the matrix
+// instructions run on while these issue). Every wavefront issues the same
+// number of DMA instructions per iteration, so one s_waitcnt covers the data
+// two iterations old. Waits are explicit and the barrier carries no memory
+// fence, which would wait for all DMA in flight.
 constexpr int kDStages = 3;
 constexpr int kDXBytes = kPBM * 128;           // x ring slot
 constexpr int kDWBytes = kPBN * 32;            // packed W ring slot
 constexpr int kDSBytes = kPBN * 4;             // scale (or bias) pairs ring slot
-constexpr int kDPerIter = 5;                   // DMA instructions per wavefront per iteration
 
 // Byte address of an LDS object, for inline-asm LDS instructions.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -459,83 +459,124 @@ __device__ __forceinline__ void lds_dma4(const __amdgpu_buffer_rsrc_t& rsrc, voi
 }
 // s_barrier with a compiler-only memory clobber (no hardware wait).
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// s_waitcnt with only vmcnt (N <= 15) or only lgkmcnt(0) constrained. gfx9
+// s_waitcnt with only vmcnt (N < 64) or only lgkmcnt(0) constrained. gfx9
 // encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
 
-struct DmaPlan {
-    uint32_t x[4];  // per-lane x offsets of this wavefront's 4 blocks (row r, swizzled chunk)
-    uint32_t w;     // packed W / scale / bias offset
+template <int WAVES>
+struct DmaShape {
+    static constexpr int kThreads = WAVES * kWave;
+    static constexpr int kXB = 32 / WAVES;           // x DMA blocks (1 KB) per wavefront
+    static constexpr int kOB = 8 / WAVES;            // packed-W / scale / bias DMA instructions per wavefront
+    static constexpr int kPerIter = kXB + kOB;       // DMA instructions per wavefront per iteration
+    static constexpr int kWGM = WAVES / 2;           // wavefronts along M (2 along N)
+    static constexpr int kTM = 256 / kWGM / 32;      // 32-row tiles per wavefront
+    static constexpr int kTN = 2;                    // 32-column tiles per wavefront
+    static constexpr int kWPT = 1024 / kThreads;     // packed words decoded per thread per step
 };
 
-// Issues step kt's x DMA into xring slot and step kw's packed-weight-side DMA
-// (wavefronts 0-3: packed words; 4-5: scales; 6-7: biases). Steps past the
-// end use out-of-range offsets, which fetch nothing.
-__device__ __forceinline__ void dma_issue(const DmaPlan& d, int wave, int kt, int kw, int steps, uint8_t* xslot,
+template <int WAVES>
+struct DmaPlan {
+    uint32_t x[DmaShape<WAVES>::kXB];  // per-lane x offsets (row r, swizzled chunk)
+    uint32_t o[DmaShape<WAVES>::kOB];  // packed W / scale / bias offsets
+};
+
+// "Other" DMA block q (0..7) of a step: 0-3 packed words (1 KB, 32 rows
+// each), 4-5 scale pairs, 6-7 bias pairs (256 B, 64 rows each). Wavefront w
+// issues blocks w * kOB .. w * kOB + kOB - 1.
+template <int WAVES>
+__device__ __forceinline__ void dma_issue(const DmaPlan<WAVES>& d, int wave, int kt, int kw, int steps, uint8_t* xslot,
                                           uint8_t* wslot, uint8_t* sslot, uint8_t* bslot,
                                           const __amdgpu_buffer_rsrc_t& xsrc, const __amdgpu_buffer_rsrc_t& wsrc,
                                           const __amdgpu_buffer_rsrc_t& ssrc, const __amdgpu_buffer_rsrc_t& bsrc) {
+    using S = DmaShape<WAVES>;
     const bool xl = kt < steps, wl = kw < steps;
     const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(xsrc, xslot + (4 * wave + j) * 1024, xl ? d.x[j] : kOob, kx);
-    if (wave < 4) {
-        lds_dma16(wsrc, wslot + wave * 1024, wl ? d.w : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
-    } else if (wave < 6) {
-        lds_dma4(ssrc, sslot + (wave - 4) * 256, wl ? d.w : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
-    } else {
-        lds_dma4(bsrc, bslot + (wave - 6) * 256, wl ? d.w : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+    for (int j = 0; j < S::kXB; ++j) lds_dma16(xsrc, xslot + (S::kXB * wave + j) * 1024, xl ? d.x[j] : kOob, kx);
+#pragma unroll
+    for (int i = 0; i < S::kOB; ++i) {
+        const int q = wave * S::kOB + i;  // wave-uniform
+        if (q < 4)
+            lds_dma16(wsrc, wslot + q * 1024, wl ? d.o[i] : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
+        else if (q < 6)
+            lds_dma4(ssrc, sslot + (q - 4) * 256, wl ? d.o[i] : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+        else
+            lds_dma4(bsrc, bslot + (q - 6) * 256, wl ? d.o[i] : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
     }
 }
 
-// Decodes one step's weights from the packed ring slot into a W tile: thread
-// t takes row t / 4, group (t / 2) % 2, words 2 (t % 2), 2 (t % 2) + 1.
+// Decodes one step's weights from the packed ring slot into a W tile: each
+// row's 8 words (two groups) are split over 8 / kWPT threads.
+template <int WAVES>
 __device__ __forceinline__ void dma_decode(int tid, const uint8_t* wslot, const uint8_t* sslot, const uint8_t* bslot,
                                            uint16_t* Bs, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
-    const int r = tid >> 2, g = (tid >> 1) & 1, h = tid & 1;
-    const u32x2 words = *reinterpret_cast<const u32x2*>(wslot + r * 32 + 16 * g + 8 * h);
+    constexpr int WPT = DmaShape<WAVES>::kWPT, TPR = 8 / WPT;
+    const int r = tid / TPR, w0 = (tid % TPR) * WPT, g = w0 / 4;
     const uint32_t sp = *reinterpret_cast<const uint32_t*>(sslot + 4 * r);
     const uint32_t bp = *reinterpret_cast<const uint32_t*>(bslot + 4 * r);
     const float s = bf16_bits_to_f32(g ? (sp >> 16) : (sp & 0xFFFFu));
     const float b = bf16_bits_to_f32(g ? (bp >> 16) : (bp & 0xFFFFu));
     const float c = __builtin_fmaf(-1024.f, s, b), s16 = 0.0625f * s, c16 = __builtin_fmaf(-64.f, s, b);
-    uint16_t* dst = Bs + r * kPLd + 32 * g + 16 * h;
-    *reinterpret_cast<u32x4*>(dst) = affine_word_bf16(words[0], s, c, s16, c16, m_lo, m_hi, magic);
-    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_bf16(words[1], s, c, s16, c16, m_lo, m_hi, magic);
+    uint16_t* dst = Bs + r * kPLd + 8 * w0;
+    if constexpr (WPT == 2) {
+        const u32x2 words = *reinterpret_cast<const u32x2*>(wslot + r * 32 + 4 * w0);
+        *reinterpret_cast<u32x4*>(dst) = affine_word_bf16(words[0], s, c, s16, c16, m_lo, m_hi, magic);
+        *reinterpret_cast<u32x4*>(dst + 8) = affine_word_bf16(words[1], s, c, s16, c16, m_lo, m_hi, magic);
+    } else {
+        const u32x4 words = *reinterpret_cast<const u32x4*>(wslot + r * 32 + 4 * w0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4*>(dst + 8 * i) = affine_word_bf16(words[i], s, c, s16, c16, m_lo, m_hi, magic);
+    }
 }
 
 // Step j's matrix work on the swizzled x slot and the W tile.
+template <int WAVES>
 __device__ __forceinline__ void dma_mma(const uint8_t* xslot, const uint16_t* Bs, int wm, int wn, int lane,
-                                        f32x16 (&acc)[kPTM][kPTN]) {
+                                        f32x16 (&acc)[DmaShape<WAVES>::kTM][DmaShape<WAVES>::kTN]) {
+    constexpr int TM = DmaShape<WAVES>::kTM, TN = DmaShape<WAVES>::kTN;
     const uint16_t* bb = Bs + (wn * 64 + (lane & 31)) * kPLd + 8 * (lane >> 5);
 #pragma unroll
     for (int sub = 0; sub < kPBK / 16; ++sub) {
-        u32x4 a[kPTM], b[kPTN];
+        u32x4 a[TM], b[TN];
         const int c = 2 * sub + (lane >> 5);
 #pragma unroll
-        for (int f = 0; f < kPTM; ++f) {
-            const int row = wm * 64 + f * 32 + (lane & 31);
+        for (int f = 0; f < TM; ++f) {
+            const int row = wm * TM * 32 + f * 32 + (lane & 31);
             a[f] = *reinterpret_cast<const u32x4*>(xslot + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
         }
 #pragma unroll
-        for (int g = 0; g < kPTN; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+        for (int g = 0; g < TN; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
 #pragma unroll
-        for (int f = 0; f < kPTM; ++f)
+        for (int f = 0; f < TM; ++f)
 #pragma unroll
-            for (int g = 0; g < kPTN; ++g)
+            for (int g = 0; g < TN; ++g)
                 acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[f]),
                                                                    __builtin_bit_cast(bf16x8, b[g]), acc[f][g], 0, 0, 0);
     }
 }
 
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_dma_kernel(
+// ---------------------------------------------------------------- prefill GEMM, specialised wavefronts
+// The LDS-DMA form with the work split by role, so that the matrix pipe, the
+// memory pipe and the vector ALU are kept busy at the same time instead of
+// in turns: of the 8 wavefronts (two per SIMD), 4 "consumers" (a 2 x 2 grid
+// of 128 x 64 sub-tiles) only read operands from LDS and issue
+// v_mfma_f32_32x32x16_bf16, and 4 "producers" issue the DMA of later steps
+// and decode the next step's weights into the free W tile. One barrier per
+// step hands the buffers over.
+constexpr int kWsThreads = 512;
+
+__global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_ws_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
+    using S = DmaShape<4>;  // producer DMA split and consumer tile shape of the 4-wavefront form
+    constexpr int TM = S::kTM, TN = S::kTN;
     __shared__ __attribute__((aligned(1024))) uint8_t xring[kDStages][kDXBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wring[kDStages][kDWBytes];
     __shared__ __attribute__((aligned(256))) uint8_t sring[kDStages][kDSBytes];
@@ -543,7 +584,10 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const bool producer = wave >= 4;
+    const int role_wave = wave & 3;     // index within the role
+    const int ptid = tid - 256;         // producer thread index (valid for producers)
+    const int wm = role_wave >> 1, wn = role_wave & 1;
     const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
     const int tiles = tiles_m * tiles_n;
     int t = blockIdx.x;
@@ -559,58 +603,71 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
     const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
 
-    DmaPlan d;
+    // The two roles run separate loops (so neither holds the other's
+    // registers) with the same sequence of barriers: one before the loop
+    // (packed W of step 0 landed), one per step.
+    if (producer) {
+        DmaPlan<4> d;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 8 * (4 * wave + j) + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        d.x[j] = (uint32_t)(row * K * 2 + 16 * c);
-    }
-    if (wave < 4) {
-        d.w = (uint32_t)((32 * wave + (lane >> 1)) * (K / 2) + 16 * (lane & 1));
-    } else {
-        d.w = (uint32_t)((64 * ((wave - 4) & 1) + lane) * G * 2);
+        for (int j = 0; j < S::kXB; ++j) {
+            const int row = 8 * (S::kXB * role_wave + j) + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            d.x[j] = (uint32_t)(row * K * 2 + 16 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < S::kOB; ++i) {
+            const int q = role_wave * S::kOB + i;
+            if (q < 4)
+                d.o[i] = (uint32_t)((32 * q + (lane >> 1)) * (K / 2) + 16 * (lane & 1));
+            else
+                d.o[i] = (uint32_t)((64 * ((q - 4) & 1) + lane) * G * 2);
+        }
+        // Prologue: packed W of step 0 (with x of a nonexistent step, so every
+        // batch has the same instruction count), then steps (0, 1) and (1, 2).
+        dma_issue<4>(d, role_wave, steps, 0, steps, xring[2], wring[0], sring[0], bring[0], xsrc, wsrc, ssrc, bsrc);
+        dma_issue<4>(d, role_wave, 0, 1, steps, xring[0], wring[1], sring[1], bring[1], xsrc, wsrc, ssrc, bsrc);
+        dma_issue<4>(d, role_wave, 1, 2, steps, xring[1], wring[2], sring[2], bring[2], xsrc, wsrc, ssrc, bsrc);
+        wait_vmcnt<2 * S::kPerIter>();
+        raw_barrier();  // packed W(0) of every producer visible
+        dma_decode<4>(ptid, wring[0], sring[0], bring[0], Bs[0], m_lo, m_hi, magic);
+        for (int j = 0; j < steps; ++j) {
+            const int cur = j % kDStages, nxt = (j + 1) % kDStages, fut = (j + 2) % kDStages;
+            wait_vmcnt<S::kPerIter>();  // this wavefront's DMA of x(j) and packed W(j + 1)
+            wait_lgkmcnt0();            // this wavefront's decode of W(j)
+            raw_barrier();
+            // Decode W(j + 1) into the free W tile, then x(j + 2) into slot fut
+            // (last read by the consumers in iteration j - 1) and packed
+            // W(j + 3) into slot cur (last decoded in iteration j - 1).
+            dma_decode<4>(ptid, wring[nxt], sring[nxt], bring[nxt], Bs[(j + 1) & 1], m_lo, m_hi, magic);
+            dma_issue<4>(d, role_wave, j + 2, j + 3, steps, xring[fut], wring[cur], sring[cur], bring[cur], xsrc, wsrc,
+                         ssrc, bsrc);
+        }
+        return;
     }
 
-    f32x16 acc[kPTM][kPTN];
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int f = 0; f < kPTM; ++f)
+    for (int f = 0; f < TM; ++f)
 #pragma unroll
-        for (int g = 0; g < kPTN; ++g)
+        for (int g = 0; g < TN; ++g)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[f][g][e] = 0.f;
-
-    // Prologue: packed W of step 0 (with x of a nonexistent step, so every
-    // batch is 5 instructions), then steps (0, 1) and (1, 2).
-    dma_issue(d, wave, steps, 0, steps, xring[2], wring[0], sring[0], bring[0], xsrc, wsrc, ssrc, bsrc);
-    dma_issue(d, wave, 0, 1, steps, xring[0], wring[1], sring[1], bring[1], xsrc, wsrc, ssrc, bsrc);
-    dma_issue(d, wave, 1, 2, steps, xring[1], wring[2], sring[2], bring[2], xsrc, wsrc, ssrc, bsrc);
-    wait_vmcnt<2 * kDPerIter>();
     raw_barrier();
-    dma_decode(tid, wring[0], sring[0], bring[0], Bs[0], m_lo, m_hi, magic);
-
     for (int j = 0; j < steps; ++j) {
-        const int cur = j % kDStages, nxt = (j + 1) % kDStages, fut = (j + 2) % kDStages;
-        wait_vmcnt<kDPerIter>();  // this wavefront's DMA of x(j) and packed W(j + 1)
-        wait_lgkmcnt0();          // this wavefront's decode of W(j)
         raw_barrier();
-        // x(j + 2) and packed W(j + 3): slot fut was last read in iteration j - 1.
-        dma_issue(d, wave, j + 2, j + 3, steps, xring[fut], wring[cur], sring[cur], bring[cur], xsrc, wsrc, ssrc,
-                  bsrc);
-        dma_decode(tid, wring[nxt], sring[nxt], bring[nxt], Bs[(j + 1) & 1], m_lo, m_hi, magic);
-        dma_mma(xring[cur], Bs[j & 1], wm, wn, lane, acc);
+        dma_mma<4>(xring[j % kDStages], Bs[j & 1], wm, wn, lane, acc);
     }
 
     const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
 #pragma unroll
-    for (int g = 0; g < kPTN; ++g) {
+    for (int g = 0; g < TN; ++g) {
         const int n = n0 + wn * 64 + g * 32 + (lane & 31);
         const uint32_t voff = n < N ? (uint32_t)((4 * (lane >> 5)) * N + n) * 2u : kOob;
 #pragma unroll
-        for (int f = 0; f < kPTM; ++f)
+        for (int f = 0; f < TM; ++f)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = wm * 64 + f * 32 + 8 * (e >> 2) + (e & 3);
+                const int row = wm * TM * 32 + f * 32 + 8 * (e >> 2) + (e & 3);
                 __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[f][g][e]), ysrc, voff, row * N * 2, 0);
             }
     }
@@ -659,7 +716,7 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
     } else {
         const unsigned tiles = (unsigned)(((M + kPBM - 1) / kPBM) * ((N + kPBN - 1) / kPBN));
         if (K % kPBK == 0)
-            hipLaunchKernelGGL(qmm_affine4_prefill_dma_kernel, dim3(tiles), dim3(kPThreads), 0, s, w, scales, biases,
+            hipLaunchKernelGGL(qmm_affine4_prefill_ws_kernel, dim3(tiles), dim3(kWsThreads), 0, s, w, scales, biases,
                                x, y, (int)M, (int)K, (int)N);
         else
             hipLaunchKernelGGL(qmm_affine4_prefill_kernel<true>, dim3(tiles), dim3(kPThreads), 0, s, w, scales, biases,
