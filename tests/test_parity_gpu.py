@@ -99,6 +99,9 @@ def test_qmv_affine4(K, N, seed):
     (260, 192, 96),                       # K % 64 == 0 prefill path: 3 K steps (ring wrap), ragged M and N
     (513, 320, 416),                      # 5 K steps, M one past two 256-row tiles
     (256, 64, 128),                       # a single K step, exact tiles
+    (300, 128, 256),                      # 2 K steps (producer loop tail of 2)
+    (257, 256, 160),                      # 4 K steps (one unrolled round + a tail of 1)
+    (384, 1024, 384),                     # 16 K steps, several tiles each way
 ])
 def test_qmm_affine4_small(M, K, N):
     c = synth.affine_case(M, K, N, seed=M + K + N)

@@ -13,6 +13,8 @@
 // sub-tile and issues v_mfma_f32_16x16x32_{bf16,f16}; LDS rows are padded
 // to 80 bytes so the 16-byte operand reads of a 16-lane group hit distinct
 // banks.
+#include <type_traits>
+
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
@@ -415,47 +417,57 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // ---------------------------------------------------------------- prefill GEMM, LDS-DMA form
-// The same 256 x 128 tile and K step of 64 for K % 64 == 0, fed by
-// buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) so the data in flight does
-// not occupy registers and the prefetch can run two steps ahead of the
-// matrix-core work. WAVES = 8 (two per SIMD, 64 x 64 sub-tiles) or 4 (one
-// per SIMD, 128 x 64 sub-tiles, which cuts the LDS operand reads by a
-// quarter). LDS:
-//   x ring   3 x [256 rows x 128 B]: row r's 16-byte chunk c at slot
-//            c ^ ((r / 2) % 8), which keeps the 32x32x16 A-operand reads
-//            (32 rows x 2 chunks per instruction) conflict-free;
-//   W ring   3 x [128 rows x 32 B] packed nibbles of the step's two groups,
-//            plus 3 x [128] scale pairs and 3 x [128] bias pairs;
-//   W tiles  2 x [128 rows x 144 B] decoded bf16 operands.
-// Iteration j: wait for this wavefront's DMA of step j (x) and j + 1 (packed
-// W), barrier, run step j's matrix work, issue the DMA of steps j + 2 / j + 3
-// and decode step j + 1's weights into the free W tile (the matrix
-// instructions run on while these issue). Every wavefront issues the same
-// number of DMA instructions per iteration, so one s_waitcnt covers the data
-// two iterations old. Waits are explicit and the barrier carries no memory
-// fence, which would wait for all DMA in flight.
-constexpr int kDStages = 3;
-constexpr int kDXBytes = kPBM * 128;           // x ring slot
-constexpr int kDWBytes = kPBN * 32;            // packed W ring slot
-constexpr int kDSBytes = kPBN * 4;             // scale (or bias) pairs ring slot
+// The same 256 x 128 tile and K step of 64 for K % 64 == 0, with the work
+// split by role so that the matrix pipe, the memory pipe and the vector ALU
+// run at the same time: of the 8 wavefronts (two per SIMD), 4 consumers (a
+// 2 x 2 grid of 128 x 64 sub-tiles, 8 accumulator tiles each) only read
+// operands from LDS and issue v_mfma_f32_32x32x16_bf16; 4 producers stream
+// the next steps in and decode the weights. One barrier per step hands the
+// buffers over. Data paths:
+//   x       buffer-to-LDS DMA (buffer_load_dwordx4 ... lds: 8 rows x 128 B per
+//           instruction, two steps ahead) into a 3-slot ring of
+//           [256 rows x 128 B]; row r's 16-byte chunk c sits at slot
+//           c ^ ((r / 2) % 8), which keeps the A-operand reads (32 rows x 2
+//           chunks per instruction) conflict-free. DMA'd data occupies no
+//           registers, and LDS-DMA moves these rows faster than loads into
+//           registers do.
+//   packed W, scales, biases
+//           plain loads into producer registers three steps ahead (a 3-deep
+//           register ring, the producer loop unrolled by 3): lane l of
+//           producer p holds row 32 p + l / 2, group l % 2 of the step
+//           (16 bytes of nibbles and the group's scale and bias), which is
+//           exactly what it decodes.
+//   W tile  2 x [128 rows x 144 B] decoded bf16 operands (the 144-byte row
+//           keeps 16 consecutive rows' operand reads conflict-free).
+// All producer memory instructions are inline asm with explicit waits: the
+// compiler does not count asm-issued loads, and its own waits would stall on
+// the DMA in flight. Every producer issues the same number (kWsPerIter) per
+// iteration, so one s_waitcnt covers the data two iterations old; the
+// barrier carries no memory fence, which would wait for all DMA in flight.
+constexpr int kWsThreads = 512;
+constexpr int kWsXb = 8;                // x DMA instructions (1 KB each) per producer per step
+constexpr int kWsPerIter = kWsXb + 3;   // + packed W, scale, bias loads
+constexpr int kDXBytes = kPBM * 128;    // x ring slot
 
 // Byte address of an LDS object, for inline-asm LDS instructions.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// Buffer-to-LDS DMA of 16 (or 4) bytes per lane: lane l's bytes land at
-// lds + 16 l (or 4 l); M0 carries the wave-uniform LDS base. Issued as inline
-// asm so that the compiler, which cannot tell DMA targets apart, does not
-// wait for all DMA in flight before every LDS access; completion is awaited
-// explicitly (wait_vmcnt) before the data is read. Nothing else in these
-// kernels uses M0.
+// Buffer-to-LDS DMA of 16 bytes per lane: lane l's bytes land at lds + 16 l;
+// M0 carries the wave-uniform LDS base. Issued as inline asm so that the
+// compiler, which cannot tell DMA targets apart, does not wait for all DMA in
+// flight before every LDS access; completion is awaited explicitly
+// (wait_vmcnt) before the data is read. Nothing else in these kernels uses M0.
 __device__ __forceinline__ void lds_dma16(const __amdgpu_buffer_rsrc_t& rsrc, void* lds, uint32_t voff, int soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  ::"s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff));
 }
-__device__ __forceinline__ void lds_dma4(const __amdgpu_buffer_rsrc_t& rsrc, void* lds, uint32_t voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff));
+// Loads into registers, also counted by hand (see above).
+__device__ __forceinline__ void asm_load_b128(u32x4& d, const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int soff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(d) : "v"(voff), "s"(r), "s"(soff));
+}
+__device__ __forceinline__ void asm_load_u16(uint32_t& d, const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int soff) {
+    asm volatile("buffer_load_ushort %0, %1, %2, %3 offen" : "=v"(d) : "v"(voff), "s"(r), "s"(soff));
 }
 // s_barrier with a compiler-only memory clobber (no hardware wait).
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -468,206 +480,155 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
 
-template <int WAVES>
-struct DmaShape {
-    static constexpr int kThreads = WAVES * kWave;
-    static constexpr int kXB = 32 / WAVES;           // x DMA blocks (1 KB) per wavefront
-    static constexpr int kOB = 8 / WAVES;            // packed-W / scale / bias DMA instructions per wavefront
-    static constexpr int kPerIter = kXB + kOB;       // DMA instructions per wavefront per iteration
-    static constexpr int kWGM = WAVES / 2;           // wavefronts along M (2 along N)
-    static constexpr int kTM = 256 / kWGM / 32;      // 32-row tiles per wavefront
-    static constexpr int kTN = 2;                    // 32-column tiles per wavefront
-    static constexpr int kWPT = 1024 / kThreads;     // packed words decoded per thread per step
+// One producer lane's share of a step's weights: 4 words (32 nibbles, one
+// quantisation group of one row) with the group's scale and bias bits.
+struct WsWeights {
+    u32x4 words;
+    uint32_t s, b;
 };
+// Makes the registers of a ring entry opaque to the compiler after the wait
+// that covers their loads, so that no use is scheduled before that wait.
+__device__ __forceinline__ void ws_fence(WsWeights& e) { asm volatile("" : "+v"(e.words), "+v"(e.s), "+v"(e.b)); }
 
-template <int WAVES>
-struct DmaPlan {
-    uint32_t x[DmaShape<WAVES>::kXB];  // per-lane x offsets (row r, swizzled chunk)
-    uint32_t o[DmaShape<WAVES>::kOB];  // packed W / scale / bias offsets
-};
-
-// "Other" DMA block q (0..7) of a step: 0-3 packed words (1 KB, 32 rows
-// each), 4-5 scale pairs, 6-7 bias pairs (256 B, 64 rows each). Wavefront w
-// issues blocks w * kOB .. w * kOB + kOB - 1.
-template <int WAVES>
-__device__ __forceinline__ void dma_issue(const DmaPlan<WAVES>& d, int wave, int kt, int kw, int steps, uint8_t* xslot,
-                                          uint8_t* wslot, uint8_t* sslot, uint8_t* bslot,
-                                          const __amdgpu_buffer_rsrc_t& xsrc, const __amdgpu_buffer_rsrc_t& wsrc,
-                                          const __amdgpu_buffer_rsrc_t& ssrc, const __amdgpu_buffer_rsrc_t& bsrc) {
-    using S = DmaShape<WAVES>;
-    const bool xl = kt < steps, wl = kw < steps;
-    const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
-#pragma unroll
-    for (int j = 0; j < S::kXB; ++j) lds_dma16(xsrc, xslot + (S::kXB * wave + j) * 1024, xl ? d.x[j] : kOob, kx);
-#pragma unroll
-    for (int i = 0; i < S::kOB; ++i) {
-        const int q = wave * S::kOB + i;  // wave-uniform
-        if (q < 4)
-            lds_dma16(wsrc, wslot + q * 1024, wl ? d.o[i] : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
-        else if (q < 6)
-            lds_dma4(ssrc, sslot + (q - 4) * 256, wl ? d.o[i] : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
-        else
-            lds_dma4(bsrc, bslot + (q - 6) * 256, wl ? d.o[i] : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
-    }
-}
-
-// Decodes one step's weights from the packed ring slot into a W tile: each
-// row's 8 words (two groups) are split over 8 / kWPT threads.
-template <int WAVES>
-__device__ __forceinline__ void dma_decode(int tid, const uint8_t* wslot, const uint8_t* sslot, const uint8_t* bslot,
-                                           uint16_t* Bs, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
-    constexpr int WPT = DmaShape<WAVES>::kWPT, TPR = 8 / WPT;
-    const int r = tid / TPR, w0 = (tid % TPR) * WPT, g = w0 / 4;
-    const uint32_t sp = *reinterpret_cast<const uint32_t*>(sslot + 4 * r);
-    const uint32_t bp = *reinterpret_cast<const uint32_t*>(bslot + 4 * r);
-    const float s = bf16_bits_to_f32(g ? (sp >> 16) : (sp & 0xFFFFu));
-    const float b = bf16_bits_to_f32(g ? (bp >> 16) : (bp & 0xFFFFu));
+// Decodes one ring entry into its 32 bf16 operands (row r, k 32 g .. 32 g + 31).
+__device__ __forceinline__ void ws_decode(const WsWeights& e, uint16_t* dst, uint32_t m_lo, uint32_t m_hi,
+                                          uint32_t magic) {
+    const float s = bf16_bits_to_f32(e.s), b = bf16_bits_to_f32(e.b);
     const float c = __builtin_fmaf(-1024.f, s, b), s16 = 0.0625f * s, c16 = __builtin_fmaf(-64.f, s, b);
-    uint16_t* dst = Bs + r * kPLd + 8 * w0;
-    if constexpr (WPT == 2) {
-        const u32x2 words = *reinterpret_cast<const u32x2*>(wslot + r * 32 + 4 * w0);
-        *reinterpret_cast<u32x4*>(dst) = affine_word_bf16(words[0], s, c, s16, c16, m_lo, m_hi, magic);
-        *reinterpret_cast<u32x4*>(dst + 8) = affine_word_bf16(words[1], s, c, s16, c16, m_lo, m_hi, magic);
-    } else {
-        const u32x4 words = *reinterpret_cast<const u32x4*>(wslot + r * 32 + 4 * w0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(dst + 8 * i) = affine_word_bf16(words[i], s, c, s16, c16, m_lo, m_hi, magic);
-    }
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(dst + 8 * i) = affine_word_bf16(e.words[i], s, c, s16, c16, m_lo, m_hi, magic);
 }
 
-// Step j's matrix work on the swizzled x slot and the W tile.
-template <int WAVES>
-__device__ __forceinline__ void dma_mma(const uint8_t* xslot, const uint16_t* Bs, int wm, int wn, int lane,
-                                        f32x16 (&acc)[DmaShape<WAVES>::kTM][DmaShape<WAVES>::kTN]) {
-    constexpr int TM = DmaShape<WAVES>::kTM, TN = DmaShape<WAVES>::kTN;
+// Step j's matrix work for a consumer: 4 sub-steps of k16, each 4 A reads
+// (swizzled x slot), 2 B reads (W tile) and 8 MFMAs.
+__device__ __forceinline__ void ws_mma(const uint8_t* xslot, const uint16_t* Bs, int wm, int wn, int lane,
+                                       f32x16 (&acc)[4][2]) {
     const uint16_t* bb = Bs + (wn * 64 + (lane & 31)) * kPLd + 8 * (lane >> 5);
 #pragma unroll
     for (int sub = 0; sub < kPBK / 16; ++sub) {
-        u32x4 a[TM], b[TN];
+        u32x4 a[4], b[2];
         const int c = 2 * sub + (lane >> 5);
 #pragma unroll
-        for (int f = 0; f < TM; ++f) {
-            const int row = wm * TM * 32 + f * 32 + (lane & 31);
+        for (int f = 0; f < 4; ++f) {
+            const int row = wm * 128 + f * 32 + (lane & 31);
             a[f] = *reinterpret_cast<const u32x4*>(xslot + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
         }
 #pragma unroll
-        for (int g = 0; g < TN; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+        for (int g = 0; g < 2; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
 #pragma unroll
-        for (int f = 0; f < TM; ++f)
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int g = 0; g < TN; ++g)
+            for (int g = 0; g < 2; ++g)
                 acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[f]),
                                                                    __builtin_bit_cast(bf16x8, b[g]), acc[f][g], 0, 0, 0);
     }
 }
 
-// ---------------------------------------------------------------- prefill GEMM, specialised wavefronts
-// The LDS-DMA form with the work split by role, so that the matrix pipe, the
-// memory pipe and the vector ALU are kept busy at the same time instead of
-// in turns: of the 8 wavefronts (two per SIMD), 4 "consumers" (a 2 x 2 grid
-// of 128 x 64 sub-tiles) only read operands from LDS and issue
-// v_mfma_f32_32x32x16_bf16, and 4 "producers" issue the DMA of later steps
-// and decode the next step's weights into the free W tile. One barrier per
-// step hands the buffers over.
-constexpr int kWsThreads = 512;
-
 __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_ws_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
-    using S = DmaShape<4>;  // producer DMA split and consumer tile shape of the 4-wavefront form
-    constexpr int TM = S::kTM, TN = S::kTN;
-    __shared__ __attribute__((aligned(1024))) uint8_t xring[kDStages][kDXBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wring[kDStages][kDWBytes];
-    __shared__ __attribute__((aligned(256))) uint8_t sring[kDStages][kDSBytes];
-    __shared__ __attribute__((aligned(256))) uint8_t bring[kDStages][kDSBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t xring[3][kDXBytes];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool producer = wave >= 4;
     const int role_wave = wave & 3;     // index within the role
-    const int ptid = tid - 256;         // producer thread index (valid for producers)
-    const int wm = role_wave >> 1, wn = role_wave & 1;
     const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
     const int tiles = tiles_m * tiles_n;
     int t = blockIdx.x;
     if (tiles % 8 == 0) t = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
     const int m0 = (t / tiles_n) * kPBM, n0 = (t % tiles_n) * kPBN;
     const int G = K / 32, steps = K / kPBK;
-
     const int mrows = min(kPBM, M - m0), nrows = min(kPBN, N - n0);
-    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
-    const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * (K / 2), (uint32_t)(nrows * (K / 2)));
-    const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
-    const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
-    const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
 
     // The two roles run separate loops (so neither holds the other's
-    // registers) with the same sequence of barriers: one before the loop
-    // (packed W of step 0 landed), one per step.
-    if (producer) {
-        DmaPlan<4> d;
+    // registers) with the same sequence of barriers, one per step: at barrier
+    // j, x(j) has landed and W(j) is decoded, and the consumers are done with
+    // the buffers of step j - 1.
+    if (wave >= 4) {
+        const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+        const __amdgpu_buffer_rsrc_t wsrc =
+            make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * (K / 2), (uint32_t)(nrows * (K / 2)));
+        const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
+        const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
+        const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
+        uint32_t xo[kWsXb];  // x rows 64 p .. 64 p + 63, 8 per instruction, swizzled chunk order
 #pragma unroll
-        for (int j = 0; j < S::kXB; ++j) {
-            const int row = 8 * (S::kXB * role_wave + j) + (lane >> 3);
-            const int c = (lane & 7) ^ ((row >> 1) & 7);
-            d.x[j] = (uint32_t)(row * K * 2 + 16 * c);
+        for (int i = 0; i < kWsXb; ++i) {
+            const int row = 8 * (kWsXb * role_wave + i) + (lane >> 3);
+            xo[i] = (uint32_t)(row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7)));
         }
+        const int r = 32 * role_wave + (lane >> 1), g = lane & 1;
+        const uint32_t wo = (uint32_t)(r * (K / 2) + 16 * g), so = (uint32_t)((r * G + g) * 2);
+        uint16_t* const bdst = Bs[0] + r * kPLd + 32 * g;
+        WsWeights ring[3];
+        // x of step kt into xslot, the weights of step kw into e (past the end: zeros).
+        auto issue = [&](int kt, int kw, uint8_t* xslot, WsWeights& e) {
+            const bool xl = kt < steps, wl = kw < steps;
+            const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
 #pragma unroll
-        for (int i = 0; i < S::kOB; ++i) {
-            const int q = role_wave * S::kOB + i;
-            if (q < 4)
-                d.o[i] = (uint32_t)((32 * q + (lane >> 1)) * (K / 2) + 16 * (lane & 1));
-            else
-                d.o[i] = (uint32_t)((64 * ((q - 4) & 1) + lane) * G * 2);
-        }
-        // Prologue: packed W of step 0 (with x of a nonexistent step, so every
-        // batch has the same instruction count), then steps (0, 1) and (1, 2).
-        dma_issue<4>(d, role_wave, steps, 0, steps, xring[2], wring[0], sring[0], bring[0], xsrc, wsrc, ssrc, bsrc);
-        dma_issue<4>(d, role_wave, 0, 1, steps, xring[0], wring[1], sring[1], bring[1], xsrc, wsrc, ssrc, bsrc);
-        dma_issue<4>(d, role_wave, 1, 2, steps, xring[1], wring[2], sring[2], bring[2], xsrc, wsrc, ssrc, bsrc);
-        wait_vmcnt<2 * S::kPerIter>();
-        raw_barrier();  // packed W(0) of every producer visible
-        dma_decode<4>(ptid, wring[0], sring[0], bring[0], Bs[0], m_lo, m_hi, magic);
-        for (int j = 0; j < steps; ++j) {
-            const int cur = j % kDStages, nxt = (j + 1) % kDStages, fut = (j + 2) % kDStages;
-            wait_vmcnt<S::kPerIter>();  // this wavefront's DMA of x(j) and packed W(j + 1)
-            wait_lgkmcnt0();            // this wavefront's decode of W(j)
+            for (int i = 0; i < kWsXb; ++i)
+                lds_dma16(xsrc, xslot + (kWsXb * role_wave + i) * 1024, xl ? xo[i] : kOob, kx);
+            asm_load_b128(e.words, wsrc, wl ? wo : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
+            asm_load_u16(e.s, ssrc, wl ? so : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+            asm_load_u16(e.b, bsrc, wl ? so : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+        };
+        // Prologue: W(0) (with x of a nonexistent step, so every batch has the
+        // same instruction count), then (x(0), W(1)) and (x(1), W(2)).
+        issue(steps, 0, xring[2], ring[0]);
+        issue(0, 1, xring[0], ring[1]);
+        issue(1, 2, xring[1], ring[2]);
+        wait_vmcnt<2 * kWsPerIter>();
+        ws_fence(ring[0]);
+        ws_decode(ring[0], bdst, m_lo, m_hi, magic);
+        // Iteration j (j mod 3 == S0): wait for the batch of iteration j - 2
+        // (x(j), W(j + 1)), barrier, decode W(j + 1) into the free W tile,
+        // then issue x(j + 2) into the slot the consumers left in iteration
+        // j - 1 and W(j + 3) into the ring entry decoded in iteration j - 1.
+        auto body = [&](auto slot, int j) {
+            constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+            wait_vmcnt<kWsPerIter>();
+            wait_lgkmcnt0();  // this wavefront's decode of W(j)
+            ws_fence(ring[S1]);
             raw_barrier();
-            // Decode W(j + 1) into the free W tile, then x(j + 2) into slot fut
-            // (last read by the consumers in iteration j - 1) and packed
-            // W(j + 3) into slot cur (last decoded in iteration j - 1).
-            dma_decode<4>(ptid, wring[nxt], sring[nxt], bring[nxt], Bs[(j + 1) & 1], m_lo, m_hi, magic);
-            dma_issue<4>(d, role_wave, j + 2, j + 3, steps, xring[fut], wring[cur], sring[cur], bring[cur], xsrc, wsrc,
-                         ssrc, bsrc);
+            ws_decode(ring[S1], bdst + ((j + 1) & 1) * (kPBN * kPLd), m_lo, m_hi, magic);
+            issue(j + 2, j + 3, xring[S2], ring[S0]);
+        };
+        int j = 0;
+        for (; j + 3 <= steps; j += 3) {
+            body(std::integral_constant<int, 0>{}, j);
+            body(std::integral_constant<int, 1>{}, j + 1);
+            body(std::integral_constant<int, 2>{}, j + 2);
         }
+        if (j < steps) body(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
+        wait_vmcnt<0>();  // the trailing (all-zero) DMA lands before this wavefront ends
         return;
     }
 
-    f32x16 acc[TM][TN];
+    const int wm = role_wave >> 1, wn = role_wave & 1;
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int f = 0; f < TM; ++f)
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int g = 0; g < TN; ++g)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[f][g][e] = 0.f;
-    raw_barrier();
     for (int j = 0; j < steps; ++j) {
         raw_barrier();
-        dma_mma<4>(xring[j % kDStages], Bs[j & 1], wm, wn, lane, acc);
+        ws_mma(xring[j % 3], Bs[j & 1], wm, wn, lane, acc);
     }
 
     const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
 #pragma unroll
-    for (int g = 0; g < TN; ++g) {
+    for (int g = 0; g < 2; ++g) {
         const int n = n0 + wn * 64 + g * 32 + (lane & 31);
         const uint32_t voff = n < N ? (uint32_t)((4 * (lane >> 5)) * N + n) * 2u : kOob;
 #pragma unroll
-        for (int f = 0; f < TM; ++f)
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = wm * TM * 32 + f * 32 + 8 * (e >> 2) + (e & 3);
+                const int row = wm * 128 + f * 32 + 8 * (e >> 2) + (e & 3);
                 __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[f][g][e]), ysrc, voff, row * N * 2, 0);
             }
     }
