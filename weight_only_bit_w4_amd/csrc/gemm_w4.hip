@@ -247,8 +247,6 @@ constexpr int kPThreads = 512;
 constexpr int kPLd = kPBK + 8;  // LDS row stride in 16-bit elements (144 bytes)
 constexpr int kPTM = 2, kPTN = 2;  // 32 x 32 accumulator tiles per wavefront
 
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-
 struct PrefillRegs {
     u32x4 x[4];       // x tile pieces i: row (tid / 8) + 64 i, 16-byte chunk tid % 8
     u32x2 w;          // two words (16 nibbles) of one quantisation group of one weight row

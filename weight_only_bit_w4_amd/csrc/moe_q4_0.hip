@@ -6,13 +6,16 @@
 //  1. moe_group_kernel: workgroup 0 counts the routed rows per expert, scans
 //     the counts and scatters row indices into per-expert lists (the page's
 //     htpe / hids); the other workgroups store x as binary16 (the matrix-core
-//     operand type). Stream order makes both visible to launch 2.
+//     operand type), each 32-wide K block in the order the weight decode
+//     produces it. Stream order makes both visible to launch 2.
 //  2. moe_gemm_kernel: one workgroup per (expert, 128 weight rows) reads that
-//     slice of the expert's weights exactly once and applies it to every
-//     routed row of the expert (up to 64 per pass) with
-//     v_mfma_f32_16x16x32_f16, f32 accumulation. The routed rows' x is staged
-//     in LDS per 256-wide K window; each lane decodes its Q4_0 nibbles to fp16
-//     (q - 8) * d in registers.
+//     slice of the expert's weights exactly once per 32 routed rows and
+//     applies it with v_mfma_f32_32x32x16_f16, f32 accumulation. Weights and
+//     the routed rows' x stream through LDS rings by buffer-to-LDS DMA, one
+//     256-wide K window (8 Q4_0 blocks, 144 bytes of each weight row) per
+//     step; each lane decodes two qs dwords per block into fp16 (q - 8) d.
+#include <type_traits>
+
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
@@ -25,12 +28,16 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
                                                                   int n_rows, int n_experts, int N, int64_t x_count,
                                                                   IdScratchLayout lay) {
     if (blockIdx.x > 0) {
-        // x -> binary16, 8 values per thread per step.
+        // x -> binary16, 8 values per thread per step: output positions
+        // 8c .. 8c + 7 of a 32-wide block hold k = 4c .. 4c + 3 and
+        // 16 + 4c .. 16 + 4c + 3 (the order q4_0_operand yields weights in).
         uint16_t* xh = reinterpret_cast<uint16_t*>(scratch + lay.xh);
         const int64_t stride = (int64_t)(gridDim.x - 1) * kGroupThreads * 8;
         for (int64_t i = ((int64_t)(blockIdx.x - 1) * kGroupThreads + threadIdx.x) * 8; i < x_count; i += stride) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(x + i);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(x + i + 4);
+            const int64_t blk = i & ~(int64_t)31;
+            const int c = (int)((i & 31) >> 3);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(x + blk + 4 * c);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(x + blk + 16 + 4 * c);
             *reinterpret_cast<u32x4*>(xh + i) = u32x4{pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]),
                                                       pack_f16x2(b[0], b[1]), pack_f16x2(b[2], b[3])};
         }
@@ -90,125 +97,271 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
     if (tid == 0) *reinterpret_cast<uint32_t*>(scratch + lay.bad_ids) = bad_s;
 }
 
-constexpr int kMoeThreads = 256;
-constexpr int kMoeNS = 2;                       // 16-row weight sub-tiles per wavefront
-constexpr int kMoeBN = 4 * 16 * kMoeNS;         // weight rows per workgroup
-constexpr int kMoeMT = 4;                       // 16-row routed tiles per pass
-constexpr int kMoeWin = 256;                    // K per window (8 Q4_0 blocks)
-constexpr int kMoeXLd = kMoeWin + 8;            // padded LDS row, fp16 elements
+constexpr int kMoeWaves = 16;          // 2 halves of 64 weight rows x 8 blocks of a window
+constexpr int kMoeThreads = kMoeWaves * 64;
+constexpr int kMoeKSplit = 8;          // wavefronts per 64 weight rows, one block of each window each
+constexpr int kMoeBN = 128;            // weight rows per workgroup: 4 x 32
+constexpr int kMoeMR = 32;             // routed rows per pass (one 32x32 MFMA tile)
+constexpr int kMoeWinBlocks = 8;       // Q4_0 blocks per K window
+constexpr int kMoeWRow = kMoeWinBlocks * 18;            // 144 bytes of a weight row per window
+constexpr int kMoeWSlot = kMoeBN * kMoeWRow;            // 18 KB
+constexpr int kMoeWDma = kMoeWSlot / 1024;              // 18 DMA instructions per W window
+constexpr int kMoeXRow = kMoeWinBlocks * 32 * 2;        // 512 bytes of a routed row's x per window
+constexpr int kMoeXSlot = kMoeMR * kMoeXRow;            // 16 KB
+constexpr int kMoeXDma = kMoeXSlot / 1024;              // 16 DMA instructions per x window
+constexpr int kMoeWStages = 4, kMoeXStages = 3;
+constexpr uint32_t kMoeOob = 0x80000000u;
 
-// The eight weights a lane feeds one 16x16x32 fragment: from one aligned qs
-// dword (bytes 4i..4i+3 of a block) the elements 4i..4i+3 (low nibbles) and
-// 16+4i..16+4i+3 (high nibbles), as fp16 (q - 8) * d in that order.
-__device__ __forceinline__ u32x4 q4_0_fragment(uint32_t qs, uint32_t d2) {
-    uint32_t raw[4];
-    q4_0_biased_pairs(qs, raw);
-    const f16x2 bias = as_f16x2(0xE408E408u);  // -1032: (1024 + q) - 1032 = q - 8, exact
-    const f16x2 d = as_f16x2(d2);
+__device__ __forceinline__ uint32_t moe_lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Buffer-to-LDS DMA of 16 bytes per lane (lane l -> lds + 16 l). Inline asm
+// so the compiler does not wait for every DMA before each LDS access; the
+// issuing wavefront waits for its own DMA explicitly (moe_wait_vmcnt) before
+// the barrier that publishes it.
+__device__ __forceinline__ void moe_dma16(const __amdgpu_buffer_rsrc_t& rsrc, void* lds, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(moe_lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff));
+}
+template <int N>
+__device__ __forceinline__ void moe_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void moe_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// A scalar-cache load of one dword at a wave-uniform address. It is counted by
+// lgkmcnt, so waiting for it does not wait for the DMA in flight.
+__device__ __forceinline__ uint32_t moe_sload(const uint32_t* p) {
+    uint32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
+// One lane's B operand for one Q4_0 block: qs dword c (elements 4c .. 4c + 3
+// in the low nibbles, 16 + 4c .. 16 + 4c + 3 in the high ones) as fp16
+// (q - 8) d, in the order (4c, 4c+1) (4c+2, 4c+3) (16+4c, 16+4c+1)
+// (16+4c+2, 16+4c+3). Low nibbles become binary16 1024 + q and high ones
+// 64 + q (the nibble in mantissa bits 4..7 under exponent 2^6); subtracting
+// 1032 or 72 is exact and leaves q - 8, and the product with d rounds once.
+struct Q4Consts {
+    uint32_t m_lo, m_hi, magic_lo, magic_hi;  // held in VGPRs so each mask-and-insert is one v_and_or_b32
+};
+__device__ __forceinline__ u32x4 q4_0_operand(uint32_t qs, f16x2 dd, const Q4Consts& k) {
+    const uint32_t t0 = __builtin_amdgcn_perm(0u, qs, 0x0C010C00u);  // [b0, 0, b1, 0]
+    const uint32_t t1 = __builtin_amdgcn_perm(0u, qs, 0x0C030C02u);  // [b2, 0, b3, 0]
+    const f16x2 lo_bias = as_f16x2(0xE408E408u), hi_bias = as_f16x2(0xD480D480u);  // -1032, -72
     u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = as_u32((as_f16x2(raw[j]) + bias) * d);
+    o[0] = as_u32((as_f16x2(and_or_u32(t0, k.m_lo, k.magic_lo)) + lo_bias) * dd);
+    o[1] = as_u32((as_f16x2(and_or_u32(t1, k.m_lo, k.magic_lo)) + lo_bias) * dd);
+    o[2] = as_u32((as_f16x2(and_or_u32(t0, k.m_hi, k.magic_hi)) + hi_bias) * dd);
+    o[3] = as_u32((as_f16x2(and_or_u32(t1, k.m_hi, k.magic_hi)) + hi_bias) * dd);
     return o;
 }
 
+// Block b of one K window (ODD = b % 2) for a wavefront's 64 weight rows
+// (two 32-row tiles) against the 32 routed rows. Lane (n, h) = (lane % 32,
+// lane / 32) feeds MFMA k-step s with qs dword 2 s + h of row n of each tile;
+// the x operand of lane (m, h) is the same eight elements of routed row m,
+// which the xh order stores as 16 contiguous bytes (chunk 4 b + 2 s + h of
+// the window row, kept at slot chunk ^ (m % 32)); one x read serves both
+// tiles. A block past the row's end (a partial last window) gets d = 0, which
+// zeroes its weights whatever the ring holds there.
+template <int ODD>
+__device__ __forceinline__ void moe_block(const uint8_t* wrows, const uint8_t* xs, int lane, int b, bool live,
+                                          const Q4Consts& k, f32x16 (&acc)[2]) {
+    const int h = lane >> 5, m = lane & 31;
+    const uint8_t* xr = xs + m * kMoeXRow;
+    uint32_t dd[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t draw = *reinterpret_cast<const uint16_t*>(wrows + t * 32 * kMoeWRow + 18 * b);
+        dd[t] = (live ? draw : 0u) * 0x10001u;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const u32x4 xop = *reinterpret_cast<const u32x4*>(xr + 16 * ((4 * b + 2 * s + h) ^ m));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint8_t* blk = wrows + t * 32 * kMoeWRow + 18 * b;
+            // qs dword 2 s + h: 4-byte aligned for odd b, else two bytes past
+            // an aligned dword.
+            uint32_t qs;
+            if (ODD) {
+                qs = *reinterpret_cast<const uint32_t*>(blk + 2 + 8 * s + 4 * h);
+            } else {
+                const uint32_t lo = *reinterpret_cast<const uint32_t*>(blk + 8 * s + 4 * h);
+                const uint32_t hi = *reinterpret_cast<const uint32_t*>(blk + 8 * s + 4 * h + 4);
+                qs = __builtin_amdgcn_alignbyte(hi, lo, 2);
+            }
+            const u32x4 wop = q4_0_operand(qs, as_f16x2(dd[t]), k);
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, xop), __builtin_bit_cast(f16x8, wop),
+                                                            acc[t], 0, 0, 0);
+        }
+    }
+}
+
+// LDS (one array, so that the end-of-pass exchange can use all of it):
+//   W  kMoeWStages x [128 rows x 144 B]: the window's 8 blocks of each row,
+//      as stored (d then qs, 18 bytes a block);
+//   x  kMoeXStages x [32 rows x 512 B]: routed row r's 16-byte chunk p
+//      (xh order) at chunk slot p ^ (r % 32), which keeps the A-operand
+//      reads of 32 rows conflict-free.
+// Each of the 16 wavefronts issues its share of every window's DMA (W
+// kMoeWStages - 1 windows ahead, x kMoeXStages - 1 ahead) and waits for its
+// own DMA of window j before barrier j, after which every wavefront may read
+// window j and the slots of window j - 1 are free. Wavefront w takes weight
+// rows 64 (w % 2) .. + 63 and block w / 2 of each window (so each wavefront
+// runs at least 4 to a SIMD, as the decode's vector-ALU work needs); the eight
+// partial sums of a row half meet in LDS at the end of a pass.
+constexpr int kMoeLds = kMoeWStages * kMoeWSlot + kMoeXStages * kMoeXSlot;
+
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ scratch,
                                                                float* __restrict__ out, int N, int K, int top_k,
-                                                               uint64_t expert_stride, IdScratchLayout lay) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kMoeMT * 16 * kMoeXLd];
+                                                               uint64_t expert_stride, IdScratchLayout lay, int n_tokens) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kMoeLds];
+    uint8_t* const wring = lds;
+    uint8_t* const xring = lds + kMoeWStages * kMoeWSlot;
     const int tiles_n = (N + kMoeBN - 1) / kMoeBN;
     const int e = blockIdx.x / tiles_n;
-    const int nt = blockIdx.x % tiles_n;
+    const int n0 = (blockIdx.x % tiles_n) * kMoeBN;
     const uint32_t cnt = reinterpret_cast<const uint32_t*>(scratch + lay.counts)[e];
     if (cnt == 0u) return;
-    const uint32_t off = reinterpret_cast<const uint32_t*>(scratch + lay.offsets)[e];
-    const uint32_t* rows = reinterpret_cast<const uint32_t*>(scratch + lay.rows) + off;
-    const uint16_t* xh = reinterpret_cast<const uint16_t*>(scratch + lay.xh);
+    const uint32_t* rows =
+        reinterpret_cast<const uint32_t*>(scratch + lay.rows) + reinterpret_cast<const uint32_t*>(scratch + lay.offsets)[e];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = K / 32;
+    const int nwin = (nb + kMoeWinBlocks - 1) / kMoeWinBlocks;
+    const uint32_t row_bytes = (uint32_t)nb * 18u;
+    const int nrows = min(kMoeBN, N - n0);
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(w + (size_t)e * expert_stride + (size_t)n0 * row_bytes, (uint32_t)nrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(scratch + lay.xh, (uint32_t)((size_t)n_tokens * (size_t)K * 2u));
+    const Q4Consts k{vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u), vreg(0x54005400u)};
+    float* const red = reinterpret_cast<float*>(lds);  // pass-end exchange
+    static_assert((kMoeKSplit - 1) * 2 * 2 * 16 * 64 * 4 <= kMoeLds, "exchange area fits the rings");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = lane >> 4;  // block pair of the window this lane loads
-    const int nb = K / 32;    // blocks per row (even)
-    const size_t row_bytes = (size_t)nb * 18;
-    const uint8_t* wexp = w + (size_t)e * expert_stride;
-
-    for (uint32_t m0 = 0; m0 < cnt; m0 += kMoeMT * 16) {
-        const int mt = min(kMoeMT, (int)((cnt - m0 + 15) / 16));
-        f32x4 acc[kMoeMT][kMoeNS];
+    // DMA plan: W instruction i (lane l covers 16-byte chunk q = 64 i + l of
+    // the window: row q / 9, chunk q % 9) goes to wavefront i % 16, x
+    // instruction i (routed rows 2 i, 2 i + 1) to wavefront i.
+    static_assert(kMoeXDma == kMoeWaves, "one x DMA instruction per wavefront");
+    constexpr int kWPer = (kMoeWDma + kMoeWaves - 1) / kMoeWaves;
+    const int nw_dma = wave < kMoeWDma % kMoeWaves ? kWPer : kMoeWDma / kMoeWaves;
+    uint32_t wo[kWPer];
 #pragma unroll
-        for (int i = 0; i < kMoeMT; ++i)
-#pragma unroll
-            for (int j = 0; j < kMoeNS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kWPer; ++t) {
+        const int q = 64 * (wave + kMoeWaves * t) + lane, r = q / 9, j = q % 9;
+        wo[t] = r < nrows ? (uint32_t)r * row_bytes + 16u * (uint32_t)j : kMoeOob;
+    }
+    const int rh = wave & 1, b = wave >> 1;
+    const int nl = 64 * rh + (lane & 31);  // this lane's weight row in tile 0 (tile 1: + 32)
 
-        for (int k0 = 0; k0 < K; k0 += kMoeWin) {
-            // Stage x rows m0 .. m0 + 16 mt - 1 of this expert, window k0.
-            const int pieces = mt * 16 * (kMoeWin / 8);
-            for (int p = tid; p < pieces; p += kMoeThreads) {
-                const int rr = p / (kMoeWin / 8), kk = (p % (kMoeWin / 8)) * 8;
-                u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                if (m0 + rr < cnt && k0 + kk < K) {
-                    const uint32_t t = rows[m0 + rr] / (uint32_t)top_k;
-                    v = *reinterpret_cast<const u32x4*>(xh + (size_t)t * K + k0 + kk);
-                }
-                *reinterpret_cast<u32x4*>(xs + rr * kMoeXLd + kk) = v;
+    for (uint32_t m0 = 0; m0 < cnt; m0 += kMoeMR) {
+        // Routed rows past cnt are not loaded: their (stale) x only feeds
+        // output rows that are never stored.
+        const bool x_rows = m0 + 2u * (uint32_t)wave < cnt;
+        // Iteration j issues W(j + 3) and x(j + 2); the prologue runs the
+        // issues of iterations -3 .. -1 (x(-1) is all zeros, so every
+        // iteration of a wavefront issues the same count).
+        auto issue_w = [&](int j) {
+            const int win = j + kMoeWStages - 1;
+            const bool live = win < nwin;
+            uint8_t* slot = wring + (win % kMoeWStages) * kMoeWSlot;
+            const int soff = __builtin_amdgcn_readfirstlane(live ? win * kMoeWRow : 0);
+#pragma unroll
+            for (int t = 0; t < kWPer; ++t)
+                if (t < nw_dma) moe_dma16(wsrc, slot + 1024 * (wave + kMoeWaves * t), live ? wo[t] : kMoeOob, soff);
+        };
+        // W(0), W(1) need no row ids, so they go out first.
+        issue_w(-3);
+        issue_w(-2);
+        // This wavefront's x rows 2 wave, 2 wave + 1: their ids come by scalar
+        // loads, which do not wait behind the DMA in flight.
+        uint32_t xo;
+        {
+            const uint32_t r0 = __builtin_amdgcn_readfirstlane(min(m0 + 2u * (uint32_t)wave, cnt - 1u));
+            const uint32_t r1 = __builtin_amdgcn_readfirstlane(min(r0 + 1u, cnt - 1u));
+            const uint32_t id0 = moe_sload(rows + r0), id1 = moe_sload(rows + r1);
+            const uint32_t rid = (lane >> 5) ? id1 : id0;
+            const uint32_t r = m0 + 2 * wave + (lane >> 5);
+            const int p = (lane & 31) ^ (2 * wave + (lane >> 5));
+            xo = r < cnt ? (rid / (uint32_t)top_k) * (uint32_t)K * 2u + 16u * (uint32_t)p : kMoeOob;
+        }
+        auto issue_x = [&](int j) {
+            if (x_rows) {
+                const int win = j + kMoeXStages - 1;
+                const bool live = win >= 0 && win < nwin;
+                uint8_t* slot = xring + ((win + kMoeXStages) % kMoeXStages) * kMoeXSlot;
+                const int soff = __builtin_amdgcn_readfirstlane(live ? win * kMoeXRow : 0);
+                moe_dma16(xsrc, slot + 1024 * wave, live ? xo : kMoeOob, soff);
             }
-            // Raw weights: lane (n = lane%16, c) loads block pair c of the window
-            // (36 bytes, 4-byte aligned) for each of its sub-tiles.
-            uint32_t raw[kMoeNS][9];
-            const int pair = k0 / 64 + c;
+        };
+        auto issue = [&](int j) {
+            issue_w(j);
+            issue_x(j);
+        };
+        static_assert(kMoeWStages - 1 == 3 && kMoeXStages - 1 == 2, "prologue below assumes 3 and 2 windows ahead");
+        // Order W(0) W(1) x(-1) x(0) W(2) x(1): at window 0 only the last
+        // iteration's issue (W(2), x(1)) may still be in flight.
+        issue_x(-3);
+        issue_x(-2);
+        issue(-1);
+        f32x16 acc[2];
 #pragma unroll
-            for (int s = 0; s < kMoeNS; ++s) {
-                const int n = nt * kMoeBN + wave * (16 * kMoeNS) + s * 16 + (lane & 15);
-                if (n < N && pair < nb / 2) {
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(wexp + (size_t)n * row_bytes + (size_t)pair * 36);
-#pragma unroll
-                    for (int j = 0; j < 9; ++j) raw[s][j] = src[j];
+        for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
+        // The window loop is specialised on the block parity once per pass
+        // (a branch per window would make the compiler copy the accumulators).
+        auto windows = [&](auto odd) {
+            for (int win = 0; win < nwin; ++win) {
+                // Everything but the last iteration's issue has landed: W(win), x(win).
+                if (nw_dma == kWPer) {
+                    if (x_rows)
+                        moe_wait_vmcnt<kWPer + 1>();
+                    else
+                        moe_wait_vmcnt<kWPer>();
                 } else {
-#pragma unroll
-                    for (int j = 0; j < 9; ++j) raw[s][j] = 0u;
+                    if (x_rows)
+                        moe_wait_vmcnt<kMoeWDma / kMoeWaves + 1>();
+                    else
+                        moe_wait_vmcnt<kMoeWDma / kMoeWaves>();
                 }
+                moe_barrier();
+                issue(win);
+                moe_block<decltype(odd)::value>(wring + (win % kMoeWStages) * kMoeWSlot + nl * kMoeWRow,
+                                                xring + (win % kMoeXStages) * kMoeXSlot, lane, b,
+                                                b < nb - kMoeWinBlocks * win, k, acc);
             }
-            __syncthreads();
+        };
+        if (b & 1)
+            windows(std::integral_constant<int, 1>{});
+        else
+            windows(std::integral_constant<int, 0>{});
+        moe_wait_vmcnt<0>();  // the trailing (all-zero) DMA has landed
+        moe_barrier();        // every wavefront is done with the rings
+        // Blocks 1 .. 7 hand their sums to block 0.
+        if (b) {
 #pragma unroll
-            for (int s = 0; s < kMoeNS; ++s) {
-                uint32_t dA, dB, qsA[4], qsB[4];
-                q4_0_split_pair(raw[s], dA, dB, qsA, qsB);
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int f = 0; f < 8; ++f) {
-                    const int blk = 2 * c + (f >> 2);  // block within the window
-                    const int i = f & 3;               // qs dword within the block
-                    const uint32_t q = (f < 4) ? qsA[i] : qsB[i];
-                    const uint32_t d = (f < 4) ? dA : dB;
-                    const u32x4 b = q4_0_fragment(q, d | (d << 16));
-                    const int kx = blk * 32 + 4 * i;
-#pragma unroll
-                    for (int m = 0; m < kMoeMT; ++m) {
-                        if (m < mt) {
-                            const uint16_t* xr = xs + (m * 16 + (lane & 15)) * kMoeXLd;
-                            const u32x2 lo = *reinterpret_cast<const u32x2*>(xr + kx);
-                            const u32x2 hi = *reinterpret_cast<const u32x2*>(xr + kx + 16);
-                            const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                            acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc[m][s], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-            __syncthreads();
+                for (int i = 0; i < 16; ++i) red[((((b - 1) * 2 + rh) * 2 + t) * 16 + i) * 64 + lane] = acc[t][i];
         }
-        // Scatter: fragment lane holds routed rows 4*(lane/16)+r, weight row lane%16.
+        moe_barrier();
+        if (!b) {
+            // Lane (n, h) of tile t holds routed rows 8 (i / 4) + 4 h + i % 4 of weight row n.
 #pragma unroll
-        for (int m = 0; m < kMoeMT; ++m) {
-            if (m >= mt) continue;
+            for (int t = 0; t < 2; ++t) {
+                const int ncol = n0 + nl + 32 * t;
 #pragma unroll
-            for (int s = 0; s < kMoeNS; ++s) {
-                const int n = nt * kMoeBN + wave * (16 * kMoeNS) + s * 16 + (lane & 15);
-                if (n >= N) continue;
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t idx = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    float v = acc[t][i];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t idx = m0 + m * 16 + 4 * (lane >> 4) + r;
-                    if (idx < cnt) out[(size_t)rows[idx] * N + n] = acc[m][s][r];
+                    for (int q = 0; q < kMoeKSplit - 1; ++q) v += red[(((q * 2 + rh) * 2 + t) * 16 + i) * 64 + lane];
+                    if (idx < cnt && ncol < N) out[(size_t)rows[idx] * N + ncol] = v;
                 }
             }
         }
+        moe_barrier();  // the exchange area is free again
     }
 }
 
@@ -237,6 +390,7 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     if (st != W4_OK) return st;
     const int tiles_n = (int)((p->n + kMoeBN - 1) / kMoeBN);
     hipLaunchKernelGGL(moe_gemm_kernel, dim3((unsigned)(p->n_experts * tiles_n)), dim3(kMoeThreads), 0, s, w,
-                       (const uint8_t*)scratch, out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay);
+                       (const uint8_t*)scratch, out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay,
+                       (int)p->n_tokens);
     return launch_status("qmm_id_q4_0 (grouped GEMM)");
 }
