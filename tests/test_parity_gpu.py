@@ -150,7 +150,12 @@ def _lut_dev(c):
     return _t(c["x"].view(np.int16), torch.float16), _t(c["packed"]), _t(c["scales"].view(np.int16), torch.float16)
 
 
-@pytest.mark.parametrize("M,K,N,block", [(5, 128, 48, 64), (70, 256, 200, 64), (300, 64, 130, 32), (3, 64, 16, 8)])
+@pytest.mark.parametrize("M,K,N,block", [
+    (5, 128, 48, 64), (70, 256, 200, 64), (300, 64, 130, 32), (3, 64, 16, 8),
+    (260, 320, 300, 16),     # 5 K steps, two scales per K step, ragged M and N
+    (513, 384, 96, 128),     # 6 K steps, one scale per two steps, M one past two 256-row tiles
+    (72, 192, 1000, 8),      # block 8: the general path
+])
 def test_qmm_lut4_small(M, K, N, block):
     c = synth.lut_case(M, K, N, seed=M + N, block=block)
     x, p, s = _lut_dev(c)

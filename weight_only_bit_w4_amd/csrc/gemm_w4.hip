@@ -652,6 +652,203 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* 
     gemm_w4_body<WM, WN, FM, FN, true>(x, y, M, K, N, dec, As, Bs);
 }
 
+// ---------------------------------------------------------------- LUT GEMM, specialised wavefronts
+// y = x . W^T for the lookup-codebook weight (fp16 throughout, f32
+// accumulation) on the same plan as the affine prefill: a 256 x 96 tile
+// (M = 512, N = 11008 gives 230 tiles for 256 CUs), K step 64, x by LDS DMA
+// into a swizzled 3-slot ring, and
+//   4 consumer wavefronts, one per 64 x rows, each with all 96 weight rows
+//     (2 x 3 accumulator tiles of v_mfma_f32_32x32x16_f16);
+//   8 producer wavefronts issuing the x DMA (4 instructions each per step)
+//     and, for the first 6 of them, decoding one (weight row, 16-wide K
+//     quarter) per lane: 8 packed bytes and the block's scale arrive in a
+//     3-deep register ring, the lane builds its row's 16-entry table
+//     T[c] = fp16(book[c] * scale) as byte planes and looks codes up four at
+//     a time with v_perm_b32.
+// The block size must be a power of two of at least 16 (one scale per lane
+// and step).
+constexpr int kLBM = 256, kLBN = 96;
+constexpr int kLConsumers = 4, kLProducers = 8;
+constexpr int kLThreads = (kLConsumers + kLProducers) * 64;
+constexpr int kLXb = 32 / kLProducers;              // x DMA instructions per producer per step
+constexpr int kLDecodeWaves = kLBN * 4 / 64;        // producers that decode (one lane per row quarter)
+
+// The 16 table entries of one row's block as byte planes: lo[j] holds the low
+// bytes of entries 4j .. 4j + 3, hi[j] the high bytes.
+struct LutPlanes {
+    uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ LutPlanes lut_planes(const Book16& book, float s) {
+    uint32_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = pack_f16x2(book.v[2 * i] * s, book.v[2 * i + 1] * s);
+    LutPlanes P;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        P.lo[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x06040200u);
+        P.hi[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x07050301u);
+    }
+    return P;
+}
+// Looks up four codes (one per byte, 0..15): returns the low and high bytes
+// of their table entries. Selector byte 12 reads 0x00 and 13 reads 0xFF,
+// which turns bit 3 of each code into a byte mask.
+__device__ __forceinline__ void lut_lookup4(uint32_t codes, const LutPlanes& P, uint32_t& lo, uint32_t& hi) {
+    const uint32_t sel = codes & 0x07070707u;
+    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, ((codes >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+    const uint32_t lo_a = __builtin_amdgcn_perm(P.lo[1], P.lo[0], sel), lo_b = __builtin_amdgcn_perm(P.lo[3], P.lo[2], sel);
+    const uint32_t hi_a = __builtin_amdgcn_perm(P.hi[1], P.hi[0], sel), hi_b = __builtin_amdgcn_perm(P.hi[3], P.hi[2], sel);
+    lo = (mask & lo_b) | (~mask & lo_a);
+    hi = (mask & hi_b) | (~mask & hi_a);
+}
+// Eight weights k .. k + 7 from one packed dword (byte j: code of k + 2j in
+// the high nibble, of k + 2j + 1 in the low one) as four fp16 pairs.
+__device__ __forceinline__ u32x4 lut_decode8(uint32_t word, const LutPlanes& P) {
+    uint32_t elo, ehi, olo, ohi;
+    lut_lookup4((word >> 4) & 0x0F0F0F0Fu, P, elo, ehi);  // k, k + 2, k + 4, k + 6
+    lut_lookup4(word & 0x0F0F0F0Fu, P, olo, ohi);         // k + 1, k + 3, k + 5, k + 7
+    const uint32_t a0 = __builtin_amdgcn_perm(olo, elo, 0x05010400u), b0 = __builtin_amdgcn_perm(ohi, ehi, 0x05010400u);
+    const uint32_t a1 = __builtin_amdgcn_perm(olo, elo, 0x07030602u), b1 = __builtin_amdgcn_perm(ohi, ehi, 0x07030602u);
+    return u32x4{__builtin_amdgcn_perm(b0, a0, 0x05010400u), __builtin_amdgcn_perm(b0, a0, 0x07030602u),
+                 __builtin_amdgcn_perm(b1, a1, 0x05010400u), __builtin_amdgcn_perm(b1, a1, 0x07030602u)};
+}
+
+struct LutWeights {
+    u32x2 words;  // 16 codes: the lane's K quarter of its row
+    uint32_t s;   // the block's scale (binary16 bits)
+};
+__device__ __forceinline__ void lut_fence(LutWeights& e) { asm volatile("" : "+v"(e.words), "+v"(e.s)); }
+__device__ __forceinline__ void asm_load_b64(u32x2& d, const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int soff) {
+    asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen" : "=v"(d) : "v"(voff), "s"(r), "s"(soff));
+}
+
+__global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void qmm_lut4_ws_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+    Book16 book, uint16_t* __restrict__ y, int M, int K, int N, int block_shift) {
+    __shared__ __attribute__((aligned(1024))) uint8_t xring[3][kDXBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kLBN * kPLd];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles_n = (N + kLBN - 1) / kLBN;
+    const int m0 = (blockIdx.x / tiles_n) * kLBM, n0 = (blockIdx.x % tiles_n) * kLBN;
+    const int steps = K / kPBK;
+    const int mrows = min(kLBM, M - m0), nrows = min(kLBN, N - n0);
+
+    if (wave >= kLConsumers) {
+        const int pw = wave - kLConsumers;
+        const bool decoder = pw < kLDecodeWaves;
+        const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+        const __amdgpu_buffer_rsrc_t psrc = make_rsrc(packed + (size_t)n0 * (K / 2), (uint32_t)(nrows * (K / 2)));
+        const int spr = K >> block_shift;  // scales per row
+        const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * spr, (uint32_t)(nrows * spr * 2));
+        uint32_t xo[kLXb];
+#pragma unroll
+        for (int i = 0; i < kLXb; ++i) {
+            const int row = 8 * (kLXb * pw + i) + (lane >> 3);
+            xo[i] = (uint32_t)(row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7)));
+        }
+        const int item = 64 * pw + lane;              // decode item: row item / 4, K quarter item % 4
+        const int r = item >> 2, q = item & 3;
+        const uint32_t po = (uint32_t)(r * (K / 2) + 8 * q);
+        uint16_t* const bdst = Bs[0] + r * kPLd + 16 * q;
+        LutWeights ring[3];
+        auto issue = [&](int kt, int kw, uint8_t* xslot, LutWeights& e) {
+            const bool xl = kt < steps, wl = kw < steps;
+            const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
+#pragma unroll
+            for (int i = 0; i < kLXb; ++i) lds_dma16(xsrc, xslot + (kLXb * pw + i) * 1024, xl ? xo[i] : kOob, kx);
+            if (decoder) {
+                // scale index r * spr + (64 kw + 16 q) >> block_shift
+                const uint32_t so = (uint32_t)(r * spr + ((64 * kw + 16 * q) >> block_shift)) * 2u;
+                asm_load_b64(e.words, psrc, wl ? po : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
+                asm_load_u16(e.s, ssrc, wl ? so : kOob, 0);
+            }
+        };
+        auto decode = [&](const LutWeights& e, int buf) {
+            const LutPlanes P = lut_planes(book, f16_bits_to_f32(e.s));
+            uint16_t* dst = bdst + buf * (kLBN * kPLd);
+            *reinterpret_cast<u32x4*>(dst) = lut_decode8(e.words[0], P);
+            *reinterpret_cast<u32x4*>(dst + 8) = lut_decode8(e.words[1], P);
+        };
+        issue(steps, 0, xring[2], ring[0]);
+        issue(0, 1, xring[0], ring[1]);
+        issue(1, 2, xring[1], ring[2]);
+        if (decoder) {
+            wait_vmcnt<2 * (kLXb + 2)>();
+            lut_fence(ring[0]);
+            decode(ring[0], 0);
+        }
+        auto body = [&](auto slot, int j) {
+            constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+            if (decoder)
+                wait_vmcnt<kLXb + 2>();
+            else
+                wait_vmcnt<kLXb>();
+            wait_lgkmcnt0();
+            lut_fence(ring[S1]);
+            raw_barrier();
+            if (decoder) decode(ring[S1], (j + 1) & 1);
+            issue(j + 2, j + 3, xring[S2], ring[S0]);
+        };
+        int j = 0;
+        for (; j + 3 <= steps; j += 3) {
+            body(std::integral_constant<int, 0>{}, j);
+            body(std::integral_constant<int, 1>{}, j + 1);
+            body(std::integral_constant<int, 2>{}, j + 2);
+        }
+        if (j < steps) body(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
+        wait_vmcnt<0>();  // the trailing (all-zero) DMA lands before this wavefront ends
+        return;
+    }
+
+    // Consumer c: x rows 64 c .. 64 c + 63 (A tiles f), weight rows 32 g (B tiles g).
+    const int c = wave;
+    f32x16 acc[2][3];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][g][e] = 0.f;
+    for (int j = 0; j < steps; ++j) {
+        raw_barrier();
+        const uint8_t* xslot = xring[j % 3];
+        const uint16_t* bb = Bs[j & 1] + (lane & 31) * kPLd + 8 * (lane >> 5);
+#pragma unroll
+        for (int sub = 0; sub < kPBK / 16; ++sub) {
+            u32x4 a[2], b[3];
+            const int ch = 2 * sub + (lane >> 5);
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const int row = 64 * c + 32 * f + (lane & 31);
+                a[f] = *reinterpret_cast<const u32x4*>(xslot + row * 128 + 16 * (ch ^ ((row >> 1) & 7)));
+            }
+#pragma unroll
+            for (int g = 0; g < 3; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int g = 0; g < 3; ++g)
+                    acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[f]),
+                                                                      __builtin_bit_cast(f16x8, b[g]), acc[f][g], 0, 0, 0);
+        }
+    }
+    const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        const int n = n0 + g * 32 + (lane & 31);
+        const uint32_t voff = n < N ? (uint32_t)((4 * (lane >> 5)) * N + n) * 2u : kOob;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 64 * c + 32 * f + 8 * (e >> 2) + (e & 3);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_f16_bits(acc[f][g][e]), ysrc, voff, row * N * 2, 0);
+            }
+    }
+}
+
 }  // namespace w4mi
 
 using namespace w4mi;
@@ -700,6 +897,12 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
         hipLaunchKernelGGL((qmm_lut4_kernel<1, 4, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, x, packed, scales, b, y,
                            (int)M, (int)K, (int)N, (int)block);
+    } else if (K % kPBK == 0 && block >= 16 && (block & (block - 1)) == 0 && K <= (1 << 22) && N <= (1 << 22)) {
+        int shift = 0;
+        while ((1 << shift) < block) ++shift;
+        const unsigned tiles = (unsigned)(((M + kLBM - 1) / kLBM) * ((N + kLBN - 1) / kLBN));
+        hipLaunchKernelGGL(qmm_lut4_ws_kernel, dim3(tiles), dim3(kLThreads), 0, s, x, packed, scales, b, y, (int)M, (int)K,
+                           (int)N, shift);
     } else {
         constexpr int BM = 256, BN = 128;
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
