@@ -37,10 +37,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "a9670cebebdd79c1", 36838257 + 114688),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "55838a81b0d8fafa", 144938255 + 16777324),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "55838a81b0d8fafa", 81733639 + 11272192),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "2dd6faddd5f81754", 113850817 + 5768631),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "91de53da33ca6190", 36838239 + 114688),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b9a69d7d2c7bf951", 100826023 + 16803487),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b9a69d7d2c7bf951", 81613871 + 11291487),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "50ab93697ca97ae1", 114076239 + 5767168),
 }
 
 

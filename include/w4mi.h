@@ -63,6 +63,8 @@ const char* w4_version(void);
  * qmm_affine4 is the prefill form and requires M > 1 ([P1] `eligible`:
  * the kernel is only used for M > 1). qmv_affine4 is the decode GEMV and
  * requires M == 1 ([P1]: single-row decode takes the library qmv path).
+ * This library implements qmm_affine4 for K and N up to 2^21 (2,097,152);
+ * larger valid shapes return W4_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
                       const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
@@ -120,6 +122,8 @@ w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const uint16_t* sca
  * length in p at least what the shapes need. Ids must be < n_experts: a row
  * whose id is not is written as zeros, and the number of such rows is left
  * as a uint32 at byte offset W4_ID_SCRATCH_BAD_IDS of scratch.
+ * This library implements K % 64 == 0 with n_tokens * K * 2 < 2^32; other
+ * valid shapes return W4_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct {
     uint32_t n_tokens;      /* input tokens */

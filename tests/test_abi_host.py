@@ -118,3 +118,27 @@ def test_id_stride_padding_counts_last_expert_only():
     assert B.w4_check_id(p, scratch) == B.W4_OK
     p.w_bytes -= 1
     assert B.w4_check_id(p, scratch) == B.W4_EINVAL
+
+
+def _fake(addr=0x100000):
+    import ctypes
+    return ctypes.c_void_p(addr)
+
+
+def test_affine_prefill_size_limit_is_reported_before_any_launch():
+    # K past 2^21: a valid shape this library does not implement; the call
+    # returns before touching the (fake) device pointers.
+    lib = B.lib()
+    K = (1 << 21) + 32
+    st = lib.qmm_affine4(_fake(), _fake(), _fake(), _fake(), _fake(), 4, K, 256, 32, 4, None)
+    assert st == B.W4_EUNSUPPORTED
+    assert "2097152" in B.last_error()
+
+
+def test_id_size_limit_is_reported_before_any_launch():
+    lib = B.lib()
+    import ctypes
+    p, scratch = _params(n_tokens=1 << 20)  # n_tokens * K * 2 = 2^32 bytes of binary16 x
+    st = lib.qmm_id_q4_0(_fake(), _fake(), _fake(), _fake(), ctypes.byref(p), _fake(), ctypes.c_size_t(scratch), None)
+    assert st == B.W4_EUNSUPPORTED
+    assert "2^32" in B.last_error()

@@ -863,6 +863,10 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
     if (M == 0) return W4_OK;
     if (!w || !scales || !biases || !x || !y) return fail(W4_EINVAL, "qmm_affine4: null pointer argument");
     if (!aligned16(w) || !aligned16(x)) return fail(W4_EINVAL, "qmm_affine4: w and x must be 16-byte aligned");
+    // Buffer descriptors cover one 256-row tile of x or y: 256 * K * 2 bytes must fit 32 bits.
+    if (K > (1 << 21) || N > (1 << 21))
+        return fail(W4_EUNSUPPORTED, "qmm_affine4: implemented for K and N up to 2097152 (K=%lld N=%lld)", (long long)K,
+                    (long long)N);
     hipStream_t s = as_stream(stream);
     if (M <= 64) {
         constexpr int BM = 64, BN = 128;
@@ -897,7 +901,7 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
         hipLaunchKernelGGL((qmm_lut4_kernel<1, 4, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, x, packed, scales, b, y,
                            (int)M, (int)K, (int)N, (int)block);
-    } else if (K % kPBK == 0 && block >= 16 && (block & (block - 1)) == 0 && K <= (1 << 22) && N <= (1 << 22)) {
+    } else if (K % kPBK == 0 && block >= 16 && (block & (block - 1)) == 0 && K <= (1 << 21) && N <= (1 << 21)) {
         int shift = 0;
         while ((1 << shift) < block) ++shift;
         const unsigned tiles = (unsigned)(((M + kLBM - 1) / kLBM) * ((N + kLBN - 1) / kLBN));

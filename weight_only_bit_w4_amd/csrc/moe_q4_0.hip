@@ -377,6 +377,9 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     if (p->k % 64 != 0)
         return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for K %% 64 == 0 (whole 36-byte block pairs), got %u",
                     p->k);
+    // Buffer descriptors cover the binary16 x copy and one 128-row weight slice in 32 bits.
+    if ((uint64_t)p->n_tokens * p->k * 2u >= (1ull << 32) || 128ull * (p->k / 32) * 18u >= (1ull << 32))
+        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for n_tokens * K * 2 < 2^32 bytes");
     if (((uintptr_t)w & 3u) || (p->expert_stride & 3u) || ((uintptr_t)x & 15u) || ((uintptr_t)scratch & 255u))
         return fail(W4_EINVAL, "qmm_id_q4_0: w and expert_stride must be 4-byte, x 16-byte, scratch 256-byte aligned");
     const IdScratchLayout lay = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k);
