@@ -131,9 +131,16 @@ __device__ __forceinline__ void moe_wait_vmcnt() {
 __device__ __forceinline__ void moe_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // A scalar-cache load of one dword at a wave-uniform address. It is counted by
 // lgkmcnt, so waiting for it does not wait for the DMA in flight.
+// The address is passed through readfirstlane so that it is in scalar
+// registers even where the compiler cannot prove it uniform.
 __device__ __forceinline__ uint32_t moe_sload(const uint32_t* p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    // readfirstlane returns int: widen through uint32_t, or the low word would sign-extend.
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
     uint32_t v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa) : "memory");
     return v;
 }
 
