@@ -333,10 +333,13 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
                         moe_wait_vmcnt<kMoeWDma / kMoeWaves>();
                 }
                 moe_barrier();
-                issue(win);
                 moe_block<decltype(odd)::value>(wring + (win % kMoeWStages) * kMoeWSlot + nl * kMoeWRow,
                                                 xring + (win % kMoeXStages) * kMoeXSlot, lane, b,
                                                 b < nb - kMoeWinBlocks * win, k, acc);
+                // After the window's matrix work, so that the 16 wavefronts' DMA
+                // issues (which queue behind one another in the memory pipe) do
+                // not all stall the compute at the start of the window.
+                issue(win);
             }
         };
         if (b & 1)
