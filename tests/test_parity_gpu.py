@@ -78,6 +78,9 @@ def test_unpack_q4_0_bit_exact(E, N, K):
     (96, 64, 1),          # fewer groups than lanes
     (4096 + 32, 96, 2),   # a ragged second chunk of groups
     (10240, 64, 3),       # more chunks than the unrolled forms (runtime loop)
+    (8192, 64, 4),        # the largest shared-x form: 4 chunks
+    (8224, 32, 5),        # one group past it: the runtime loop with a 1-group last chunk
+    (2080, 160, 6),       # 2 chunks, the second holding one group; 10 workgroups of 16 rows
     (4096, 14336, 0),     # the decode workload at full size
 ])
 def test_qmv_affine4(K, N, seed):

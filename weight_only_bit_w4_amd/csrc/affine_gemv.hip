@@ -2,30 +2,41 @@
 // group-32 weights (INT4 MatMulNBits page: the M = 1 route, which that page
 // leaves to the library mat-vec).
 //
-// HBM-bound: every weight byte is read once. Each wavefront (one per
-// workgroup, so the rows spread evenly over the CUs) owns R output rows; its
-// 64 lanes split K by quantisation group (lane l takes groups l, l + 64, ...),
-// so one 128-bit load per lane and row fetches exactly one group's 32 nibbles
-// and consecutive lanes read consecutive 16-byte pieces of the row. All loads
-// of a wavefront are issued before its first arithmetic, x first; rows are
-// then consumed in load order, so arithmetic on early rows overlaps the
-// arrival of later ones. x stays in registers for all R rows, and the R row
-// sums are reduced across lanes together, in the vector ALU (lane swaps and
-// DPP moves, no LDS round trips).
+// HBM-bound: every weight byte is read once. Each wavefront owns R output
+// rows; its 64 lanes split K by quantisation group (lane l takes groups l,
+// l + 64, ...), so one 128-bit load per lane and row fetches exactly one
+// group's 32 nibbles and consecutive lanes read consecutive 16-byte pieces of
+// the row. All weight loads of a wavefront are issued before its first
+// arithmetic; rows are then consumed in load order, so arithmetic on early
+// rows overlaps the arrival of later ones. The R row sums are reduced across
+// lanes together, in the vector ALU (lane swaps and DPP moves).
 //
 // Arithmetic per group, for the bf16 pairs (128 + q) that one AND-OR makes
 // from a shifted weight word (exact: 128 + q has 8 significant bits):
 //   sum_k x_k (q_k s + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k,
 // so the scale and bias are applied once per group, not per weight, and the
 // inner loop is 7 integer ops + 4 v_dot2_f32_bf16 per 8 weights.
+//
+// Up to 256 groups (K <= 8192) the x side is shared: a workgroup of 8
+// wavefronts x 2 rows loads x once (one 16-byte piece per lane, ahead of its
+// weight loads), turns each piece into its bf16 pairs and partial group sum,
+// and publishes them in LDS, from which every wavefront reads its groups.
+// That takes the x loads off the per-wavefront path (x was otherwise read
+// 14 times per compute unit) and keeps each wavefront's post-load work, which
+// sets the end of the kernel, short. Longer K uses one wavefront per
+// workgroup with x in registers, one 64-group chunk at a time.
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
 namespace w4mi {
 
-constexpr int kGemvRows = 4;  // output rows per wavefront (one wavefront per workgroup)
+constexpr int kGemvRows = 4;  // output rows per wavefront of the long-K form (one wavefront per workgroup)
 constexpr int kGemvAux = 2;   // non-temporal weight loads: each byte is read once
 constexpr int kGemvAcc = 2;   // independent partial sums per group dot product
+constexpr int kXWaves = 8;    // wavefronts per workgroup of the shared-x form
+constexpr int kXRows = 2;     // output rows per wavefront of the shared-x form
+constexpr int kXChunks = 4;   // the shared-x form covers up to 4 x 64 groups
+constexpr int kXStride = 20;  // LDS dwords per group: 16 pairs, the sum, pad (80 B: conflict-free 16-byte reads)
 
 // Lane view of one quantisation group of x: bf16 pairs matching the nibble
 // pairs (i, i + 4) of each of the group's four words, and the group sum.
@@ -236,6 +247,111 @@ __global__ __launch_bounds__(kWave) void qmv_affine4_kernel(
     if ((lane & ((1 << shift) - 1)) == 0) y[n0 + (lane >> shift)] = f32_to_bf16_bits(total);
 }
 
+
+// Shared-x form: T chunks of 64 groups (T <= kXChunks), kXWaves wavefronts x
+// kXRows rows per workgroup. Piece p (16 bytes = 8 x values) of x is loaded
+// by thread p mod 512 and becomes the four pairs (8j+i, 8j+i+4) of group
+// p / 4, piece j = p % 4, plus a partial sum that the group's four (adjacent)
+// lanes add up. Pieces past the last group load as zeros (the buffer bound),
+// so idle groups contribute nothing.
+template <int T>
+__global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
+    const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int K, int N) {
+    constexpr int R = kXRows, kThreads = kWave * kXWaves;
+    constexpr int kPieces = T * kWave * 4;
+    constexpr int kPerLane = (kPieces + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) uint32_t xp[T * kWave * kXStride];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = (blockIdx.x * kXWaves + wave) * R;  // N % 16 == 0: rows n0, n0 + 1 exist
+    const int G = K / 32;
+    const uint32_t mask = vreg(kAffinePairMask), bias = vreg(kAffinePairBias);
+    const int wrow = K / 2, srow = G * 2;
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * wrow, (uint32_t)(R * wrow));
+    const __amdgpu_buffer_rsrc_t ssrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow, (uint32_t)(R * srow));
+    const __amdgpu_buffer_rsrc_t bsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow, (uint32_t)(R * srow));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)(K * 2));
+
+    // Issue order = consumption order (loads complete in issue order for the
+    // wait counter): x pieces, scales and biases, then the weights row by row.
+    u32x4 xv[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i)
+        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, (uint32_t)(tid + i * kThreads) * 16u, 0, 0);
+    uint32_t sv[T][R], bv[T][R];
+    u32x4 wv[T][R];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int g = t * kWave + lane;
+        const uint32_t gc = (uint32_t)(g < G ? g : G - 1);  // idle lanes re-read the last group
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            sv[t][r] = __builtin_amdgcn_raw_buffer_load_b16(ssrc, gc * 2u, r * srow, kGemvAux);
+            bv[t][r] = __builtin_amdgcn_raw_buffer_load_b16(bsrc, gc * 2u, r * srow, kGemvAux);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int g = t * kWave + lane;
+        const uint32_t gc = (uint32_t)(g < G ? g : G - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            wv[t][r] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, gc * 16u, r * wrow, kGemvAux);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int p = tid + i * kThreads;
+        const u32x4 v = xv[i];
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[j]), as_bf16x2(0x3F803F80u), s, false);
+        s += dpp_get<kDppQuadXor1>(s);
+        s += dpp_get<kDppQuadXor2>(s);
+        if (p < kPieces) {
+            uint32_t* d = xp + (p >> 2) * kXStride;
+            *reinterpret_cast<u32x4*>(d + 4 * (p & 3)) =
+                u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                      __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+            if ((p & 3) == 0) d[16] = __float_as_uint(s);
+        }
+    }
+    __syncthreads();
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        XGroup xg;
+        const uint32_t* d = xp + (t * kWave + lane) * kXStride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(d + 4 * j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xg.pair[j][i] = v[i];
+        }
+        xg.sum = __uint_as_float(d[16]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float s = bf16_bits_to_f32(sv[t][r]);
+            const float b = bf16_bits_to_f32(bv[t][r]);
+            const float dd = group_dot_biased<kGemvAcc>(wv[t][r], xg, mask, bias);
+            acc[r] = __builtin_fmaf(s, dd, acc[r]);
+            acc[r] = __builtin_fmaf(__builtin_fmaf(-128.f, s, b), xg.sum, acc[r]);
+        }
+    }
+    const float total = wave_reduce_rows<R>(acc, lane);
+    constexpr int shift = 6 - log2_rows<R>();
+    if ((lane & ((1 << shift) - 1)) == 0) y[n0 + (lane >> shift)] = f32_to_bf16_bits(total);
+}
+
 }  // namespace w4mi
 
 using namespace w4mi;
@@ -248,17 +364,20 @@ extern "C" w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, cons
     if (M == 0) return W4_OK;
     if (!w || !scales || !biases || !x || !y) return fail(W4_EINVAL, "qmv_affine4: null pointer argument");
     if (((uintptr_t)w & 15u) || ((uintptr_t)x & 15u)) return fail(W4_EINVAL, "qmv_affine4: w and x must be 16-byte aligned");
-    constexpr int R = kGemvRows;
-    const dim3 grid((unsigned)(N / R));
     const int G = (int)(K / 32);
     const int chunks = (G + kWave - 1) / kWave;
     hipStream_t s = as_stream(stream);
+    const dim3 xgrid((unsigned)(N / (kXWaves * kXRows))), xblock(kWave * kXWaves);
+    static_assert(kXChunks == 4, "one case per chunk count below");
     switch (chunks) {
-        case 1: hipLaunchKernelGGL((qmv_affine4_kernel<R, 1, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        case 2: hipLaunchKernelGGL((qmv_affine4_kernel<R, 2, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        case 3: hipLaunchKernelGGL((qmv_affine4_kernel<R, 3, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        case 4: hipLaunchKernelGGL((qmv_affine4_kernel<R, 4, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
-        default: hipLaunchKernelGGL((qmv_affine4_kernel<R, 0, kGemvAux, kGemvAcc>), grid, dim3(kWave), 0, s, w, scales, biases, x, y, (int)K, (int)N, chunks); break;
+        case 1: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<1>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
+        case 2: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<2>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
+        case 3: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<3>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
+        case 4: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<4>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
+        default:
+            hipLaunchKernelGGL((qmv_affine4_kernel<kGemvRows, 0, kGemvAux, kGemvAcc>), dim3((unsigned)(N / kGemvRows)), dim3(kWave), 0, s,
+                               w, scales, biases, x, y, (int)K, (int)N, chunks);
+            break;
     }
     return launch_status("qmv_affine4");
 }
