@@ -7,8 +7,9 @@ copies are rotated (>= 512 MiB in total) so the 256 MB Infinity Cache cannot
 serve them. The same JSON line carries the other kernels of the path, each
 timed over its own back-to-back launches: the prefill GEMM (M=2048,
 K=N=4096, TFLOP/s), the lookup-codebook GEMM (M=512, K=4096, N=11008) and the
-expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8), each
-with its roofline fraction, plus the CPU oracle timed on a bounded sample.
+expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8; and one
+decode token, top-8, on the mat-vec route), each with its roofline fraction,
+plus the CPU oracle timed on a bounded sample.
 
 Launches are captured in HIP graphs (torch.cuda.CUDAGraph over the library's
 own launches on the capture stream) and replayed, so the host-side cost of a
@@ -17,7 +18,7 @@ under counter collection). Times come from HIP events recorded on the stream
 the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only decode|prefill|lut|moe] [--eager] [--calib]
+                       [--only decode|prefill|lut|moe|moe_decode] [--eager] [--calib]
 """
 from __future__ import annotations
 
@@ -41,6 +42,7 @@ TRAFFIC = {
     "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b9a69d7d2c7bf951", 100826023 + 16803487),
     "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b9a69d7d2c7bf951", 81613871 + 11291487),
     "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "50ab93697ca97ae1", 114076239 + 5767168),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "", 0),
 }
 
 
@@ -64,7 +66,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "moe"],
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "moe", "moe_decode"],
                     help="time one kernel only")
     ap.add_argument("--eager", action="store_true", help="launch one by one instead of replaying graphs")
     ap.add_argument("--calib", action="store_true",
@@ -252,6 +254,35 @@ def main():
         result["moe"] = {"ms": ms, "GBps": wbytes5 / (ms * 1e-3) / 1e9, "copies": ncopy5, "launches": n5}
         del w5, x5, ids5, out5, scratch5
 
+    # ------------------------------------------------------------ expert-routed Q4_0, one decode token
+    if args.only in (None, "moe_decode"):
+        c6 = synth.moe_q4_0_case()
+        E, N6, K6, top_k6 = c6["n_experts"], c6["N"], c6["K"], c6["top_k"]
+        expert_bytes = N6 * (K6 // 32) * 18
+        wbytes6 = top_k6 * expert_bytes  # the selected experts' weights, read once
+        # Rotate over disjoint expert sets (a seeded permutation of all experts,
+        # top_k at a time) and weight copies, so that successive calls touch
+        # >= 512 MiB before any byte comes round again.
+        perm = np.random.default_rng(6).permutation(E).astype(np.uint32)
+        sets = [to_dev(perm[i:i + top_k6].view(np.int32)) for i in range(0, E - top_k6 + 1, top_k6)]
+        ncopy6 = rotation(wbytes6 * len(sets))
+        w6 = [to_dev(c6["w"])]
+        for _ in range(ncopy6 - 1):
+            w6.append(w6[0].clone())
+        x6 = to_dev(c6["x"][:1])
+        out6 = torch.empty((top_k6, N6), dtype=torch.float32, device=dev)
+        scratch6 = torch.empty(B.qmm_id_q4_0_scratch_bytes(E, 1, top_k6, K6), dtype=torch.uint8, device=dev)
+        n6 = max(200, steps // 2)
+        combos = ncopy6 * len(sets)
+        log(f"moe decode: qmm_id_q4_0 E={E} N={N6} K={K6} tokens=1 top_k={top_k6}, {len(sets)} expert sets x "
+            f"{ncopy6} weight copies, {n6} launches")
+        ms = timer.run(lambda i: B.qmm_id_q4_0(x6, w6[(i // len(sets)) % ncopy6], sets[i % len(sets)], 1, top_k6, N6,
+                                               K6, E, c6["expert_stride"], out=out6, scratch=scratch6),
+                       n6, max(10, warmup), chunk=combos * 2)
+        result["moe_decode"] = {"ms": ms, "GBps": wbytes6 / (ms * 1e-3) / 1e9, "copies": ncopy6, "sets": len(sets),
+                                "launches": n6}
+        del w6, x6, sets, out6, scratch6
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu and args.only in (None, "decode"):
@@ -321,6 +352,13 @@ def main():
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe")}}
+    if "moe_decode" in result:
+        p = result["moe_decode"]
+        comps["moe_q4_0_decode"] = {
+            "workload": "qmm_id_q4_0 E=64 N=1408 K=2048 tokens=1 top_k=8 (mat-vec route; 8 experts' weights)",
+            "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_decode")}}
     if comps:
         out["components"] = comps
     if cpu is not None:

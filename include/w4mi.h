@@ -111,19 +111,28 @@ w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const uint16_t* sca
  * w       device bytes, at least n_experts * N * (K/32) * 18 long.
  * ids     device uint32 [n_tokens * top_k].
  * out     device f32 [n_tokens * top_k, N] (written).
- * scratch device buffer of at least qmm_id_q4_0_scratch_bytes(...) bytes; the
- *         call groups the routed rows by expert into it (and stores x as
- *         binary16 there) before the grouped GEMM reads it ([P3] map0 + mm,
- *         caller-owned scratch as in IdMmScratch). Its contents need no
- *         initialisation. Calls that share one scratch buffer must be ordered
- *         (same stream). The binary16 copy of x bounds |x| by 65504.
+ * scratch device buffer of at least qmm_id_q4_0_scratch_bytes(...) bytes,
+ *         256-byte aligned; its contents need no initialisation. Calls that
+ *         share one scratch buffer must be ordered (same stream).
+ * Routes ([P3] MM_ID_ROUTING_THRESHOLD = 32 and dispatch_id_mv / dispatch_id_mm):
+ *   - n_tokens <= 32 (with n_tokens * top_k <= 256 and K <= 8192): one
+ *     mat-vec launch; each selected expert's weights are read once and
+ *     applied to every routed row that selects it. Scratch holds only the
+ *     bad-id count.
+ *   - otherwise: the routed rows are grouped by expert into scratch (and x
+ *     is stored there as binary16) before a grouped matrix-core GEMM reads
+ *     them ([P3] map0 + mm, caller-owned scratch as in IdMmScratch).
+ * Both routes round x to binary16 (round to nearest even) before the
+ * products, which bounds |x| by 65504; accumulation is f32.
  * Contract ([P3] quantized_matmul_id_ggml): n_tokens, K, N, top_k and
  * n_experts > 0; K % 32 == 0; expert_stride >= N * (K/32) * 18; each byte
  * length in p at least what the shapes need. Ids must be < n_experts: a row
  * whose id is not is written as zeros, and the number of such rows is left
  * as a uint32 at byte offset W4_ID_SCRATCH_BAD_IDS of scratch.
- * This library implements K % 64 == 0 with n_tokens * K * 2 < 2^32; other
- * valid shapes return W4_EUNSUPPORTED.
+ * x must be 16-byte aligned, w and expert_stride 2-byte aligned. This
+ * library implements the grouped route for K % 64 == 0, n_tokens * K * 2 <
+ * 2^32 and 4-byte-aligned w and expert_stride; other valid requests that
+ * need it return W4_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct {
     uint32_t n_tokens;      /* input tokens */

@@ -202,29 +202,51 @@ def _max_d(c):
 
 
 @pytest.mark.parametrize("E,N,K,T,top_k", [
-    (4, 40, 128, 3, 2),      # tiny, N not a multiple of the 128-row tile
+    # grouped GEMM route (more than 32 tokens)
+    (4, 40, 128, 33, 2),     # one token past the mat-vec threshold; N not a multiple of the 128-row tile
     (2, 64, 64, 100, 2),     # 100 routed rows per expert: two passes of 64
-    (8, 200, 320, 9, 3),     # K not a multiple of the 256 window
+    (8, 200, 320, 40, 3),    # K not a multiple of the 256 window
+    (16, 96, 256, 32, 9),    # 32 tokens but 288 routed rows: past the mat-vec id scan
+    # mat-vec route (at most 32 tokens)
+    (4, 40, 128, 3, 2),      # tiny, N not a multiple of the 32-row tile
+    (8, 200, 320, 9, 3),     # 10 blocks: a ragged first chunk
+    (6, 33, 96, 4, 1),       # K % 64 != 0 (3 blocks), top_k 1, 33 rows: a 1-row last tile
+    (5, 64, 8192, 2, 3),     # 4 chunks of 64 blocks, the most the route takes
+    (64, 1408, 2048, 1, 8),  # one decode token of the MoE workload's shapes
+    (64, 1408, 2048, 32, 8), # at the threshold: 256 routed rows, experts shared between tokens
 ])
 def test_qmm_id_q4_0_small(E, N, K, T, top_k):
     c = synth.moe_case(E, N, K, T, top_k, seed=E + N + T)
     got, scratch = _moe_run(c)
     acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], T, top_k, N, K, E, c["expert_stride"])
-    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(c), f"moe E={E} N={N} K={K}")
+    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(c), f"moe E={E} N={N} K={K} T={T}")
     assert scratch[:4].view(torch.int32).item() == 0
 
 
-def test_qmm_id_q4_0_duplicate_and_out_of_range_ids():
-    c = synth.moe_case(4, 32, 64, 5, 3, seed=31)
+@pytest.mark.parametrize("T", [5, 40])  # mat-vec route, grouped GEMM route
+def test_qmm_id_q4_0_duplicate_and_out_of_range_ids(T):
+    c = synth.moe_case(4, 32, 64, T, 3, seed=31)
     ids = c["ids"].copy()
     ids[1] = ids[0]          # the same expert twice for token 0
     ids[4] = 9               # no such expert
     ids[10] = 0xFFFFFFFF
+    ids[13] = 9              # the same missing expert again
     got, scratch = _moe_run(c, ids)
-    acc, _ = oracle.moe_q4_0(c["x"], c["w"], ids, 5, 3, 32, 64, 4, c["expert_stride"])
-    _assert_within(got, acc, 64, float(np.abs(c["x"]).max()), _max_d(c), "moe odd ids")
-    assert np.all(got[4] == 0) and np.all(got[10] == 0)
-    assert scratch[:4].view(torch.int32).item() == 2
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], ids, T, 3, 32, 64, 4, c["expert_stride"])
+    _assert_within(got, acc, 64, float(np.abs(c["x"]).max()), _max_d(c), f"moe odd ids T={T}")
+    assert np.all(got[4] == 0) and np.all(got[10] == 0) and np.all(got[13] == 0)
+    assert scratch[:4].view(torch.int32).item() == 3
+
+
+def test_qmm_id_q4_0_mat_vec_route_limits():
+    # Past 4 chunks (K > 8192) a few tokens go to the grouped GEMM, which needs K % 64 == 0.
+    c = synth.moe_case(2, 32, 8256, 2, 2, seed=5)
+    got, _ = _moe_run(c)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], 2, 2, 32, 8256, 2, c["expert_stride"])
+    _assert_within(got, acc, 8256, float(np.abs(c["x"]).max()), _max_d(c), "moe K=8256")
+    c = synth.moe_case(2, 32, 8224, 2, 2, seed=6)
+    with pytest.raises(RuntimeError, match="K % 64"):
+        _moe_run(c)
 
 
 def test_qmm_id_q4_0_full_size_sampled():

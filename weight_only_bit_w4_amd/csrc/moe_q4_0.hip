@@ -375,6 +375,239 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
     }
 }
 
+
+// ---------------------------------------------------------------- mat-vec route
+// Below the page's routing threshold (n_tokens <= 32) a call is a set of
+// mat-vecs, one per routed row (the page's mv_id dispatch): each weight row
+// slice is applied to a handful of x rows, so the work is bound by reading
+// the selected experts' weights once and the matrix cores would idle. One
+// launch, no grouping pass and no scratch traffic:
+//  - workgroup (tile, r) covers weight rows tile*32 .. +31 of expert ids[r].
+//    If an earlier routed row has the same id it exits at once; otherwise it
+//    serves every routed row with that id, so each selected expert's weights
+//    are read once, and kept in registers across those rows.
+//  - a wavefront owns 4 weight rows, 16 lanes each; lane j of a row takes
+//    blocks 4j .. 4j+3 of each 64-block chunk, i.e. 72 contiguous bytes at a
+//    4-byte-aligned offset (four 16-byte and one 8-byte load; consecutive
+//    lanes read consecutive bytes of the row).
+//  - x of the routed row's token is rounded to binary16 (as in the grouped
+//    GEMM route) and laid out in LDS as the pairs q4_0_dot_pairs pairs
+//    weights into, with each block's bias sum 1032 sum(lo) + 72 sum(hi);
+//    sum_k x (q - 8) of a block is then 16 v_dot2_f32_f16 minus that sum.
+constexpr int kMvWaves = 4;                    // wavefronts per workgroup
+constexpr int kMvRows = 4;                     // weight rows per wavefront
+constexpr int kMvTile = kMvWaves * kMvRows;    // weight rows per workgroup
+constexpr int kMvChunk = 64;                   // Q4_0 blocks per chunk: 16 lanes x 4
+constexpr int kMvMaxChunks = 4;                // K <= 8192 on this route
+constexpr int kMvStride = 20;                  // LDS dwords per block: 16 pairs, bias sum, pad (80 B)
+constexpr int kMvIdSlots = 4;                  // routed rows scanned per lane: n_tokens * top_k <= 256
+constexpr uint32_t kMvMaxTokens = 32;          // the page's mv / mm routing threshold
+
+// LDS slot of block b: within a chunk, lanes j = 0..15 reading block 4j + i
+// hit 16 consecutive 80-byte records (conflict-free 16-byte reads).
+__device__ __forceinline__ int mv_slot(int b) { return (b & ~(kMvChunk - 1)) + (b & 3) * 16 + ((b & (kMvChunk - 1)) >> 2); }
+
+template <int T, bool REALIGN>
+__global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __restrict__ x, const uint8_t* __restrict__ w,
+                                                               const uint32_t* __restrict__ ids, float* __restrict__ out,
+                                                               uint32_t* __restrict__ bad_ids, int N, int K, int top_k,
+                                                               int n_rows, int n_experts, uint64_t expert_stride) {
+    constexpr int kThreads = kMvWaves * 64;
+    constexpr int kPieces = T * kMvChunk * 4;  // (block, quarter) pieces of x
+    constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) uint32_t xp[T * kMvChunk * kMvStride];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = blockIdx.y;
+    const int n0 = blockIdx.x * kMvTile;
+    const int nb = K / 32;
+    const uint32_t row_bytes = (uint32_t)nb * 18u;
+
+    // The routed-row ids, all of them (n_rows <= 64 kMvIdSlots), one vector
+    // load per slot, together with this workgroup's own id.
+    const __amdgpu_buffer_rsrc_t isrc = make_rsrc(ids, (uint32_t)n_rows * 4u);
+    uint32_t idv[kMvIdSlots];
+#pragma unroll
+    for (int q = 0; q < kMvIdSlots; ++q) idv[q] = __builtin_amdgcn_raw_buffer_load_b32(isrc, (uint32_t)(64 * q + lane) * 4u, 0, 0);
+    const uint32_t e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(isrc, (uint32_t)r * 4u, 0, 0));
+    uint64_t match[kMvIdSlots];
+    bool dup = false;
+    uint32_t bad = 0;
+#pragma unroll
+    for (int q = 0; q < kMvIdSlots; ++q) {
+        const int i = 64 * q + lane;
+        dup |= __ballot(i < r && idv[q] == e) != 0;
+        match[q] = __ballot(i >= r && i < n_rows && idv[q] == e);
+        bad += __builtin_popcountll(__ballot(i < n_rows && idv[q] >= (uint32_t)n_experts));
+    }
+    if (r == 0 && blockIdx.x == 0 && tid == 0) *bad_ids = bad;
+    if (dup) return;  // an earlier routed row with this id serves it (uniform over the workgroup)
+
+    const int lr = kMvRows * wave + (lane >> 4);  // this lane's weight row within the tile
+    const int j = lane & 15;
+    const int n = n0 + lr;
+    if (e >= (uint32_t)n_experts) {
+        // Out-of-range id: its rows are written as zeros.
+#pragma unroll
+        for (int q = 0; q < kMvIdSlots; ++q)
+            for (uint64_t m = match[q]; m; m &= m - 1) {
+                const int r2 = 64 * q + (int)__builtin_ctzll(m);
+                if (j == 0 && n < N) out[(size_t)r2 * N + n] = 0.f;
+            }
+        return;
+    }
+
+    // x of the first routed row goes out first, then the weights.
+    auto load_x = [&](int r2, f32x4 (&lo)[kPer], f32x4 (&hi)[kPer]) {
+        const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)(r2 / top_k) * K, (uint32_t)K * 4u);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int p = tid + i * kThreads, b = p >> 2, c = p & 3;
+            // Pieces past the last block read past the row: zeros.
+            const uint32_t off = b < nb ? (uint32_t)(32 * b + 4 * c) * 4u : 0x80000000u;
+            lo[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, off, 0, 0));
+            hi[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, off + 64u, 0, 0));
+        }
+    };
+    auto publish_x = [&](const f32x4 (&lo)[kPer], const f32x4 (&hi)[kPer]) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int p = tid + i * kThreads, b = p >> 2, c = p & 3;
+            f16x2 l02, h02, l13, h13;
+            l02[0] = (_Float16)lo[i][0]; l02[1] = (_Float16)lo[i][2];
+            h02[0] = (_Float16)hi[i][0]; h02[1] = (_Float16)hi[i][2];
+            l13[0] = (_Float16)lo[i][1]; l13[1] = (_Float16)lo[i][3];
+            h13[0] = (_Float16)hi[i][1]; h13[1] = (_Float16)hi[i][3];
+            float bs = 0.f;
+            bs = __builtin_amdgcn_fdot2(l02, f16x2{(_Float16)kQ4DotBiasLo, (_Float16)kQ4DotBiasLo}, bs, false);
+            bs = __builtin_amdgcn_fdot2(l13, f16x2{(_Float16)kQ4DotBiasLo, (_Float16)kQ4DotBiasLo}, bs, false);
+            bs = __builtin_amdgcn_fdot2(h02, f16x2{(_Float16)kQ4DotBiasHi, (_Float16)kQ4DotBiasHi}, bs, false);
+            bs = __builtin_amdgcn_fdot2(h13, f16x2{(_Float16)kQ4DotBiasHi, (_Float16)kQ4DotBiasHi}, bs, false);
+            // The block's four quarters sit in four adjacent lanes.
+            bs += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(bs), 0xB1, 0xF, 0xF, false));
+            bs += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(bs), 0x4E, 0xF, 0xF, false));
+            if (p < kPieces) {
+                uint32_t* d = xp + mv_slot(b) * kMvStride;
+                *reinterpret_cast<u32x4*>(d + 4 * c) = u32x4{as_u32(l02), as_u32(h02), as_u32(l13), as_u32(h13)};
+                if (c == 0) d[16] = __float_as_uint(bs);
+            }
+        }
+    };
+    f32x4 xlo[kPer], xhi[kPer];
+    load_x(r, xlo, xhi);
+    __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weights (the wait counter is in order)
+    const int rows_here = min(kMvTile, N - n0);
+    // The tile's bytes start at a 2-byte boundary; the descriptor starts at the
+    // dword below it (dword accesses ignore the low two address bits) and
+    // every lane offset carries the difference. Its length is rounded up to
+    // whole dwords: the range check drops any dword not wholly inside it, and
+    // a dword holding the tile's last bytes lies in the same page as they do.
+    const uint8_t* tile = w + (uint64_t)e * expert_stride + (uint64_t)n0 * row_bytes;
+    const uint32_t delta = (uint32_t)((uintptr_t)tile & 3u);
+    const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(tile - delta, ((uint32_t)rows_here * row_bytes + delta + 3u) & ~3u);
+    uint32_t raw[T][18];
+#pragma unroll
+    for (int c = 0; c < T; ++c) {
+        // Lanes whose blocks lie past the row read neighbouring bytes (or
+        // zeros past the tile); their blocks are skipped below.
+        const uint32_t off = delta + (uint32_t)lr * row_bytes + (uint32_t)(c * kMvChunk * 18 + 72 * j);
+        if constexpr (!REALIGN) {
+            // A 4-byte-aligned tile and an even block count keep every lane's span 4-byte aligned.
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off + 16u * q, 0, 0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) raw[c][4 * q + t] = v[t];
+            }
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wsrc, off + 64u, 0, 0);
+            raw[c][16] = v[0];
+            raw[c][17] = v[1];
+        } else {
+            // A span that starts 2 bytes past a dword boundary (odd block
+            // count, or a tile so placed): load the 19 dwords around it and
+            // shift them into place.
+            const uint32_t base = off & ~3u, sh = off & 3u;
+            uint32_t ld[19];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, base + 16u * q, 0, 0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) ld[4 * q + t] = v[t];
+            }
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wsrc, base + 64u, 0, 0);
+            ld[16] = v[0];
+            ld[17] = v[1];
+            ld[18] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, base + 72u, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 18; ++t) raw[c][t] = __builtin_amdgcn_alignbyte(ld[t + 1], ld[t], sh);
+        }
+    }
+    const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), mg_lo = vreg(0x64006400u), mg_hi = vreg(0x54005400u);
+
+    // The routed rows this workgroup serves, in ascending order (the first is
+    // r): wavefront 0 lists them in LDS, read after the first barrier.
+    __shared__ int mlist[64 * kMvIdSlots];
+    int count = 0;
+#pragma unroll
+    for (int q = 0; q < kMvIdSlots; ++q) {
+        if (wave == 0 && ((match[q] >> lane) & 1u))
+            mlist[count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(match[q] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)match[q], 0u))] = 64 * q + lane;
+        count += __builtin_popcountll(match[q]);
+    }
+    for (int k = 0; k < count; ++k) {
+        int r2 = r;
+        if (k > 0) {
+            __syncthreads();  // every wavefront is done with the previous row's x
+            r2 = __builtin_amdgcn_readfirstlane(mlist[k]);
+            load_x(r2, xlo, xhi);
+        }
+        publish_x(xlo, xhi);
+        __syncthreads();
+        // Decode the weights afresh for each routed row: hoisted out of the
+        // loop, the decoded pairs would take 16 registers per block.
+#pragma unroll
+        for (int c = 0; c < T; ++c)
+#pragma unroll
+            for (int t = 0; t < 18; ++t) asm volatile("" : "+v"(raw[c][t]));
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < T; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // Blocks 4j + 2h and 4j + 2h + 1: bytes 36 h .. 36 h + 35 of the lane's 72.
+                uint32_t pr[9];
+#pragma unroll
+                for (int t = 0; t < 9; ++t) pr[t] = raw[c][9 * h + t];
+                uint32_t dA, dB, qsA[4], qsB[4];
+                q4_0_split_pair(pr, dA, dB, qsA, qsB);
+#pragma unroll
+                for (int ab = 0; ab < 2; ++ab) {
+                    const int b = c * kMvChunk + 4 * j + 2 * h + ab;
+                    const uint32_t* xs = xp + mv_slot(b) * kMvStride;
+                    float dot = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + 4 * t);
+                        uint32_t pw[4];
+                        q4_0_dot_pairs(ab ? qsB[t] : qsA[t], m_lo, m_hi, mg_lo, mg_hi, pw);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) dot = __builtin_amdgcn_fdot2(as_f16x2(pw[u]), as_f16x2(xv[u]), dot, false);
+                    }
+                    const float v = f16_bits_to_f32(ab ? dB : dA) * (dot - __uint_as_float(xs[16]));
+                    acc += b < nb ? v : 0.f;
+                }
+                // Bound the x pairs held in registers to two blocks' worth.
+                asm volatile("" ::: "memory");
+            }
+        // Sum over the row's 16 lanes (one DPP row).
+        acc += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(acc), 0x128, 0xF, 0xF, false));
+        acc += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(acc), 0x124, 0xF, 0xF, false));
+        acc += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(acc), 0x122, 0xF, 0xF, false));
+        acc += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(acc), 0x121, 0xF, 0xF, false));
+        if (j == 0 && n < N) out[(size_t)r2 * N + n] = acc;
+    }
+}
+
 }  // namespace w4mi
 
 using namespace w4mi;
@@ -384,18 +617,44 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     w4_status st = w4_check_id(p, scratch_bytes);
     if (st != W4_OK) return st;
     if (!x || !w || !ids || !out || !scratch) return fail(W4_EINVAL, "qmm_id_q4_0: null pointer argument");
+    if (((uintptr_t)w & 1u) || (p->expert_stride & 1u) || ((uintptr_t)x & 15u) || ((uintptr_t)scratch & 255u))
+        return fail(W4_EINVAL, "qmm_id_q4_0: w and expert_stride must be 2-byte, x 16-byte, scratch 256-byte aligned");
+    const IdScratchLayout lay = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k);
+    hipStream_t s = as_stream(stream);
+    const uint64_t n_routed = (uint64_t)p->n_tokens * p->top_k;
+    const int chunks = (int)((p->k / 32 + kMvChunk - 1) / kMvChunk);
+    if (p->n_tokens <= kMvMaxTokens && n_routed <= 64u * kMvIdSlots && chunks <= kMvMaxChunks) {
+        // Mat-vec route (the page's mv_id below its routing threshold).
+        const dim3 grid((unsigned)((p->n + kMvTile - 1) / kMvTile), (unsigned)n_routed);
+        uint32_t* bad = reinterpret_cast<uint32_t*>((uint8_t*)scratch + lay.bad_ids);
+#define W4_MV_LAUNCH(T, REALIGN)                                                                                    \
+    hipLaunchKernelGGL((moe_mv_kernel<T, REALIGN>), grid, dim3(kMvWaves * 64), 0, s, x, w, ids, out, bad, (int)p->n,   \
+                       (int)p->k, (int)p->top_k, (int)n_routed, (int)p->n_experts, p->expert_stride)
+        // Spans that may start off a dword boundary take the realigning form.
+        const bool odd = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
+        switch (chunks * 2 + (odd ? 1 : 0)) {
+            case 2: W4_MV_LAUNCH(1, false); break;
+            case 3: W4_MV_LAUNCH(1, true); break;
+            case 4: W4_MV_LAUNCH(2, false); break;
+            case 5: W4_MV_LAUNCH(2, true); break;
+            case 6: W4_MV_LAUNCH(3, false); break;
+            case 7: W4_MV_LAUNCH(3, true); break;
+            case 8: W4_MV_LAUNCH(4, false); break;
+            default: W4_MV_LAUNCH(4, true); break;
+        }
+#undef W4_MV_LAUNCH
+        return launch_status("qmm_id_q4_0 (mat-vec route)");
+    }
     if (p->k % 64 != 0)
-        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for K %% 64 == 0 (whole 36-byte block pairs), got %u",
-                    p->k);
+        return fail(W4_EUNSUPPORTED,
+                    "qmm_id_q4_0: above 32 tokens, implemented for K %% 64 == 0 (whole 36-byte block pairs), got %u", p->k);
+    if (((uintptr_t)w & 3u) || (p->expert_stride & 3u))
+        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: above 32 tokens, implemented for 4-byte-aligned w and expert_stride");
     // Buffer descriptors cover the binary16 x copy and one 128-row weight slice in 32 bits.
     if ((uint64_t)p->n_tokens * p->k * 2u >= (1ull << 32) || 128ull * (p->k / 32) * 18u >= (1ull << 32))
         return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for n_tokens * K * 2 < 2^32 bytes");
-    if (((uintptr_t)w & 3u) || (p->expert_stride & 3u) || ((uintptr_t)x & 15u) || ((uintptr_t)scratch & 255u))
-        return fail(W4_EINVAL, "qmm_id_q4_0: w and expert_stride must be 4-byte, x 16-byte, scratch 256-byte aligned");
-    const IdScratchLayout lay = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k);
     const int n_rows = (int)(p->n_tokens * p->top_k);
     const int64_t x_count = (int64_t)p->n_tokens * p->k;
-    hipStream_t s = as_stream(stream);
     const int conv_blocks = (int)std::min<int64_t>(1024, (x_count / 8 + kGroupThreads - 1) / kGroupThreads);
     hipLaunchKernelGGL(moe_group_kernel, dim3(1 + conv_blocks), dim3(kGroupThreads), p->n_experts * sizeof(uint32_t), s,
                        ids, x, (uint8_t*)scratch, out, n_rows, (int)p->n_experts, (int)p->n, x_count, lay);

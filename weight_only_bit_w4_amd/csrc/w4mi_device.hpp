@@ -116,6 +116,27 @@ __device__ __forceinline__ void q4_0_biased_pairs(uint32_t qs, uint32_t (&out)[4
     out[3] = ((t1 >> 4) & 0x000F000Fu) | 0x64006400u;
 }
 
+// The same qs dword as four fp16 pairs for a dot product against x pairs in
+// the matching order, one shift and four AND-ORs: low nibbles sit at bits
+// 0..3 of a binary16 whose exponent makes 1024 + q, high nibbles at bits 4..7
+// of one whose exponent makes 64 + q (ulp 1/16, so 16 q / 16 = q); all exact.
+//   out[0] = (4i, 4i+2)        as 1024 + q
+//   out[1] = (16+4i, 16+4i+2)  as 64 + q
+//   out[2] = (4i+1, 4i+3)      as 1024 + q
+//   out[3] = (16+4i+1, 16+4i+3) as 64 + q
+// lo = 0x000F000F, hi = 0x00F000F0, m_lo = 0x64006400, m_hi = 0x54005400 in
+// vector registers (vreg).
+__device__ __forceinline__ void q4_0_dot_pairs(uint32_t qs, uint32_t lo, uint32_t hi, uint32_t m_lo, uint32_t m_hi,
+                                               uint32_t (&out)[4]) {
+    const uint32_t s8 = qs >> 8;
+    out[0] = and_or_u32(qs, lo, m_lo);
+    out[1] = and_or_u32(qs, hi, m_hi);
+    out[2] = and_or_u32(s8, lo, m_lo);
+    out[3] = and_or_u32(s8, hi, m_hi);
+}
+constexpr float kQ4DotBiasLo = 1032.f;  // 1024 + 8: removes the low-nibble magic and GGML's offset 8
+constexpr float kQ4DotBiasHi = 72.f;    // 64 + 8
+
 // Two consecutive Q4_0 blocks (36 bytes, read as nine 4-byte-aligned dwords):
 // block A is bytes 0..17 (d at 0, qs at 2), block B bytes 18..35 (d at 18,
 // qs at 20). Returns both scales' binary16 bits and both qs as aligned dwords.
