@@ -70,6 +70,7 @@ def _load():
                 "w4o_unpack_q4_0": [P, I, I, P, P],
                 "w4o_moe_q4_0": [P, P, P, I, I, I, I, I, U, P, P],
                 "w4o_moe_q4_0_points": [P, P, P, I, I, I, U, P, P, I, P],
+                "w4o_moe_swiglu_q4_0": [P, P, P, P, I, I, I, I, U, P, P],
             }
             for name, args in sig.items():
                 fn = getattr(lib, name)
@@ -240,6 +241,19 @@ def moe_q4_0_points(x, w_bytes, ids, top_k: int, K: int, n_experts: int, expert_
     _load().w4o_moe_q4_0_points(_p(x), _p(w), _p(ids), top_k, K, n_experts, expert_stride,
                                 _p(rs), _p(ns), rs.size, _p(acc))
     return acc
+
+
+def moe_swiglu_q4_0(gate, up, w_bytes, ids, rows: int, N: int, K: int, n_experts: int, expert_stride: int):
+    """Fused SwiGLU routed mat-vec: returns (acc fp64 [rows, N], out f32 [rows, N]) for
+    out[r][n] = sum_k dequant(W[ids[r]][n][k]) * silu(gate[r][k]) * up[r][k]."""
+    gate, up = _c(gate, np.float32), _c(up, np.float32)
+    w, ids = _c(w_bytes, np.uint8), _c(ids, np.uint32)
+    assert gate.size == rows * K and up.size == rows * K and ids.size == rows
+    acc = np.empty((rows, N), np.float64)
+    out = np.empty((rows, N), np.float32)
+    _load().w4o_moe_swiglu_q4_0(_p(gate), _p(up), _p(w), _p(ids), rows, N, K, n_experts, expert_stride,
+                                _p(acc), _p(out))
+    return acc, out
 
 
 # ---------------------------------------------------------------- tolerance

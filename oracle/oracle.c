@@ -360,6 +360,37 @@ void w4o_moe_q4_0(const float* x, const uint8_t* w, const uint32_t* ids,
 }
 
 /* Point checks for (row r, column n) pairs. */
+/* P3 quantized_matmul_id_swiglu_q4_0 doc: for each routed row r, expert
+ * e = ids[r] and out[r][n] = sum_k dequant(W[e][n][k]) * (silu(gate[r][k]) *
+ * up[r][k]), where gate and up are per routed row (f32 [rows, K]) and
+ * silu(g) = g * sigmoid(g) = g / (1 + e^-g). The activation product is
+ * formed in double from the f32 inputs. Out-of-range ids give zero rows, as
+ * in w4o_moe_q4_0. */
+static double silu(double g)
+{
+    return g / (1.0 + exp(-g)); /* g -> -inf: exp overflows to inf and the quotient is -0 */
+}
+
+void w4o_moe_swiglu_q4_0(const float* gate, const float* up, const uint8_t* w, const uint32_t* ids,
+                         int64_t rows, int64_t N, int64_t K, int64_t n_experts, uint64_t expert_stride,
+                         double* acc, float* out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t e = ids[r];
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            if (e < n_experts)
+                for (int64_t k = 0; k < K; ++k) {
+                    double a = silu((double)gate[r * K + k]) * (double)up[r * K + k];
+                    s += a * (double)q4_0_weight(w, expert_stride, K, e, n, k);
+                }
+            if (acc) acc[r * N + n] = s;
+            if (out) out[r * N + n] = (float)s;
+        }
+    }
+}
+
 void w4o_moe_q4_0_points(const float* x, const uint8_t* w, const uint32_t* ids, int64_t top_k,
                          int64_t K, int64_t n_experts, uint64_t expert_stride,
                          const int64_t* rs, const int64_t* ns, int64_t count, double* acc)

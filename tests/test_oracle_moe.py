@@ -120,3 +120,76 @@ def test_dequant_round_trip_bound():
     q, d = oracle.unpack_q4_0(w, 4, 64)
     deq = (q.astype(np.float32) - 8) * np.repeat(d, 32, axis=1)
     assert np.all(np.abs(deq - Wt) <= np.repeat(d, 32, axis=1) / 2 + 1e-7)
+
+
+# ---------------------------------------------------------------- fused SwiGLU routed mat-vec
+# The page's fused form (quantized_matmul_id_swiglu_q4_0 doc):
+# out[r][n] = sum_k dequant(W[ids[r]][n][k]) * silu(gate[r][k]) * up[r][k],
+# gate and up per routed row, silu(g) = g / (1 + e^-g).
+
+def test_swiglu_closed_form_gate_values():
+    # One weight row whose only nonzero contribution is element 0 (all other
+    # gates are 0, and silu(0) = 0): out = silu(g) * up * (q - 8) * d with
+    # silu(ln 3) = 3/4 ln 3 and silu(-ln 3) = -1/4 ln 3 (a flipped exponent
+    # sign would give 1/4 and -3/4).
+    qs = [0x0A] + [0x88] * 15                           # element 0: q = 10 -> +2; element 16: q = 0 -> -8
+    blk = _block(0x3800, qs)                            # d = 0.5
+    for g, silu_exact in [(np.log(3.0), 0.75 * np.log(3.0)), (-np.log(3.0), -0.25 * np.log(3.0)), (0.0, 0.0)]:
+        gate = np.zeros((1, 32), np.float32)
+        up = np.zeros((1, 32), np.float32)
+        gate[0, 0] = np.float32(g)
+        up[0, 0] = 2.0
+        acc, _ = oracle.moe_swiglu_q4_0(gate, up, blk, np.array([0], np.uint32), 1, 1, 32, 1, 18)
+        # The input is g rounded to f32: correct to first order with silu'(g) = s + g s (1 - s), s = sigmoid(g).
+        sg = 1.0 / (1.0 + np.exp(-g))
+        silu_in = silu_exact + (sg + g * sg * (1.0 - sg)) * (float(np.float32(g)) - g)
+        expect = silu_in * 2.0 * 2 * 0.5                        # up * (q - 8) * d
+        assert abs(acc[0, 0] - expect) <= 1e-12 * max(1.0, abs(expect)), (g, acc[0, 0], expect)
+
+
+def test_swiglu_odd_part_is_the_plain_product():
+    # silu(g) - silu(-g) = g exactly, so out(gate) - out(-gate) equals the
+    # unfused routed product with x = gate * up (one slot per token).
+    c = synth.moe_case(3, 12, 64, 6, 1, seed=7)
+    rng = np.random.default_rng(8)
+    gate = rng.standard_normal((6, 64)).astype(np.float32) * 2
+    up = rng.standard_normal((6, 64)).astype(np.float32)
+    a_pos, _ = oracle.moe_swiglu_q4_0(gate, up, c["w"], c["ids"], 6, 12, 64, 3, c["expert_stride"])
+    a_neg, _ = oracle.moe_swiglu_q4_0(-gate, up, c["w"], c["ids"], 6, 12, 64, 3, c["expert_stride"])
+    x = gate.astype(np.float64) * up.astype(np.float64)          # exact in f64; round to f32 for the
+    acc_x, _ = oracle.moe_q4_0(x.astype(np.float32), c["w"], c["ids"], 6, 1, 12, 64, 3, c["expert_stride"])
+    # f32 input of the unfused routine: its products are off by at most 2^-24 relative each
+    bound = 1e-6 * np.abs(acc_x).max() + 1e-9
+    assert np.all(np.abs((a_pos - a_neg) - acc_x) <= bound)
+
+
+def test_swiglu_brute_force_and_degenerate_inputs():
+    c = synth.moe_case(4, 5, 64, 3, 2, seed=9)
+    rows = 6
+    rng = np.random.default_rng(10)
+    gate = (rng.standard_normal((rows, 64)) * 3).astype(np.float32)
+    gate[0, :4] = [-200.0, 200.0, -1e-30, 88.0]                  # saturated and tiny gates
+    up = rng.standard_normal((rows, 64)).astype(np.float32)
+    ids = c["ids"].copy()
+    ids[3] = 11                                                   # no such expert: zero row
+    acc, out = oracle.moe_swiglu_q4_0(gate, up, c["w"], ids, rows, 5, 64, 4, c["expert_stride"])
+    wb = c["w"].reshape(4, 5, 2, 18)
+    for r in range(rows):
+        e = int(ids[r])
+        for n in range(5):
+            if e >= 4:
+                assert acc[r, n] == 0.0
+                continue
+            s = 0.0
+            for k in range(64):
+                blk = wb[e, n, k // 32]
+                d = float(np.frombuffer(blk[0:2].tobytes(), "<f2")[0])
+                i = k % 32
+                q = int(blk[2 + i] & 15) if i < 16 else int(blk[2 + i - 16] >> 4)
+                g = float(gate[r, k])
+                sig = 1.0 / (1.0 + np.exp(-g)) if g >= 0 else np.exp(g) / (1.0 + np.exp(g))
+                s += g * sig * float(up[r, k]) * (q - 8) * d
+            assert abs(acc[r, n] - s) <= 1e-12 * (1 + abs(s))
+    assert np.array_equal(out, acc.astype(np.float32))
+    zero, _ = oracle.moe_swiglu_q4_0(gate, np.zeros_like(up), c["w"], c["ids"], rows, 5, 64, 4, c["expert_stride"])
+    assert np.all(zero == 0.0)
