@@ -8,7 +8,8 @@ serve them. The same JSON line carries the other kernels of the path, each
 timed over its own back-to-back launches: the prefill GEMM (M=2048,
 K=N=4096, TFLOP/s), the lookup-codebook GEMM (M=512, K=4096, N=11008) and the
 expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8; and one
-decode token, top-8, on the mat-vec route), each with its roofline fraction,
+decode token, top-8, on the mat-vec route, plain and with the fused SwiGLU
+activation), each with its roofline fraction,
 plus the CPU oracle timed on a bounded sample.
 
 Launches are captured in HIP graphs (torch.cuda.CUDAGraph over the library's
@@ -281,7 +282,16 @@ def main():
                        n6, max(10, warmup), chunk=combos * 2)
         result["moe_decode"] = {"ms": ms, "GBps": wbytes6 / (ms * 1e-3) / 1e9, "copies": ncopy6, "sets": len(sets),
                                 "launches": n6}
-        del w6, x6, sets, out6, scratch6
+        # The fused SwiGLU form on the same experts: gate and up per routed row.
+        c7 = synth.moe_swiglu_decode_case()
+        g7, u7 = to_dev(c7["gate"]), to_dev(c7["up"])
+        log(f"moe swiglu decode: qmm_id_swiglu_q4_0 E={E} N={N6} K={K6} tokens=1 top_k={top_k6}, same rotation, "
+            f"{n6} launches")
+        ms = timer.run(lambda i: B.qmm_id_swiglu_q4_0(g7, u7, w6[(i // len(sets)) % ncopy6], sets[i % len(sets)], 1,
+                                                      top_k6, N6, K6, E, c6["expert_stride"], out=out6),
+                       n6, max(10, warmup), chunk=combos * 2)
+        result["moe_swiglu_decode"] = {"ms": ms, "GBps": wbytes6 / (ms * 1e-3) / 1e9, "launches": n6}
+        del w6, x6, sets, out6, scratch6, g7, u7
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -356,6 +366,13 @@ def main():
         p = result["moe_decode"]
         comps["moe_q4_0_decode"] = {
             "workload": "qmm_id_q4_0 E=64 N=1408 K=2048 tokens=1 top_k=8 (mat-vec route; 8 experts' weights)",
+            "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_decode")}}
+    if "moe_swiglu_decode" in result:
+        p = result["moe_swiglu_decode"]
+        comps["moe_swiglu_q4_0_decode"] = {
+            "workload": "qmm_id_swiglu_q4_0 E=64 N=1408 K=2048 tokens=1 top_k=8 (fused silu(gate)*up; 8 experts' weights)",
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_decode")}}

@@ -158,6 +158,31 @@ w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_t* ids, flo
                       const w4_id_params* p, void* scratch, size_t scratch_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Fused SwiGLU + expert-routed Q4_0 mat-vec [P3] (quantized_matmul_id_swiglu_q4_0):
+ * for every routed row r = t*top_k + s, e = ids[r] and
+ *   out[r][n] = sum_k dequant(W[e][n][k]) * silu(gate[r][k]) * up[r][k],
+ * silu(g) = g / (1 + exp(-g)). gate and up are per ROUTED ROW (the outputs of
+ * that row's expert projections), not per token.
+ *
+ * gate, up  device f32 [n_tokens * top_k, K], 16-byte aligned; p->x_bytes is
+ *           the byte length of each.
+ * w, ids, out, p  as for qmm_id_q4_0 (same Q4_0 layout and params struct).
+ * bad_ids   optional device uint32 (NULL: not reported) that receives the
+ *           number of routed rows whose id is not < n_experts; those rows are
+ *           written as zeros.
+ * One launch, no scratch: each selected expert's weights are read once and
+ * applied to every routed row that selects it. The activation is formed in
+ * f32 and rounded to binary16 (round to nearest even) before the products,
+ * which bounds |silu(gate) * up| by 65504; accumulation is f32.
+ * Contract ([P3]): n_tokens, K, N, top_k, n_experts > 0; K % 32 == 0;
+ * expert_stride >= N * (K/32) * 18; byte lengths at least what the shapes
+ * need. This library implements n_tokens * top_k <= 256 and K <= 8192 (the
+ * page's decode use); larger valid requests return W4_EUNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+w4_status qmm_id_swiglu_q4_0(const float* gate, const float* up, const uint8_t* w, const uint32_t* ids,
+                             float* out, const w4_id_params* p, uint32_t* bad_ids, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host-only argument checks: the exact validation the entry points above
  * run before launching (no device access; callable without a GPU).
  * decode != 0 checks the qmv_affine4 contract, else qmm_affine4's.
@@ -166,6 +191,7 @@ w4_status w4_check_affine(int64_t M, int64_t K, int64_t N, int32_t group_size, i
                           int32_t decode);
 w4_status w4_check_lut(int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose);
 w4_status w4_check_id(const w4_id_params* p, size_t scratch_bytes);
+w4_status w4_check_id_swiglu(const w4_id_params* p);
 
 /* ------------------------------------------------------------------------
  * Unpack exports: the codes the hot kernels decode, written out one byte

@@ -142,3 +142,42 @@ def test_id_size_limit_is_reported_before_any_launch():
     st = lib.qmm_id_q4_0(_fake(), _fake(), _fake(), _fake(), ctypes.byref(p), _fake(), ctypes.c_size_t(scratch), None)
     assert st == B.W4_EUNSUPPORTED
     assert "2^32" in B.last_error()
+
+
+def _swiglu_params(**kw):
+    p, _ = _params(**kw)
+    if "x_bytes" not in kw:
+        p.x_bytes = p.n_tokens * p.top_k * p.k * 4  # gate and up are per routed row
+    return p
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    ({"n_tokens": 1}, B.W4_OK, ""),
+    ({"n_tokens": 0}, B.W4_EINVAL, "must all be > 0"),
+    ({"n_tokens": 1, "top_k": 0}, B.W4_EINVAL, "top_k"),
+    ({"n_tokens": 1, "n_experts": 0}, B.W4_EINVAL, "n_experts"),
+    ({"n_tokens": 1, "k": 2047}, B.W4_EINVAL, "divisible"),
+    ({"n_tokens": 1, "expert_stride": 1000}, B.W4_EINVAL, "expert_stride"),
+    ({"n_tokens": 1, "x_bytes": 1 * 8 * 2048 * 4 - 1}, B.W4_EINVAL, "gate/up buffer too small"),
+    ({"n_tokens": 1, "w_bytes": 1}, B.W4_EINVAL, "weight buffer too small"),
+    ({"n_tokens": 1, "ids_bytes": 4}, B.W4_EINVAL, "ids buffer too small"),
+    ({"n_tokens": 1, "out_bytes": 4}, B.W4_EINVAL, "output buffer too small"),
+    ({"n_tokens": 1, "reserved": 1}, B.W4_EINVAL, "reserved"),
+])
+def test_id_swiglu_contract(kw, status, needle):
+    p = _swiglu_params(**kw)
+    assert B.w4_check_id_swiglu(p) == status
+    if status != B.W4_OK:
+        assert needle in B.last_error()
+
+
+@pytest.mark.parametrize("kw", [{"n_tokens": 33, "top_k": 8}, {"n_tokens": 1, "k": 8224}])
+def test_id_swiglu_limits_are_reported_before_any_launch(kw):
+    import ctypes
+    p = _swiglu_params(**kw)
+    p.expert_stride = p.n * (p.k // 32) * 18
+    p.w_bytes = p.n_experts * p.expert_stride
+    assert B.w4_check_id_swiglu(p) == B.W4_OK  # valid: the request is only beyond this library
+    st = B.lib().qmm_id_swiglu_q4_0(_fake(), _fake(), _fake(), _fake(), _fake(), ctypes.byref(p), None, None)
+    assert st == B.W4_EUNSUPPORTED
+    assert "256" in B.last_error() and "8192" in B.last_error()

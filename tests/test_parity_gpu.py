@@ -260,3 +260,48 @@ def test_qmm_id_q4_0_full_size_sampled():
                                  rs, ns)
     _assert_within(got[rs, ns], acc, c["K"], float(np.abs(c["x"]).max()), _max_d(c), "moe full sampled")
     assert np.isfinite(got).all()
+
+
+# ---------------------------------------------------------------- fused SwiGLU routed mat-vec
+def _swiglu_run(c, ids=None, bad=False):
+    ids = c["ids"] if ids is None else ids
+    bad_t = torch.zeros(1, dtype=torch.int32, device=DEV) if bad else None
+    out = B.qmm_id_swiglu_q4_0(_t(c["gate"]), _t(c["up"]), _t(c["w"]), _t(ids.view(np.int32)), c["n_tokens"],
+                               c["top_k"], c["N"], c["K"], c["n_experts"], c["expert_stride"], bad_ids=bad_t)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), (None if bad_t is None else int(bad_t.item()))
+
+
+def _max_act(c):
+    g, u = c["gate"].astype(np.float64), c["up"].astype(np.float64)
+    return float(np.abs(g / (1 + np.exp(-g)) * u).max())
+
+
+@pytest.mark.parametrize("E,N,K,T,top_k", [
+    (64, 1408, 2048, 1, 8),  # one decode token on the MoE workload's experts
+    (8, 200, 320, 9, 3),     # ragged chunk, N not a multiple of the 32-row tile
+    (6, 33, 96, 4, 1),       # odd block count (realigned spans), a 1-row last tile
+    (5, 64, 8192, 2, 3),     # 4 chunks, the most the route takes
+    (16, 96, 256, 32, 8),    # 256 routed rows, experts shared between tokens
+])
+def test_qmm_id_swiglu_q4_0(E, N, K, T, top_k):
+    c = synth.moe_swiglu_case(E, N, K, T, top_k, seed=E + N + T)
+    got, bad = _swiglu_run(c, bad=True)
+    acc, _ = oracle.moe_swiglu_q4_0(c["gate"], c["up"], c["w"], c["ids"], T * top_k, N, K, E, c["expert_stride"])
+    _assert_within(got, acc, K, _max_act(c), _max_d(c), f"swiglu E={E} N={N} K={K} T={T}")
+    assert bad == 0
+
+
+def test_qmm_id_swiglu_q4_0_odd_ids_and_saturated_gates():
+    c = synth.moe_swiglu_case(4, 32, 64, 5, 3, seed=41)
+    c["gate"][0, :6] = [-200.0, 200.0, -88.0, 88.0, -1e-30, 0.0]   # silu: -0, 200, ~0, 88, ~0, 0
+    ids = c["ids"].copy()
+    ids[1] = ids[0]          # the same expert twice for token 0 (different gate/up rows)
+    ids[4] = 9               # no such expert
+    ids[10] = 0xFFFFFFFF
+    got, bad = _swiglu_run(c, ids, bad=True)
+    acc, _ = oracle.moe_swiglu_q4_0(c["gate"], c["up"], c["w"], ids, 15, 32, 64, 4, c["expert_stride"])
+    _assert_within(got, acc, 64, _max_act(c), _max_d(c), "swiglu odd ids")
+    assert np.all(got[4] == 0) and np.all(got[10] == 0) and bad == 2
+    got2, none = _swiglu_run(c, ids, bad=False)        # no count requested
+    assert none is None and np.array_equal(got2, got)

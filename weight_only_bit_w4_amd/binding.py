@@ -54,9 +54,11 @@ SIGNATURES = {
     "qmm_lut4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "qmm_id_q4_0_scratch_bytes": ([_U32, _U32, _U32, _U32], _SZ),
     "qmm_id_q4_0": ([_P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _SZ, _P], ctypes.c_int),
+    "qmm_id_swiglu_q4_0": ([_P, _P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _P], ctypes.c_int),
     "w4_check_affine": ([_I64, _I64, _I64, _I32, _I32, _I32], ctypes.c_int),
     "w4_check_lut": ([_I64, _I64, _I64, _I32, _I32], ctypes.c_int),
     "w4_check_id": ([ctypes.POINTER(IdParams), _SZ], ctypes.c_int),
+    "w4_check_id_swiglu": ([ctypes.POINTER(IdParams)], ctypes.c_int),
     "w4_unpack_affine": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
     "w4_unpack_lut": ([_P, _P, _I64, _P], ctypes.c_int),
     "w4_unpack_q4_0": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
@@ -172,6 +174,22 @@ def qmm_id_q4_0(x, w, ids, n_tokens: int, top_k: int, n: int, k: int, n_experts:
     return out
 
 
+def qmm_id_swiglu_q4_0(gate, up, w, ids, n_tokens: int, top_k: int, n: int, k: int, n_experts: int,
+                       expert_stride: int, out=None, bad_ids=None):
+    """out [n_tokens*top_k, n] f32 = dequant(W[ids[r]]) . (silu(gate[r]) * up[r]) per routed row r.
+    bad_ids: optional device uint32 tensor [1] receiving the out-of-range id count."""
+    if out is None:
+        out = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=gate.device)
+    if up.numel() != gate.numel():
+        raise ValueError("gate and up must have the same shape")
+    p = id_params(gate, w, ids, out, n_tokens, top_k, n, k, n_experts, expert_stride)
+    bad = None if bad_ids is None else _dev(bad_ids, "bad_ids", U32)
+    _check(lib().qmm_id_swiglu_q4_0(_dev(gate, "gate", F32), _dev(up, "up", F32), _dev(w, "w", U8),
+                                    _dev(ids, "ids", U32), _dev(out, "out", F32), ctypes.byref(p), bad,
+                                    _stream(gate)))
+    return out
+
+
 # ---------------------------------------------------------------- host checks
 def w4_check_affine(M, K, N, group_size=32, bits=4, decode=0) -> int:
     return int(lib().w4_check_affine(M, K, N, group_size, bits, decode))
@@ -183,6 +201,10 @@ def w4_check_lut(M, K, N, block, transpose=1) -> int:
 
 def w4_check_id(params: IdParams, scratch_bytes: int) -> int:
     return int(lib().w4_check_id(ctypes.byref(params), scratch_bytes))
+
+
+def w4_check_id_swiglu(params: IdParams) -> int:
+    return int(lib().w4_check_id_swiglu(ctypes.byref(params)))
 
 
 def last_error() -> str:

@@ -141,6 +141,39 @@ w4_status w4_check_id(const w4_id_params* p, size_t scratch_bytes) {
     return W4_OK;
 }
 
+w4_status w4_check_id_swiglu(const w4_id_params* p) {
+    if (!p) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: params is null");
+    if (p->n_tokens == 0 || p->k == 0 || p->n == 0)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: n_tokens, K, and N must all be > 0");
+    if (p->top_k == 0) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: top_k must be > 0");
+    if (p->n_experts == 0) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: n_experts must be > 0");
+    if (p->reserved != 0) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: reserved field must be 0");
+    if (p->k % 32 != 0)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: K (%u) must be divisible by block QK (32)", p->k);
+    const uint64_t per_expert = (uint64_t)p->n * (p->k / 32) * 18u;
+    if (p->expert_stride < per_expert)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: expert_stride (%llu) < per_expert_bytes (%llu)",
+                    (unsigned long long)p->expert_stride, (unsigned long long)per_expert);
+    const uint64_t rows = (uint64_t)p->n_tokens * p->top_k;
+    if (rows > INT32_MAX) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: n_tokens * top_k must fit in int32");
+    const uint64_t need_in = rows * p->k * 4u;
+    if (p->x_bytes < need_in)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: gate/up buffer too small: expected %llu bytes, got %llu",
+                    (unsigned long long)need_in, (unsigned long long)p->x_bytes);
+    const uint64_t need_w = (uint64_t)(p->n_experts - 1) * p->expert_stride + per_expert;
+    if (p->w_bytes < need_w)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: weight buffer too small: expected %llu bytes for %u experts, got %llu",
+                    (unsigned long long)need_w, p->n_experts, (unsigned long long)p->w_bytes);
+    if (p->ids_bytes < rows * 4u)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: ids buffer too small: expected %llu bytes, got %llu",
+                    (unsigned long long)(rows * 4u), (unsigned long long)p->ids_bytes);
+    if (p->out_bytes < rows * p->n * 4u)
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: output buffer too small: expected %llu bytes, got %llu",
+                    (unsigned long long)(rows * p->n * 4u), (unsigned long long)p->out_bytes);
+    clear_error();
+    return W4_OK;
+}
+
 size_t qmm_id_q4_0_scratch_bytes(uint32_t n_experts, uint32_t n_tokens, uint32_t top_k, uint32_t k) {
     return id_scratch_layout(n_experts, n_tokens, top_k, k).total;
 }

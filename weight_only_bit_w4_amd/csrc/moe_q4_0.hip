@@ -407,8 +407,12 @@ constexpr uint32_t kMvMaxTokens = 32;          // the page's mv / mm routing thr
 // hit 16 consecutive 80-byte records (conflict-free 16-byte reads).
 __device__ __forceinline__ int mv_slot(int b) { return (b & ~(kMvChunk - 1)) + (b & 3) * 16 + ((b & (kMvChunk - 1)) >> 2); }
 
-template <int T, bool REALIGN>
-__global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __restrict__ x, const uint8_t* __restrict__ w,
+// SWIGLU: the fused form of the same page (quantized_matmul_id_swiglu_q4_0):
+// the activation of routed row r is silu(gate[r]) * up[r] (x = gate, per
+// routed row, not per token), formed in f32 when x is published.
+template <int T, bool REALIGN, bool SWIGLU>
+__global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __restrict__ x, const float* __restrict__ up,
+                                                               const uint8_t* __restrict__ w,
                                                                const uint32_t* __restrict__ ids, float* __restrict__ out,
                                                                uint32_t* __restrict__ bad_ids, int N, int K, int top_k,
                                                                int n_rows, int n_experts, uint64_t expert_stride) {
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
         match[q] = __ballot(i >= r && i < n_rows && idv[q] == e);
         bad += __builtin_popcountll(__ballot(i < n_rows && idv[q] >= (uint32_t)n_experts));
     }
-    if (r == 0 && blockIdx.x == 0 && tid == 0) *bad_ids = bad;
+    if (bad_ids != nullptr && r == 0 && blockIdx.x == 0 && tid == 0) *bad_ids = bad;
     if (dup) return;  // an earlier routed row with this id serves it (uniform over the workgroup)
 
     const int lr = kMvRows * wave + (lane >> 4);  // this lane's weight row within the tile
@@ -458,26 +462,46 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
     }
 
     // x of the first routed row goes out first, then the weights.
-    auto load_x = [&](int r2, f32x4 (&lo)[kPer], f32x4 (&hi)[kPer]) {
-        const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)(r2 / top_k) * K, (uint32_t)K * 4u);
+    constexpr int kSrc = SWIGLU ? 2 : 1;  // gate and up, or x
+    auto load_x = [&](int r2, f32x4 (&lo)[kSrc][kPer], f32x4 (&hi)[kSrc][kPer]) {
+        const size_t row = SWIGLU ? (size_t)r2 : (size_t)(r2 / top_k);
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int p = tid + i * kThreads, b = p >> 2, c = p & 3;
-            // Pieces past the last block read past the row: zeros.
-            const uint32_t off = b < nb ? (uint32_t)(32 * b + 4 * c) * 4u : 0x80000000u;
-            lo[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, off, 0, 0));
-            hi[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, off + 64u, 0, 0));
+        for (int v = 0; v < kSrc; ++v) {
+            const __amdgpu_buffer_rsrc_t xsrc = make_rsrc((v ? up : x) + row * K, (uint32_t)K * 4u);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int p = tid + i * kThreads, b = p >> 2, c = p & 3;
+                // Pieces past the last block read past the row: zeros.
+                const uint32_t off = b < nb ? (uint32_t)(32 * b + 4 * c) * 4u : 0x80000000u;
+                lo[v][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, off, 0, 0));
+                hi[v][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, off + 64u, 0, 0));
+            }
         }
     };
-    auto publish_x = [&](const f32x4 (&lo)[kPer], const f32x4 (&hi)[kPer]) {
+    // silu(g) u = g u / (1 + e^-g); for g -> -inf the reciprocal of inf is 0.
+    auto swiglu = [](f32x4 g, f32x4 u) {
+        f32x4 a;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[t] = g[t] * u[t] * __builtin_amdgcn_rcpf(1.f + __expf(-g[t]));
+        return a;
+    };
+    auto publish_x = [&](const f32x4 (&src_lo)[kSrc][kPer], const f32x4 (&src_hi)[kSrc][kPer]) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int p = tid + i * kThreads, b = p >> 2, c = p & 3;
+            f32x4 lo[1], hi[1];
+            if constexpr (SWIGLU) {
+                lo[0] = swiglu(src_lo[0][i], src_lo[1][i]);
+                hi[0] = swiglu(src_hi[0][i], src_hi[1][i]);
+            } else {
+                lo[0] = src_lo[0][i];
+                hi[0] = src_hi[0][i];
+            }
             f16x2 l02, h02, l13, h13;
-            l02[0] = (_Float16)lo[i][0]; l02[1] = (_Float16)lo[i][2];
-            h02[0] = (_Float16)hi[i][0]; h02[1] = (_Float16)hi[i][2];
-            l13[0] = (_Float16)lo[i][1]; l13[1] = (_Float16)lo[i][3];
-            h13[0] = (_Float16)hi[i][1]; h13[1] = (_Float16)hi[i][3];
+            l02[0] = (_Float16)lo[0][0]; l02[1] = (_Float16)lo[0][2];
+            h02[0] = (_Float16)hi[0][0]; h02[1] = (_Float16)hi[0][2];
+            l13[0] = (_Float16)lo[0][1]; l13[1] = (_Float16)lo[0][3];
+            h13[0] = (_Float16)hi[0][1]; h13[1] = (_Float16)hi[0][3];
             float bs = 0.f;
             bs = __builtin_amdgcn_fdot2(l02, f16x2{(_Float16)kQ4DotBiasLo, (_Float16)kQ4DotBiasLo}, bs, false);
             bs = __builtin_amdgcn_fdot2(l13, f16x2{(_Float16)kQ4DotBiasLo, (_Float16)kQ4DotBiasLo}, bs, false);
@@ -493,7 +517,7 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
             }
         }
     };
-    f32x4 xlo[kPer], xhi[kPer];
+    f32x4 xlo[kSrc][kPer], xhi[kSrc][kPer];
     load_x(r, xlo, xhi);
     __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weights (the wait counter is in order)
     const int rows_here = min(kMvTile, N - n0);
@@ -612,6 +636,36 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
 
 using namespace w4mi;
 
+namespace w4mi {
+
+// One mat-vec launch over n_tokens * top_k routed rows (the caller checked
+// n_routed <= 64 kMvIdSlots and K <= 32 kMvChunk kMvMaxChunks).
+template <bool SWIGLU>
+void mv_launch(const float* x, const float* up, const uint8_t* w, const uint32_t* ids, float* out, uint32_t* bad,
+               const w4_id_params* p, hipStream_t s) {
+    const uint32_t n_routed = p->n_tokens * p->top_k;
+    const int chunks = (int)((p->k / 32 + kMvChunk - 1) / kMvChunk);
+    const dim3 grid((unsigned)((p->n + kMvTile - 1) / kMvTile), n_routed), block(kMvWaves * 64);
+    // Spans that may start off a dword boundary take the realigning form.
+    const bool realign = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
+#define W4_MV_LAUNCH(T, RE)                                                                                      \
+    hipLaunchKernelGGL((moe_mv_kernel<T, RE, SWIGLU>), grid, block, 0, s, x, up, w, ids, out, bad, (int)p->n,   \
+                       (int)p->k, (int)p->top_k, (int)n_routed, (int)p->n_experts, p->expert_stride)
+    switch (chunks * 2 + (realign ? 1 : 0)) {
+        case 2: W4_MV_LAUNCH(1, false); break;
+        case 3: W4_MV_LAUNCH(1, true); break;
+        case 4: W4_MV_LAUNCH(2, false); break;
+        case 5: W4_MV_LAUNCH(2, true); break;
+        case 6: W4_MV_LAUNCH(3, false); break;
+        case 7: W4_MV_LAUNCH(3, true); break;
+        case 8: W4_MV_LAUNCH(4, false); break;
+        default: W4_MV_LAUNCH(4, true); break;
+    }
+#undef W4_MV_LAUNCH
+}
+
+}  // namespace w4mi
+
 extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_t* ids, float* out,
                                  const w4_id_params* p, void* scratch, size_t scratch_bytes, void* stream) {
     w4_status st = w4_check_id(p, scratch_bytes);
@@ -625,24 +679,8 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     const int chunks = (int)((p->k / 32 + kMvChunk - 1) / kMvChunk);
     if (p->n_tokens <= kMvMaxTokens && n_routed <= 64u * kMvIdSlots && chunks <= kMvMaxChunks) {
         // Mat-vec route (the page's mv_id below its routing threshold).
-        const dim3 grid((unsigned)((p->n + kMvTile - 1) / kMvTile), (unsigned)n_routed);
         uint32_t* bad = reinterpret_cast<uint32_t*>((uint8_t*)scratch + lay.bad_ids);
-#define W4_MV_LAUNCH(T, REALIGN)                                                                                    \
-    hipLaunchKernelGGL((moe_mv_kernel<T, REALIGN>), grid, dim3(kMvWaves * 64), 0, s, x, w, ids, out, bad, (int)p->n,   \
-                       (int)p->k, (int)p->top_k, (int)n_routed, (int)p->n_experts, p->expert_stride)
-        // Spans that may start off a dword boundary take the realigning form.
-        const bool odd = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
-        switch (chunks * 2 + (odd ? 1 : 0)) {
-            case 2: W4_MV_LAUNCH(1, false); break;
-            case 3: W4_MV_LAUNCH(1, true); break;
-            case 4: W4_MV_LAUNCH(2, false); break;
-            case 5: W4_MV_LAUNCH(2, true); break;
-            case 6: W4_MV_LAUNCH(3, false); break;
-            case 7: W4_MV_LAUNCH(3, true); break;
-            case 8: W4_MV_LAUNCH(4, false); break;
-            default: W4_MV_LAUNCH(4, true); break;
-        }
-#undef W4_MV_LAUNCH
+        mv_launch<false>(x, nullptr, w, ids, out, bad, p, s);
         return launch_status("qmm_id_q4_0 (mat-vec route)");
     }
     if (p->k % 64 != 0)
@@ -665,4 +703,21 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
                        (const uint8_t*)scratch, out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay,
                        (int)p->n_tokens);
     return launch_status("qmm_id_q4_0 (grouped GEMM)");
+}
+
+extern "C" w4_status qmm_id_swiglu_q4_0(const float* gate, const float* up, const uint8_t* w, const uint32_t* ids,
+                                        float* out, const w4_id_params* p, uint32_t* bad_ids, void* stream) {
+    w4_status st = w4_check_id_swiglu(p);
+    if (st != W4_OK) return st;
+    if (!gate || !up || !w || !ids || !out) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: null pointer argument");
+    if (((uintptr_t)w & 1u) || (p->expert_stride & 1u) || ((uintptr_t)gate & 15u) || ((uintptr_t)up & 15u) ||
+        ((uintptr_t)bad_ids & 3u))
+        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: w and expert_stride must be 2-byte, gate and up 16-byte, bad_ids 4-byte aligned");
+    const uint64_t n_routed = (uint64_t)p->n_tokens * p->top_k;
+    const uint64_t chunks = (p->k / 32 + kMvChunk - 1) / kMvChunk;
+    if (n_routed > 64u * kMvIdSlots || chunks > (uint64_t)kMvMaxChunks)
+        return fail(W4_EUNSUPPORTED, "qmm_id_swiglu_q4_0: implemented for n_tokens * top_k <= %d and K <= %d",
+                    64 * kMvIdSlots, 32 * kMvChunk * kMvMaxChunks);
+    mv_launch<true>(gate, up, w, ids, out, bad_ids, p, as_stream(stream));
+    return launch_status("qmm_id_swiglu_q4_0");
 }

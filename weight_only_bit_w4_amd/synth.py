@@ -105,6 +105,18 @@ def moe_case(n_experts: int, N: int, K: int, n_tokens: int, top_k: int, seed: in
     }
 
 
+def moe_swiglu_case(n_experts: int, N: int, K: int, n_tokens: int, top_k: int, seed: int = 0,
+                    d_range=(0.002, 0.01)):
+    """moe_case's weights and ids, plus per-routed-row gate and up, f32 ~ N(0, 1) each
+    (drawn from their own generator, seed + 1, gate first)."""
+    c = moe_case(n_experts, N, K, n_tokens, top_k, seed, d_range)
+    rng = np.random.default_rng(seed + 1)
+    rows = n_tokens * top_k
+    c["gate"] = rng.standard_normal((rows, K)).astype(np.float32)
+    c["up"] = rng.standard_normal((rows, K)).astype(np.float32)
+    return c
+
+
 # The workloads the path is measured and checked on.
 def tiny_affine(seed: int = 0):
     return affine_case(4, 256, 256, seed)
@@ -124,3 +136,8 @@ def lut_matmul_case(seed: int = 0):
 
 def moe_q4_0_case(seed: int = 0):
     return moe_case(64, 1408, 2048, 128, 8, seed)
+
+
+def moe_swiglu_decode_case(seed: int = 0):
+    """One decode token through the fused SwiGLU routed mat-vec, on the MoE workload's experts."""
+    return moe_swiglu_case(64, 1408, 2048, 1, 8, seed)
