@@ -249,19 +249,23 @@ __global__ __launch_bounds__(kWave) void qmv_affine4_kernel(
 
 
 // Shared-x form: T chunks of 64 groups (T <= kXChunks), kXWaves wavefronts x
-// kXRows rows per workgroup. Piece p (16 bytes = 8 x values) of x is loaded
-// by thread p mod 512 and becomes the four pairs (8j+i, 8j+i+4) of group
-// p / 4, piece j = p % 4, plus a partial sum that the group's four (adjacent)
-// lanes add up. Pieces past the last group load as zeros (the buffer bound),
-// so idle groups contribute nothing.
-template <int T>
+// kXRows weight rows per workgroup, and M rows of x taken MB at a time (a
+// small batch: every weight row read once serves all of them). Piece p
+// (16 bytes = 8 x values) of a batch's x is loaded by thread p mod 512 and
+// becomes the four pairs (8j+i, 8j+i+4) of its group, piece j = p % 4, plus a
+// partial sum that the group's four (adjacent) lanes add up. Pieces past the
+// last group or row load as zeros (the buffer bound), so idle groups
+// contribute nothing. Weights stay in registers across batches.
+template <int T, int MB>
 __global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int K, int N) {
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
     constexpr int R = kXRows, kThreads = kWave * kXWaves;
-    constexpr int kPieces = T * kWave * 4;
+    constexpr int kRowPieces = T * kWave * 4;  // pieces of one x row
+    constexpr int kPieces = MB * kRowPieces;
     constexpr int kPerLane = (kPieces + kThreads - 1) / kThreads;
-    __shared__ __attribute__((aligned(16))) uint32_t xp[T * kWave * kXStride];
+    constexpr int kVals = R * MB;              // row sums per lane, reduced together
+    __shared__ __attribute__((aligned(16))) uint32_t xp[MB * T * kWave * kXStride];
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = (blockIdx.x * kXWaves + wave) * R;  // N % 16 == 0: rows n0, n0 + 1 exist
@@ -274,14 +278,22 @@ __global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
         make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow, (uint32_t)(R * srow));
     const __amdgpu_buffer_rsrc_t bsrc =
         make_rsrc(reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow, (uint32_t)(R * srow));
-    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)(K * 2));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
 
     // Issue order = consumption order (loads complete in issue order for the
-    // wait counter): x pieces, scales and biases, then the weights row by row.
-    u32x4 xv[kPerLane];
+    // wait counter): the first batch's x pieces, scales and biases, then the
+    // weights row by row.
+    auto load_x = [&](int m0, u32x4 (&xv)[kPerLane]) {
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i)
-        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, (uint32_t)(tid + i * kThreads) * 16u, 0, 0);
+        for (int i = 0; i < kPerLane; ++i) {
+            const int p = tid + i * kThreads, mm = p / kRowPieces, q = p % kRowPieces;
+            const bool live = m0 + mm < M && q < 4 * G;
+            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                xsrc, live ? ((uint32_t)(m0 + mm) * (uint32_t)K * 2u + (uint32_t)q * 16u) : 0x80000000u, 0, 0);
+        }
+    };
+    u32x4 xv[kPerLane];
+    load_x(0, xv);
     uint32_t sv[T][R], bv[T][R];
     u32x4 wv[T][R];
 #pragma unroll
@@ -305,56 +317,134 @@ __global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        const int p = tid + i * kThreads;
-        const u32x4 v = xv[i];
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[j]), as_bf16x2(0x3F803F80u), s, false);
-        s += dpp_get<kDppQuadXor1>(s);
-        s += dpp_get<kDppQuadXor2>(s);
-        if (p < kPieces) {
-            uint32_t* d = xp + (p >> 2) * kXStride;
-            *reinterpret_cast<u32x4*>(d + 4 * (p & 3)) =
-                u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
-                      __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
-            if ((p & 3) == 0) d[16] = __float_as_uint(s);
+    for (int m0 = 0; m0 < M; m0 += MB) {
+        if (m0 > 0) {
+            __syncthreads();  // every wavefront is done with the previous batch's x
+            load_x(m0, xv);
         }
-    }
-    __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int p = tid + i * kThreads, mm = p / kRowPieces, q = p % kRowPieces;
+            const u32x4 v = xv[i];
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[j]), as_bf16x2(0x3F803F80u), s, false);
+            s += dpp_get<kDppQuadXor1>(s);
+            s += dpp_get<kDppQuadXor2>(s);
+            if (p < kPieces) {
+                uint32_t* d = xp + (mm * T * kWave + (q >> 2)) * kXStride;
+                *reinterpret_cast<u32x4*>(d + 4 * (q & 3)) =
+                    u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                          __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+                if ((q & 3) == 0) d[16] = __float_as_uint(s);
+            }
+        }
+        __syncthreads();
+        // Decode the weights afresh for each batch: hoisted out of the loop, the
+        // pairs would hold 16 registers per group and row.
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < R; ++r) asm volatile("" : "+v"(wv[t][r]));
 
-    float acc[R];
+        float acc[kVals];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        for (int v = 0; v < kVals; ++v) acc[v] = 0.f;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        XGroup xg;
-        const uint32_t* d = xp + (t * kWave + lane) * kXStride;
+        for (int t = 0; t < T; ++t) {
+            if constexpr (MB == 1) {
+                XGroup xg;
+                const uint32_t* d = xp + (t * kWave + lane) * kXStride;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(d + 4 * j);
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(d + 4 * j);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xg.pair[j][i] = v[i];
+                    for (int i = 0; i < 4; ++i) xg.pair[j][i] = v[i];
+                }
+                xg.sum = __uint_as_float(d[16]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float s = bf16_bits_to_f32(sv[t][r]);
+                    const float b = bf16_bits_to_f32(bv[t][r]);
+                    const float dd = group_dot_biased<kGemvAcc>(wv[t][r], xg, mask, bias);
+                    acc[r] = __builtin_fmaf(s, dd, acc[r]);
+                    acc[r] = __builtin_fmaf(__builtin_fmaf(-128.f, s, b), xg.sum, acc[r]);
+                }
+            } else {
+                // Each row's pairs once, against every x row of the batch.
+                uint32_t pr[R][4][4];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pr[r][j][i] = affine_pair_biased_bf16(wv[t][r][j], i, mask, bias);
+#pragma unroll
+                for (int mm = 0; mm < MB; ++mm) {
+                    const uint32_t* d = xp + (mm * T * kWave + t * kWave + lane) * kXStride;
+                    u32x4 xq[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) xq[j] = *reinterpret_cast<const u32x4*>(d + 4 * j);
+                    const float xs = __uint_as_float(d[16]);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                float& dd = (j & 1) ? d1 : d0;
+                                dd = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr[r][j][i]), as_bf16x2(xq[j][i]), dd, false);
+                            }
+                        const float s = bf16_bits_to_f32(sv[t][r]);
+                        const float b = bf16_bits_to_f32(bv[t][r]);
+                        float& a = acc[r * MB + mm];
+                        a = __builtin_fmaf(s, d0 + d1, a);
+                        a = __builtin_fmaf(__builtin_fmaf(-128.f, s, b), xs, a);
+                    }
+                }
+            }
         }
-        xg.sum = __uint_as_float(d[16]);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float s = bf16_bits_to_f32(sv[t][r]);
-            const float b = bf16_bits_to_f32(bv[t][r]);
-            const float dd = group_dot_biased<kGemvAcc>(wv[t][r], xg, mask, bias);
-            acc[r] = __builtin_fmaf(s, dd, acc[r]);
-            acc[r] = __builtin_fmaf(__builtin_fmaf(-128.f, s, b), xg.sum, acc[r]);
-        }
+        const float total = wave_reduce_rows<kVals>(acc, lane);
+        constexpr int shift = 6 - log2_rows<kVals>();
+        const int v = lane >> shift;  // r * MB + mm
+        if ((lane & ((1 << shift) - 1)) == 0 && m0 + v % MB < M)
+            y[(size_t)(m0 + v % MB) * N + n0 + v / MB] = f32_to_bf16_bits(total);
     }
-    const float total = wave_reduce_rows<R>(acc, lane);
-    constexpr int shift = 6 - log2_rows<R>();
-    if ((lane & ((1 << shift) - 1)) == 0) y[n0 + (lane >> shift)] = f32_to_bf16_bits(total);
 }
 
 }  // namespace w4mi
 
 using namespace w4mi;
+
+namespace w4mi {
+
+// The shared-x form for M rows of x (1 <= M <= kAffineBatchRows, K <=
+// kAffineBatchMaxK = 64 * 32 * kXChunks): MB rows of x per batch (4, or 2 where 4 chunks would take 80 KB
+// of LDS), one workgroup per 16 weight rows.
+void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, const uint16_t* x, uint16_t* y,
+                 int M, int K, int N, hipStream_t s) {
+    static_assert(kAffineBatchMaxK == 32 * kWave * kXChunks, "four chunks of 64 groups");
+    const int chunks = (K / 32 + kWave - 1) / kWave;
+    const int mb = M == 1 ? 1 : (M == 2 || chunks > 2) ? 2 : 4;
+    const dim3 grid((unsigned)(N / (kXWaves * kXRows))), block(kWave * kXWaves);
+#define W4_XLDS(T, MB) hipLaunchKernelGGL((qmv_affine4_xlds_kernel<T, MB>), grid, block, 0, s, w, scales, biases, x, y, M, K, N)
+    switch (chunks * 8 + mb) {
+        case 1 * 8 + 1: W4_XLDS(1, 1); break;
+        case 2 * 8 + 1: W4_XLDS(2, 1); break;
+        case 3 * 8 + 1: W4_XLDS(3, 1); break;
+        case 4 * 8 + 1: W4_XLDS(4, 1); break;
+        case 1 * 8 + 2: W4_XLDS(1, 2); break;
+        case 2 * 8 + 2: W4_XLDS(2, 2); break;
+        case 3 * 8 + 2: W4_XLDS(3, 2); break;
+        case 4 * 8 + 2: W4_XLDS(4, 2); break;
+        case 1 * 8 + 4: W4_XLDS(1, 4); break;
+        default: W4_XLDS(2, 4); break;
+    }
+#undef W4_XLDS
+}
+
+}  // namespace w4mi
 
 extern "C" w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
                                  const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
@@ -367,17 +457,11 @@ extern "C" w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, cons
     const int G = (int)(K / 32);
     const int chunks = (G + kWave - 1) / kWave;
     hipStream_t s = as_stream(stream);
-    const dim3 xgrid((unsigned)(N / (kXWaves * kXRows))), xblock(kWave * kXWaves);
-    static_assert(kXChunks == 4, "one case per chunk count below");
-    switch (chunks) {
-        case 1: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<1>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
-        case 2: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<2>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
-        case 3: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<3>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
-        case 4: hipLaunchKernelGGL((qmv_affine4_xlds_kernel<4>), xgrid, xblock, 0, s, w, scales, biases, x, y, (int)K, (int)N); break;
-        default:
-            hipLaunchKernelGGL((qmv_affine4_kernel<kGemvRows, 0, kGemvAux, kGemvAcc>), dim3((unsigned)(N / kGemvRows)), dim3(kWave), 0, s,
-                               w, scales, biases, x, y, (int)K, (int)N, chunks);
-            break;
+    if (chunks <= kXChunks) {
+        launch_xlds(w, scales, biases, x, y, 1, (int)K, (int)N, s);
+    } else {
+        hipLaunchKernelGGL((qmv_affine4_kernel<kGemvRows, 0, kGemvAux, kGemvAcc>), dim3((unsigned)(N / kGemvRows)), dim3(kWave),
+                           0, s, w, scales, biases, x, y, (int)K, (int)N, chunks);
     }
     return launch_status("qmv_affine4");
 }

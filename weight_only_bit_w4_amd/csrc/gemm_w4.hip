@@ -868,7 +868,10 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
         return fail(W4_EUNSUPPORTED, "qmm_affine4: implemented for K and N up to 2097152 (K=%lld N=%lld)", (long long)K,
                     (long long)N);
     hipStream_t s = as_stream(stream);
-    if (M <= 64) {
+    if (M <= kAffineBatchRows && K <= kAffineBatchMaxK) {
+        // A few rows: the GEMV form (each weight row read once for all of them).
+        launch_xlds(w, scales, biases, x, y, (int)M, (int)K, (int)N, s);
+    } else if (M <= 64) {
         constexpr int BM = 64, BN = 128;
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
         hipLaunchKernelGGL((qmm_affine4_kernel<1, 4, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, w, scales, biases,

@@ -30,6 +30,14 @@ struct IdScratchLayout {
 };
 IdScratchLayout id_scratch_layout(uint32_t n_experts, uint32_t n_tokens, uint32_t top_k, uint32_t k);
 
+// Affine INT4 GEMV form with x shared per workgroup (affine_gemv.hip), for
+// 1 <= M <= kAffineBatchRows rows of x and K <= kAffineBatchMaxK (N % 16 == 0):
+// every weight row is read once and applied to all M rows.
+constexpr int kAffineBatchRows = 8;
+constexpr int64_t kAffineBatchMaxK = 8192;
+void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, const uint16_t* x, uint16_t* y,
+                 int M, int K, int N, hipStream_t s);
+
 // Largest expert count the grouping kernel keeps in its LDS histogram.
 constexpr uint32_t kMaxExperts = 8192;
 
