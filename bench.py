@@ -39,11 +39,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "91de53da33ca6190", 36838239 + 114688),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b9a69d7d2c7bf951", 100826023 + 16803487),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b9a69d7d2c7bf951", 81613871 + 11291487),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "50ab93697ca97ae1", 114076239 + 5767168),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "", 0),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "e39dd6ce9117e166", 36822903 + 28676),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "ac1d231c67af13f0", 100826107 + 16800724),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "ac1d231c67af13f0", 81614018 + 11291200),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 114229054 + 5767168),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 13134050 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 14099609 + 45056),
 }
 
 
@@ -375,7 +376,7 @@ def main():
             "workload": "qmm_id_swiglu_q4_0 E=64 N=1408 K=2048 tokens=1 top_k=8 (fused silu(gate)*up; 8 experts' weights)",
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_decode")}}
+                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_swiglu_decode")}}
     if comps:
         out["components"] = comps
     if cpu is not None:
