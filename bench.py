@@ -19,7 +19,7 @@ under counter collection). Times come from HIP events recorded on the stream
 the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only decode|prefill|lut|moe|moe_decode] [--eager] [--calib]
+                       [--only decode|prefill|lut|moe|moe_decode|small] [--eager] [--calib]
 """
 from __future__ import annotations
 
@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "moe", "moe_decode"],
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "moe", "moe_decode", "small"],
                     help="time one kernel only")
     ap.add_argument("--eager", action="store_true", help="launch one by one instead of replaying graphs")
     ap.add_argument("--calib", action="store_true",
@@ -294,6 +294,29 @@ def main():
         result["moe_swiglu_decode"] = {"ms": ms, "GBps": wbytes6 / (ms * 1e-3) / 1e9, "launches": n6}
         del w6, x6, sets, out6, scratch6, g7, u7
 
+    # ------------------------------------------------------------ small batches (on request only)
+    if args.only == "small":
+        # qmm_affine4 with a few rows of x on the decode weights (not part of the default line).
+        ncopy = rotation(wbytes2)
+        ws = [to_dev(c2["w"].view(np.int32))]
+        ss = [to_dev(c2["scales"].view(np.int16), torch.bfloat16)]
+        bs = [to_dev(c2["biases"].view(np.int16), torch.bfloat16)]
+        for _ in range(ncopy - 1):
+            ws.append(ws[0].clone())
+            ss.append(ss[0].clone())
+            bs.append(bs[0].clone())
+        rng = np.random.default_rng(7)
+        small = {}
+        for Ms in (2, 4, 8, 16, 32, 64):
+            xs = to_dev(rng.standard_normal((Ms, K)).astype(np.float32)).to(torch.bfloat16)
+            ys = torch.empty((Ms, N), dtype=torch.bfloat16, device=dev)
+            ms = timer.run(lambda i: B.qmm_affine4(ws[i % ncopy], ss[i % ncopy], bs[i % ncopy], xs, ys), 600, 30,
+                           chunk=ncopy * 4)
+            small[f"M={Ms}"] = {"ms": round(ms, 5), "GBps": round(wbytes2 / (ms * 1e-3) / 1e9, 1)}
+            log(f"small batch: qmm_affine4 M={Ms} K={K} N={N}: {ms * 1e3:.2f} us")
+        result["small"] = small
+        del ws, ss, bs
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu and args.only in (None, "decode"):
@@ -377,6 +400,9 @@ def main():
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_swiglu_decode")}}
+    if "small" in result:
+        comps["affine_small_batch"] = {"workload": f"qmm_affine4 M=2..64 K={K} N={N} (decode weights)",
+                                       "unit": "GB/s weights", "points": result["small"]}
     if comps:
         out["components"] = comps
     if cpu is not None:

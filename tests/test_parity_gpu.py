@@ -105,14 +105,19 @@ def test_qmv_affine4(K, N, seed):
     (300, 128, 256),                      # 2 K steps (producer loop tail of 2)
     (257, 256, 160),                      # 4 K steps (one unrolled round + a tail of 1)
     (384, 1024, 384),                     # 16 K steps, several tiles each way
-    # at most 8 rows of x with K <= 8192: the GEMV form, every weight row read once for all rows
+    # at most 16 rows of x with K <= 8192: the GEMV form, every weight row read once for all rows
     (2, 4096, 14336),                     # the decode workload's weights, two rows (batches of 2)
     (3, 96, 64),                          # 3 groups, one batch of 4 with a missing row
     (8, 4096, 256),                       # 2 chunks, two batches of 4
     (5, 2080, 160),                       # ragged second chunk, a 1-row second batch
     (8, 8192, 64),                        # 4 chunks: batches of 2
     (6, 6144, 96),                        # 3 chunks: batches of 2
+    (16, 4096, 160),                      # 2 chunks, four batches of 4
+    (13, 8192, 32),                       # 4 chunks, batches of 2, a 1-row last batch
     (6, 8224, 32),                        # one group past the GEMV form: the matrix-core path
+    (17, 4096, 14336),                    # one row past it: the small-M matrix-core kernel, 128 K steps
+    (40, 96, 96),                         # 3 K steps: the load ring's prologue covers all of K
+    (64, 544, 256),                       # 17 K steps: ring wrap with a partial last round
 ])
 def test_qmm_affine4_small(M, K, N):
     c = synth.affine_case(M, K, N, seed=M + K + N)

@@ -14,6 +14,7 @@
 // to 80 bytes so the 16-byte operand reads of a 16-lane group hit distinct
 // banks.
 #include <type_traits>
+#include <utility>
 
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
@@ -23,6 +24,7 @@ namespace w4mi {
 constexpr int kGemmThreads = 256;
 constexpr int kBK = 32;          // K per step
 constexpr int kLds = kBK + 8;    // padded LDS row, in 16-bit elements
+constexpr int kSmallDepth = 8;   // steps of global loads in flight in the small-M kernels
 
 // ---------------------------------------------------------------- weight decoders
 // Each decoder fills, for one weight row n and the 8 consecutive k of
@@ -110,8 +112,21 @@ struct Mfma<true> {
 };
 
 // ---------------------------------------------------------------- GEMM skeleton
-// WM x WN wavefronts, each with FM x FN 16x16 fragments.
-template <int WM, int WN, int FM, int FN, bool kF16, class BDec>
+// Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>).
+template <int... Is, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// WM x WN wavefronts, each with FM x FN 16x16 fragments. Global loads run D
+// steps ahead in a register ring (a step has little matrix work next to
+// the latency of its loads, so the loop is bound by how many are in flight);
+// the LDS tiles are double buffered, one barrier per step.
+template <int WM, int WN, int FM, int FN, bool kF16, class BDec, int D>
 __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K,
                                              int N, const BDec& bdec, uint16_t* As, uint16_t* Bs) {
     constexpr int BM = WM * FM * 16;
@@ -135,51 +150,46 @@ __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uin
 #pragma unroll
         for (int g = 0; g < FN; ++g) acc[f][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 xr[XPT];
-    typename BDec::Raw wr[WPT];
+    u32x4 xr[D][XPT];
+    typename BDec::Raw wr[D][WPT];
 
-    auto load_step = [&](int k0) {
+    auto load_step = [&](auto slot, int k0) {
+        constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int piece = tid + i * kGemmThreads;
             const int row = piece / 4, p = piece % 4;
             const int m = m0 + row;
             if (m < M)
-                xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k0 + 8 * p);
+                xr[S][i] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k0 + 8 * p);
             else
-                xr[i] = u32x4{0u, 0u, 0u, 0u};
+                xr[S][i] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
             const int piece = tid + i * kGemmThreads;
             const int row = piece / 4, p = piece % 4;
-            bdec.load(n0 + row, k0, p, n0 + row < N, wr[i]);
+            bdec.load(n0 + row, k0, p, n0 + row < N, wr[S][i]);
         }
     };
-    auto store_step = [&](int buf) {
+    auto store_step = [&](auto slot, int buf) {
+        constexpr int S = decltype(slot)::value;
         uint16_t* as = As + buf * BM * kLds;
         uint16_t* bs = Bs + buf * BN * kLds;
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int piece = tid + i * kGemmThreads;
-            *reinterpret_cast<u32x4*>(as + (piece / 4) * kLds + 8 * (piece % 4)) = xr[i];
+            *reinterpret_cast<u32x4*>(as + (piece / 4) * kLds + 8 * (piece % 4)) = xr[S][i];
         }
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
             const int piece = tid + i * kGemmThreads;
             uint32_t v[4];
-            bdec.decode(wr[i], v);
+            bdec.decode(wr[S][i], v);
             *reinterpret_cast<u32x4*>(bs + (piece / 4) * kLds + 8 * (piece % 4)) = u32x4{v[0], v[1], v[2], v[3]};
         }
     };
-
-    const int steps = K / kBK;
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int kt = 0; kt < steps; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < steps) load_step((kt + 1) * kBK);
+    auto compute = [&](int buf) {
         const uint16_t* as = As + buf * BM * kLds;
         const uint16_t* bs = Bs + buf * BN * kLds;
         u32x4 a[FM], b[FN];
@@ -193,8 +203,25 @@ __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uin
         for (int f = 0; f < FM; ++f)
 #pragma unroll
             for (int g = 0; g < FN; ++g) acc[f][g] = Mfma<kF16>::run(a[f], b[g], acc[f][g]);
-        if (kt + 1 < steps) store_step(buf ^ 1);
-        __syncthreads();
+    };
+
+    // Step kt's loads sit in slot kt % D. Writing LDS buffer kt & 1 at step kt
+    // is safe: every wavefront passed step kt - 1's barrier, so it is done
+    // with step kt - 2's reads of that buffer.
+    const int steps = K / kBK;
+    static_for<D>([&](auto S) {
+        if (S < steps) load_step(S, S * kBK);
+    });
+    for (int kt0 = 0; kt0 < steps; kt0 += D) {
+        static_for<D>([&](auto S) {
+            const int kt = kt0 + S;
+            if (kt < steps) {
+                store_step(S, kt & 1);
+                __syncthreads();
+                if (kt + D < steps) load_step(S, (kt + D) * kBK);
+                compute(kt & 1);
+            }
+        });
     }
 
     // Epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each fragment.
@@ -222,7 +249,7 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_affine4_kernel(const uint32_
     __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * kLds];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * BN * kLds];
     AffineB dec{w, scales, biases, K};
-    gemm_w4_body<WM, WN, FM, FN, false>(x, y, M, K, N, dec, As, Bs);
+    gemm_w4_body<WM, WN, FM, FN, false, AffineB, kSmallDepth>(x, y, M, K, N, dec, As, Bs);
 }
 
 // ---------------------------------------------------------------- prefill GEMM (affine)
@@ -636,7 +663,7 @@ struct Book16 {
     float v[16];
 };
 
-template <int WM, int WN, int FM, int FN>
+template <int WM, int WN, int FM, int FN, int D>
 __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* __restrict__ x,
                                                                  const uint8_t* __restrict__ packed,
                                                                  const uint16_t* __restrict__ scales, Book16 book,
@@ -649,7 +676,7 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* 
     if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
     __syncthreads();
     LutB dec{packed, scales, K, block, book_s};
-    gemm_w4_body<WM, WN, FM, FN, true>(x, y, M, K, N, dec, As, Bs);
+    gemm_w4_body<WM, WN, FM, FN, true, LutB, D>(x, y, M, K, N, dec, As, Bs);
 }
 
 // ---------------------------------------------------------------- LUT GEMM, specialised wavefronts
@@ -902,7 +929,7 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
     if (M <= 64) {
         constexpr int BM = 64, BN = 128;
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-        hipLaunchKernelGGL((qmm_lut4_kernel<1, 4, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, x, packed, scales, b, y,
+        hipLaunchKernelGGL((qmm_lut4_kernel<1, 4, 4, 2, kSmallDepth>), dim3(tiles), dim3(kGemmThreads), 0, s, x, packed, scales, b, y,
                            (int)M, (int)K, (int)N, (int)block);
     } else if (K % kPBK == 0 && block >= 16 && (block & (block - 1)) == 0 && K <= (1 << 21) && N <= (1 << 21)) {
         int shift = 0;
@@ -913,7 +940,7 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
     } else {
         constexpr int BM = 256, BN = 128;
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-        hipLaunchKernelGGL((qmm_lut4_kernel<2, 2, 8, 4>), dim3(tiles), dim3(kGemmThreads), 0, s, x, packed, scales, b, y,
+        hipLaunchKernelGGL((qmm_lut4_kernel<2, 2, 8, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, x, packed, scales, b, y,
                            (int)M, (int)K, (int)N, (int)block);
     }
     return launch_status("qmm_lut4");

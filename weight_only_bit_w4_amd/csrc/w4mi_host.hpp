@@ -33,7 +33,7 @@ IdScratchLayout id_scratch_layout(uint32_t n_experts, uint32_t n_tokens, uint32_
 // Affine INT4 GEMV form with x shared per workgroup (affine_gemv.hip), for
 // 1 <= M <= kAffineBatchRows rows of x and K <= kAffineBatchMaxK (N % 16 == 0):
 // every weight row is read once and applied to all M rows.
-constexpr int kAffineBatchRows = 8;
+constexpr int kAffineBatchRows = 16;
 constexpr int64_t kAffineBatchMaxK = 8192;
 void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, const uint16_t* x, uint16_t* y,
                  int M, int K, int N, hipStream_t s);
