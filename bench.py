@@ -19,7 +19,7 @@ under counter collection). Times come from HIP events recorded on the stream
 the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--only decode|prefill|lut|moe|moe_decode|small] [--eager] [--calib]
+                       [--only decode|prefill|lut|lut_f32|moe|moe_decode|small] [--eager] [--calib]
 """
 from __future__ import annotations
 
@@ -68,12 +68,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "moe", "moe_decode", "small"],
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "lut", "lut_f32", "moe", "moe_decode", "small"],
                     help="time one kernel only")
     ap.add_argument("--eager", action="store_true", help="launch one by one instead of replaying graphs")
     ap.add_argument("--calib", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     return ap.parse_args()
+
+
+def oracle_free_f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns to f32 (numpy's own conversion)."""
+    return np.ascontiguousarray(bits).view(np.float16).astype(np.float32)
 
 
 def rotation(bytes_per_copy: int, min_total: int = 512 * 2**20) -> int:
@@ -234,6 +239,28 @@ def main():
         flops = 2.0 * M4 * N4 * K4
         result["lut"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12, "launches": n4}
         del x4, p4, s4, y4
+
+    # ------------------------------------------------------------ lookup codebook, single precision, 4 rows
+    if args.only in (None, "lut_f32"):
+        c8 = synth.lut_matmul_case()
+        K8, N8, blk8, M8 = c8["K"], c8["N"], c8["block"], 4
+        p8 = [to_dev(c8["packed"])]
+        s8 = [to_dev(oracle_free_f16_to_f32(c8["scales"]))]
+        wbytes8 = p8[0].numel() + s8[0].numel() * 4
+        ncopy8 = rotation(wbytes8)
+        for _ in range(ncopy8 - 1):
+            p8.append(p8[0].clone())
+            s8.append(s8[0].clone())
+        x8 = to_dev(np.random.default_rng(8).standard_normal((M8, K8)).astype(np.float32))
+        y8 = torch.empty((M8, N8), dtype=torch.float32, device=dev)
+        n8 = max(200, steps // 4)
+        for t8 in (1, 0):
+            log(f"lut f32: qmm_lut4_f32 M={M8} K={K8} N={N8} block {blk8} transpose={t8}, {ncopy8} weight copies, "
+                f"{n8} launches")
+            ms = timer.run(lambda i: B.qmm_lut4_f32(x8, p8[i % ncopy8], s8[i % ncopy8], c8["book"], N8, blk8, y=y8,
+                                                    transpose=t8), n8, max(10, warmup // 2), chunk=ncopy8 * 2)
+            result[f"lut_f32_t{t8}"] = {"ms": ms, "GBps": wbytes8 / (ms * 1e-3) / 1e9, "M": M8}
+        del p8, s8, x8, y8
 
     # ------------------------------------------------------------ expert-routed Q4_0
     if args.only in (None, "moe"):
@@ -400,6 +427,14 @@ def main():
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe_swiglu_decode")}}
+    for t8, layout in ((1, "[N, K]"), (0, "[K, N]")):
+        if f"lut_f32_t{t8}" in result:
+            p = result[f"lut_f32_t{t8}"]
+            comps[f"lut_f32_transpose{t8}"] = {
+                "workload": f"qmm_lut4_f32 M=4 K=4096 N=11008 block 64, W {layout}, f32 x/scales/y",
+                "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
+                "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": None}}
     if "small" in result:
         comps["affine_small_batch"] = {"workload": f"qmm_affine4 M=2..64 K={K} N={N} (decode weights)",
                                        "unit": "GB/s weights", "points": result["small"]}

@@ -98,6 +98,27 @@ w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const uint16_t* sca
                    int32_t block, int32_t transpose, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Lookup-codebook 4-bit matmul [P2], single-precision path (the page's
+ * mlx_lookup4_matmul kernel and CPU branch, taken when the compute type is
+ * f32: the decoded weight is not rounded).
+ *
+ *   y[m][n] = sum_k x[m][k] * W(n, k),  W = book[code(flat)] * scale[flat / block]
+ *   (the product in f32), flat = n*K + k when transpose != 0 (W stored [N, K]),
+ *   k*N + n when transpose == 0 (W stored [K, N]); code(flat) is the HIGH
+ *   nibble of packed[flat / 2] for even flat, the LOW nibble for odd.
+ *
+ * x       device f32 [M, K]; y device f32 [M, N] (written).
+ * packed  device uint8 [ceil(N*K/2)]; scales device f32 [ceil(N*K/block)].
+ * book    HOST pointer to 16 f32 codebook values (copied at the call).
+ * Blocks run over the flat index and may straddle rows. Products are summed
+ * in K tiles whose partial sums are added with compensation ([P2] kernel's
+ * correction term). Contract as qmm_lut4 (M >= 0, K > 0, N > 0, block > 0 and
+ * even), both layouts, any K and N; M up to 262,140. M == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const float* scales, const float* book, float* y,
+                       int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose, void* stream);
+
+/* ------------------------------------------------------------------------
  * Expert-routed matmul over GGML Q4_0 blocks [P3].
  *
  * For every routed row r = token * top_k + slot, e = ids[r] and
@@ -190,6 +211,7 @@ w4_status qmm_id_swiglu_q4_0(const float* gate, const float* up, const uint8_t* 
 w4_status w4_check_affine(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t bits,
                           int32_t decode);
 w4_status w4_check_lut(int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose);
+w4_status w4_check_lut_f32(int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose);
 w4_status w4_check_id(const w4_id_params* p, size_t scratch_bytes);
 w4_status w4_check_id_swiglu(const w4_id_params* p);
 

@@ -197,6 +197,15 @@ def lut4(x_f16, packed, scales_f16, book, M: int, K: int, N: int, block: int,
     return acc, y
 
 
+def lut4_f32(x_f32, packed, scales_f32, book, M: int, K: int, N: int, block: int, transpose: bool = True):
+    """Single-precision path: x f32, scales f32, the decoded weight not rounded,
+    y f32. Returns (acc fp64 [M, N], y f32)."""
+    rows, cols = (N, K) if transpose else (K, N)
+    W = lut_decode(packed, scales_f32, book, rows, cols, block, False)
+    acc = lut_matmul(x_f32, W, M, K, N, transpose)
+    return acc, acc.astype(np.float32)
+
+
 def lut4_points(x_f16, packed, scales_f16, book, K: int, block: int, ms, ns, round_half: bool = True):
     x, packed, s, book = _c(x_f16, np.uint16), _c(packed, np.uint8), _c(scales_f16, np.uint16), _c(book, np.float32)
     ms, ns = _c(ms, np.int64), _c(ns, np.int64)

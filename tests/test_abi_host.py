@@ -181,3 +181,18 @@ def test_id_swiglu_limits_are_reported_before_any_launch(kw):
     st = B.lib().qmm_id_swiglu_q4_0(_fake(), _fake(), _fake(), _fake(), _fake(), ctypes.byref(p), None, None)
     assert st == B.W4_EUNSUPPORTED
     assert "256" in B.last_error() and "8192" in B.last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 4096, 11008, 64, 1), B.W4_OK),
+    ((4, 4096, 11008, 64, 0), B.W4_OK),      # both layouts
+    ((2, 5, 3, 64, 0), B.W4_OK),             # the page's worked example: blocks straddle rows
+    ((0, 5, 3, 2, 1), B.W4_OK),              # empty batch
+    ((-1, 5, 3, 2, 1), B.W4_EINVAL),
+    ((1, 0, 3, 2, 1), B.W4_EINVAL),
+    ((1, 5, 3, 3, 1), B.W4_EINVAL),          # odd block
+    ((1, 5, 3, 0, 1), B.W4_EINVAL),
+    ((262141, 32, 32, 2, 1), B.W4_EUNSUPPORTED),
+])
+def test_lut_f32_contract(args, status):
+    assert B.w4_check_lut_f32(*args) == status

@@ -7,6 +7,9 @@ element (spanning several tiles and ragged tails); the full-size workloads in
 the launch configuration the benchmark times are compared at sampled outputs
 the oracle computes one by one.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -318,3 +321,67 @@ def test_qmm_id_swiglu_q4_0_odd_ids_and_saturated_gates():
     assert np.all(got[4] == 0) and np.all(got[10] == 0) and bad == 2
     got2, none = _swiglu_run(c, ids, bad=False)        # no count requested
     assert none is None and np.array_equal(got2, got)
+
+
+# ---------------------------------------------------------------- lookup codebook, single precision
+def test_qmm_lut4_f32_worked_example_from_the_page():
+    # The page's unit test, exactly: every value is a dyadic rational, so the
+    # f32 result must equal the printed fractions bit for bit, in both layouts.
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "lut4_worked_example.json")))
+    book = [i * i / 32.0 for i in range(16)]
+    rows, cols, block = g["rows"], g["cols"], g["block"]
+    for case in g["cases"]:
+        packed = torch.full((g["packed_len"],), case["byte"], dtype=torch.uint8, device=DEV)
+        scales = torch.tensor([case["scale"]], dtype=torch.float32, device=DEV)
+        for transpose, key in ((0, "non_transposed"), (1, "transposed")):
+            K, N = (cols, rows) if transpose else (rows, cols)
+            x = torch.full((g["x_rows"], K), g["x_value"], dtype=torch.float32, device=DEV)
+            y = B.qmm_lut4_f32(x, packed, scales, book, N, block, transpose=transpose).cpu().numpy()
+            want = np.array([num / den for num, den in case[key]], np.float32)
+            for r in range(g["x_rows"]):
+                assert np.array_equal(y[r], want), (case["byte"], key, y[r], want)
+
+
+def _lut_f32_case(M, K, N, block, transpose, seed):
+    rng = np.random.default_rng(seed)
+    count = N * K
+    packed = rng.integers(0, 256, (count + 1) // 2, dtype=np.uint16).astype(np.uint8)
+    scales = rng.uniform(0.01, 0.05, -(-count // block)).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    book = synth.normal_codebook()
+    return x, packed, scales, book
+
+
+@pytest.mark.parametrize("M,K,N,block,transpose", [
+    (1, 4096, 11008, 64, 1),     # one row on the LUT workload's weights, [N, K]
+    (4, 4096, 11008, 64, 0),     # four rows, the [K, N] layout
+    (3, 100, 70, 6, 1),          # odd sizes: blocks straddle rows, a partial 64-lane step
+    (3, 100, 70, 6, 0),
+    (7, 33, 130, 2, 0),          # 3 chunks of 64 columns, K not a multiple of the 16 wavefronts
+    (130, 48, 20, 16, 1),        # more than 128 rows: 33 row groups of 4
+    (2, 5000, 40, 10, 0),        # 16 wavefronts over K = 5000 with blocks across rows
+])
+def test_qmm_lut4_f32(M, K, N, block, transpose):
+    x, packed, scales, book = _lut_f32_case(M, K, N, block, transpose, seed=M + K + N)
+    y = B.qmm_lut4_f32(_t(x), _t(packed), _t(scales), book, N, block, transpose=transpose).cpu().numpy()
+    acc, _ = oracle.lut4_f32(x, packed, scales, book, M, K, N, block, bool(transpose))
+    _assert_within(y.astype(np.float64), acc, K, float(np.abs(x).max()), float(np.abs(scales).max()),
+                   f"lut f32 M={M} K={K} N={N} block={block} t={transpose}")
+
+
+@pytest.mark.parametrize("transpose", [0, 1])
+def test_qmm_lut4_f32_compensated_sum(transpose):
+    # Long K with every term positive (positive codebook and x), where a plain
+    # f32 running sum gathers rounding error ~ 2^-24 sqrt(K / 3) of the total
+    # (about 4e-6 here): every output stays within 1e-6 of it.
+    M, K, N, block = 2, 16384, 64, 64
+    x, packed, scales, book = _lut_f32_case(M, K, N, block, transpose, seed=3)
+    x = np.abs(x) + 1.0
+    book = np.abs(book) + np.float32(0.1)
+    y = B.qmm_lut4_f32(_t(x), _t(packed), _t(scales), book, N, block, transpose=transpose).cpu().numpy()
+    acc, _ = oracle.lut4_f32(x, packed, scales, book, M, K, N, block, bool(transpose))
+    rows, cols = (N, K) if transpose else (K, N)
+    W = oracle.lut_decode(packed, scales, book, rows, cols, block, False).astype(np.float64)
+    Wt = W if transpose else W.T
+    mag = np.abs(x.astype(np.float64)) @ np.abs(Wt).T
+    assert np.all(np.abs(y - acc) <= 1e-6 * mag)

@@ -52,11 +52,13 @@ SIGNATURES = {
     "qmm_affine4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "qmv_affine4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "qmm_lut4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
+    "qmm_lut4_f32": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "qmm_id_q4_0_scratch_bytes": ([_U32, _U32, _U32, _U32], _SZ),
     "qmm_id_q4_0": ([_P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _SZ, _P], ctypes.c_int),
     "qmm_id_swiglu_q4_0": ([_P, _P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _P], ctypes.c_int),
     "w4_check_affine": ([_I64, _I64, _I64, _I32, _I32, _I32], ctypes.c_int),
     "w4_check_lut": ([_I64, _I64, _I64, _I32, _I32], ctypes.c_int),
+    "w4_check_lut_f32": ([_I64, _I64, _I64, _I32, _I32], ctypes.c_int),
     "w4_check_id": ([ctypes.POINTER(IdParams), _SZ], ctypes.c_int),
     "w4_check_id_swiglu": ([ctypes.POINTER(IdParams)], ctypes.c_int),
     "w4_unpack_affine": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
@@ -149,6 +151,19 @@ def qmm_lut4(x, packed, scales, book, N: int, block: int, y=None, transpose: int
     return y
 
 
+def qmm_lut4_f32(x, packed, scales, book, N: int, block: int, y=None, transpose: int = 1):
+    """y [M, N] f32 = x [M, K] f32 . W, W = book[code] * scale (f32, unrounded); W is [N, K]
+    when transpose else [K, N]; book: 16 host floats."""
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    book_host = (ctypes.c_float * 16)(*[float(v) for v in book])
+    _check(lib().qmm_lut4_f32(_dev(x, "x", F32), _dev(packed, "packed", U8), _dev(scales, "scales", F32),
+                              ctypes.cast(book_host, ctypes.c_void_p), _dev(y, "y", F32), M, K, N, block, transpose,
+                              _stream(x)))
+    return y
+
+
 # ---------------------------------------------------------------- expert-routed Q4_0
 def qmm_id_q4_0_scratch_bytes(n_experts: int, n_tokens: int, top_k: int, k: int) -> int:
     return int(lib().qmm_id_q4_0_scratch_bytes(n_experts, n_tokens, top_k, k))
@@ -197,6 +212,10 @@ def w4_check_affine(M, K, N, group_size=32, bits=4, decode=0) -> int:
 
 def w4_check_lut(M, K, N, block, transpose=1) -> int:
     return int(lib().w4_check_lut(M, K, N, block, transpose))
+
+
+def w4_check_lut_f32(M, K, N, block, transpose=1) -> int:
+    return int(lib().w4_check_lut_f32(M, K, N, block, transpose))
 
 
 def w4_check_id(params: IdParams, scratch_bytes: int) -> int:

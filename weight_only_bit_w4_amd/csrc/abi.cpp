@@ -98,6 +98,24 @@ w4_status w4_check_lut(int64_t M, int64_t K, int64_t N, int32_t block, int32_t t
     return W4_OK;
 }
 
+// lut4 page, single-precision path: the same contract as qmm_lut4 (recognize:
+// block positive and even; execute: M, K, N sizes), both weight layouts, any
+// K and N, blocks over the flat index.
+w4_status w4_check_lut_f32(int64_t M, int64_t K, int64_t N, int32_t block, int32_t transpose) {
+    (void)transpose;
+    if (M < 0 || K <= 0 || N <= 0)
+        return fail(W4_EINVAL, "qmm_lut4_f32: need M >= 0 and K, N > 0 (M=%lld K=%lld N=%lld)", (long long)M,
+                    (long long)K, (long long)N);
+    if (block <= 0 || block % 2 != 0)
+        return fail(W4_EINVAL, "qmm_lut4_f32: block must be positive and even, got %d", block);
+    if (M > INT32_MAX || K > INT32_MAX || N > INT32_MAX || N * K > (int64_t)1 << 40)
+        return fail(W4_EINVAL, "qmm_lut4_f32: dimensions too large");
+    if (M > 4ll * 65535)
+        return fail(W4_EUNSUPPORTED, "qmm_lut4_f32: implemented for M up to 262140, got %lld", (long long)M);
+    clear_error();
+    return W4_OK;
+}
+
 // mlx-native MoE page, quantized_matmul_id_ggml: every dimension positive,
 // K a multiple of the block size, expert stride and buffer lengths large
 // enough; plus the scratch the grouping needs.
