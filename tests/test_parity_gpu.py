@@ -360,6 +360,9 @@ def _lut_f32_case(M, K, N, block, transpose, seed):
     (7, 33, 130, 2, 0),          # 3 chunks of 64 columns, K not a multiple of the 16 wavefronts
     (130, 48, 20, 16, 1),        # more than 128 rows: 33 row groups of 4
     (2, 5000, 40, 10, 0),        # 16 wavefronts over K = 5000 with blocks across rows
+    (5, 520, 72, 8, 1),          # aligned [N, K] form: 65 groups of 8 (a partial 64-lane step)
+    (6, 72, 260, 4, 0),          # aligned [K, N] form: 3 column groups of 128, the last partial
+    (1, 4096, 11008, 64, 0),     # one row, [K, N], the LUT workload's weights
 ])
 def test_qmm_lut4_f32(M, K, N, block, transpose):
     x, packed, scales, book = _lut_f32_case(M, K, N, block, transpose, seed=M + K + N)

@@ -19,7 +19,10 @@
 //  - [K, N]: lane l owns column n0 + l; 16 wavefronts split K into contiguous
 //    ranges; x[m][k] is the same for every lane (scalar loads); the 16
 //    wavefronts' sums meet in LDS and are added in K order, compensated.
-// Rows of x are taken 4 at a time (the grid's y dimension).
+// Rows of x are taken 4 at a time (the grid's y dimension). Aligned shapes
+// (8 codes along the contiguous axis within one block; [K, N] with N a
+// multiple of the block) read a dword or a byte of codes and one scale at a
+// time; the rest decode element by element from the flat index.
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
@@ -185,6 +188,211 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const 
     }
 }
 
+
+// ---------------------------------------------------------------- aligned forms
+// When each 8 consecutive codes along the contiguous axis share one block
+// (block % 8 == 0 and the contiguous length a multiple of block), a lane reads
+// 8 codes (one dword) and one scale at a time and looks the codes up in an LDS
+// copy of the codebook.
+__device__ __forceinline__ void lut_decode8(uint32_t word, float s, const float* book_s, float (&w)[8]) {
+    // Byte i holds flat indices 2i (high nibble) and 2i + 1 (low nibble).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t byte = (word >> (8 * i)) & 0xFFu;
+        w[2 * i] = book_s[byte >> 4] * s;
+        w[2 * i + 1] = book_s[byte & 15u] * s;
+    }
+}
+
+// [N, K], K % block == 0, block % 8 == 0: a wavefront owns 4 weight rows, lane
+// l takes the 8-wide K groups l, l + 64, ... (one dword of codes per row).
+__global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows8_kernel(const float* __restrict__ x,
+                                                                             const uint8_t* __restrict__ packed,
+                                                                             const float* __restrict__ scales,
+                                                                             LutBook book, float* __restrict__ y,
+                                                                             int M, int K, int N, int block) {
+    __shared__ float book_s[16];
+    if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = (blockIdx.x * kF32RowWaves + wave) * kF32Rows;
+    const int m0 = blockIdx.y * kF32M;
+    const int G8 = K / 8, bpr = K / block;  // 8-wide groups and blocks per row
+    const int per8 = block / 8;
+    float acc[kF32Rows][kF32M], cor[kF32Rows][kF32M], part[kF32Rows][kF32M];
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m) acc[r][m] = cor[r][m] = part[r][m] = 0.f;
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(packed);
+    // One step's operands: x (8 k of each row of x) and a dword of codes and a
+    // scale for each weight row. The next step's are loaded before this one
+    // is used.
+    struct Step {
+        f32x4 xa[kF32M], xb[kF32M];
+        uint32_t word[kF32Rows];
+        float sc[kF32Rows];
+    };
+    auto load = [&](int g0, Step& st) {
+        const int g = g0 + lane;
+        const bool gv = g < G8;
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m) {
+            const bool v = gv && m0 + m < M;
+            const f32x4* xp = reinterpret_cast<const f32x4*>(x + (size_t)(m0 + m) * K + 8 * g);
+            st.xa[m] = v ? xp[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+            st.xb[m] = v ? xp[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int r = 0; r < kF32Rows; ++r) {
+            const int n = nb + r;
+            const bool v = gv && n < N;
+            st.word[r] = v ? words[(size_t)n * G8 + g] : 0u;
+            st.sc[r] = v ? scales[(size_t)n * bpr + g / per8] : 0.f;
+        }
+    };
+    Step cur, nxt;
+    load(0, cur);
+    int it = 0;
+    for (int g0 = 0; g0 < G8; g0 += 64) {
+        if (g0 + 64 < G8) load(g0 + 64, nxt);
+#pragma unroll
+        for (int r = 0; r < kF32Rows; ++r) {
+            float w[8];
+            lut_decode8(cur.word[r], cur.sc[r], book_s, w);
+#pragma unroll
+            for (int m = 0; m < kF32M; ++m) {
+                float p = part[r][m];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) p = __builtin_fmaf(cur.xa[m][t], w[t], p);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) p = __builtin_fmaf(cur.xb[m][t], w[4 + t], p);
+                part[r][m] = p;
+            }
+        }
+        if (++it == kF32Tile / 8) {  // 16 products per lane and output per tile
+            it = 0;
+#pragma unroll
+            for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+                for (int m = 0; m < kF32M; ++m) {
+                    kahan_add(acc[r][m], cor[r][m], part[r][m]);
+                    part[r][m] = 0.f;
+                }
+        }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r)
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m) {
+            kahan_add(acc[r][m], cor[r][m], part[r][m]);
+            float v = acc[r][m];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            const int n = nb + r;
+            if (lane == 0 && n < N && m0 + m < M) y[(size_t)(m0 + m) * N + n] = v;
+        }
+}
+
+// [K, N], N % block == 0, block % 2 == 0: lane l owns columns 2l, 2l + 1 of a
+// 128-column group (one byte of codes per k; the two share a scale, since an
+// even block never splits a byte); 16 wavefronts split K. A wavefront stages
+// its slice of x in LDS (its own region, 256 k at a time, read back as
+// broadcasts) and loads the codes and scales of 16 k before using them.
+constexpr int kF32XChunk = 256;
+__global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const float* __restrict__ x,
+                                                                             const uint8_t* __restrict__ packed,
+                                                                             const float* __restrict__ scales,
+                                                                             LutBook book, float* __restrict__ y,
+                                                                             int M, int K, int N, int block) {
+    __shared__ float book_s[16];
+    __shared__ __attribute__((aligned(16))) float xs[kF32ColWaves][kF32M][kF32XChunk];
+    __shared__ float red[kF32ColWaves][2 * kF32M][64];
+    if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = blockIdx.x * 128 + 2 * lane;  // and n + 1
+    const bool nv = n < N;                      // N is even: both or neither
+    const int m0 = blockIdx.y * kF32M;
+    const int span = (K + kF32ColWaves - 1) / kF32ColWaves;
+    const int kb = min(K, wave * span), ke = min(K, kb + span);
+    const int bpr = N / block;
+    float acc[2][kF32M], cor[2][kF32M], part[2][kF32M];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m) acc[c][m] = cor[c][m] = part[c][m] = 0.f;
+    const int nbyte = N / 2, sidx = nv ? n / block : 0;
+    float* xw = &xs[wave][0][0];
+    for (int c0 = kb; c0 < ke; c0 += kF32XChunk) {
+        const int len = min(kF32XChunk, ke - c0);
+        // This wavefront's x slice for k in [c0, c0 + len), zero past the end.
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m)
+            for (int t = lane; t < kF32XChunk; t += 64)
+                xw[m * kF32XChunk + t] = (t < len && m0 + m < M) ? x[(size_t)(m0 + m) * K + c0 + t] : 0.f;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wavefront's own LDS writes are done
+        uint32_t byte[kF32Tile], nbyte_[kF32Tile];
+        float sc[kF32Tile], nsc[kF32Tile];
+        auto load = [&](int t0, uint32_t (&bt)[kF32Tile], float (&st)[kF32Tile]) {
+#pragma unroll
+            for (int u = 0; u < kF32Tile; ++u) {
+                const int k = c0 + t0 + u;
+                const bool v = nv && t0 + u < len;
+                bt[u] = v ? packed[(size_t)k * nbyte + (n >> 1)] : 0u;
+                st[u] = v ? scales[(size_t)k * bpr + sidx] : 0.f;
+            }
+        };
+        load(0, byte, sc);
+        for (int t0 = 0; t0 < len; t0 += kF32Tile) {
+            if (t0 + kF32Tile < len) load(t0 + kF32Tile, nbyte_, nsc);
+#pragma unroll
+            for (int u = 0; u < kF32Tile; u += 4) {
+                f32x4 xv[kF32M];
+#pragma unroll
+                for (int m = 0; m < kF32M; ++m) xv[m] = *reinterpret_cast<const f32x4*>(xw + m * kF32XChunk + t0 + u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float w0 = book_s[byte[u + e] >> 4] * sc[u + e], w1 = book_s[byte[u + e] & 15u] * sc[u + e];
+#pragma unroll
+                    for (int m = 0; m < kF32M; ++m) {
+                        part[0][m] = __builtin_fmaf(xv[m][e], w0, part[0][m]);
+                        part[1][m] = __builtin_fmaf(xv[m][e], w1, part[1][m]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int m = 0; m < kF32M; ++m) {
+                    kahan_add(acc[c][m], cor[c][m], part[c][m]);
+                    part[c][m] = 0.f;
+                }
+#pragma unroll
+            for (int u = 0; u < kF32Tile; ++u) {
+                byte[u] = nbyte_[u];
+                sc[u] = nsc[u];
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m) red[wave][c * kF32M + m][lane] = acc[c][m];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int m = 0; m < kF32M; ++m) {
+                float a = 0.f, e = 0.f;
+                for (int v = 0; v < kF32ColWaves; ++v) kahan_add(a, e, red[v][c * kF32M + m][lane]);  // K order
+                if (nv && m0 + m < M) y[(size_t)(m0 + m) * N + n + c] = a;
+            }
+    }
+}
 }  // namespace w4mi
 
 using namespace w4mi;
@@ -203,8 +411,16 @@ extern "C" w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const f
     const unsigned my = (unsigned)((M + kF32M - 1) / kF32M);
     if (transpose) {
         const dim3 grid((unsigned)((N + kF32RowWaves * kF32Rows - 1) / (kF32RowWaves * kF32Rows)), my);
-        hipLaunchKernelGGL(lut4_f32_rows_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y, (int)M,
-                           (int)K, (int)N, (int)block);
+        if (block % 8 == 0 && K % block == 0 && ((uintptr_t)packed & 3u) == 0 && ((uintptr_t)x & 15u) == 0)
+            hipLaunchKernelGGL(lut4_f32_rows8_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y,
+                               (int)M, (int)K, (int)N, (int)block);
+        else
+            hipLaunchKernelGGL(lut4_f32_rows_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y,
+                               (int)M, (int)K, (int)N, (int)block);
+    } else if (N % block == 0) {
+        const dim3 grid((unsigned)((N + 127) / 128), my);
+        hipLaunchKernelGGL(lut4_f32_cols2_kernel, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
+                           (int)M, (int)K, (int)N, (int)block);
     } else {
         const dim3 grid((unsigned)((N + 63) / 64), my);
         hipLaunchKernelGGL(lut4_f32_cols_kernel, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y, (int)M,
