@@ -28,6 +28,8 @@
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
+#include <cmath>
+
 namespace w4mi {
 
 constexpr int kGemvRows = 4;  // output rows per wavefront of the long-K form (one wavefront per workgroup)
@@ -37,6 +39,7 @@ constexpr int kXWaves = 8;    // wavefronts per workgroup of the shared-x form
 constexpr int kXRows = 2;     // output rows per wavefront of the shared-x form
 constexpr int kXChunks = 4;   // the shared-x form covers up to 4 x 64 groups
 constexpr int kXStride = 20;  // LDS dwords per group: 16 pairs, the sum, pad (80 B: conflict-free 16-byte reads)
+constexpr int kCUs = 256;     // compute units of the MI355X
 
 // Lane view of one quantisation group of x: bf16 pairs matching the nibble
 // pairs (i, i + 4) of each of the group's four words, and the group sum.
@@ -256,11 +259,11 @@ __global__ __launch_bounds__(kWave) void qmv_affine4_kernel(
 // partial sum that the group's four (adjacent) lanes add up. Pieces past the
 // last group or row load as zeros (the buffer bound), so idle groups
 // contribute nothing. Weights stay in registers across batches.
-template <int T, int MB>
-__global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
+template <int T, int MB, int WPG = kXWaves>
+__global__ __launch_bounds__(kWave * WPG) void qmv_affine4_xlds_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
-    constexpr int R = kXRows, kThreads = kWave * kXWaves;
+    constexpr int R = kXRows, kThreads = kWave * WPG;
     constexpr int kRowPieces = T * kWave * 4;  // pieces of one x row
     constexpr int kPieces = MB * kRowPieces;
     constexpr int kPerLane = (kPieces + kThreads - 1) / kThreads;
@@ -268,16 +271,21 @@ __global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t xp[MB * T * kWave * kXStride];
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n0 = (blockIdx.x * kXWaves + wave) * R;  // N % 16 == 0: rows n0, n0 + 1 exist
+    const int n0 = (blockIdx.x * WPG + wave) * R;  // N is even: rows n0 and n0 + 1 exist when n0 < N
     const int G = K / 32;
     const uint32_t mask = vreg(kAffinePairMask), bias = vreg(kAffinePairBias);
     const int wrow = K / 2, srow = G * 2;
+    // A wavefront past the last row (when N is not a multiple of the
+    // workgroup's rows) reads nothing and stores nothing, but still takes
+    // part in the barriers.
+    const bool live = n0 < N;
+    const size_t nl = live ? (size_t)n0 : 0;
     const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * wrow, (uint32_t)(R * wrow));
+        make_rsrc(reinterpret_cast<const uint8_t*>(w) + nl * wrow, live ? (uint32_t)(R * wrow) : 0u);
     const __amdgpu_buffer_rsrc_t ssrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow, (uint32_t)(R * srow));
+        make_rsrc(reinterpret_cast<const uint8_t*>(scales) + nl * srow, live ? (uint32_t)(R * srow) : 0u);
     const __amdgpu_buffer_rsrc_t bsrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow, (uint32_t)(R * srow));
+        make_rsrc(reinterpret_cast<const uint8_t*>(biases) + nl * srow, live ? (uint32_t)(R * srow) : 0u);
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
 
     // Issue order = consumption order (loads complete in issue order for the
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(kWave * kXWaves) void qmv_affine4_xlds_kernel(
         const float total = wave_reduce_rows<kVals>(acc, lane);
         constexpr int shift = 6 - log2_rows<kVals>();
         const int v = lane >> shift;  // r * MB + mm
-        if ((lane & ((1 << shift) - 1)) == 0 && m0 + v % MB < M)
+        if (live && (lane & ((1 << shift) - 1)) == 0 && m0 + v % MB < M)
             y[(size_t)(m0 + v % MB) * N + n0 + v / MB] = f32_to_bf16_bits(total);
     }
 }
@@ -428,12 +436,40 @@ void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* bias
     const int chunks = (K / 32 + kWave - 1) / kWave;
     const int mb = M == 1 ? 1 : (M == 2 || chunks > 2) ? 2 : 4;
     const dim3 grid((unsigned)(N / (kXWaves * kXRows))), block(kWave * kXWaves);
+    if (mb == 1) {
+        // One row of x: pick 8, 7 or 6 wavefronts per workgroup so that the
+        // workgroups fill whole rounds of the 256 compute units best (every
+        // CU then streams the same share of the weights to the end).
+        int best = kXWaves;
+        double best_eff = 0.0;
+        for (int wpg = kXWaves; wpg >= kXWaves - 2; --wpg) {
+            const double rounds = (double)((N + 2 * wpg - 1) / (2 * wpg)) / kCUs;
+            const double eff = rounds / std::ceil(rounds);
+            if (eff > best_eff + 1e-9) {
+                best_eff = eff;
+                best = wpg;
+            }
+        }
+        const dim3 g1((unsigned)((N + kXRows * best - 1) / (kXRows * best))), b1(kWave * best);
+#define W4_XLDS1(T, W) hipLaunchKernelGGL((qmv_affine4_xlds_kernel<T, 1, W>), g1, b1, 0, s, w, scales, biases, x, y, M, K, N)
+#define W4_XLDS1_T(T) \
+    switch (best) {   \
+        case 7: W4_XLDS1(T, 7); break; \
+        case 6: W4_XLDS1(T, 6); break; \
+        default: W4_XLDS1(T, kXWaves); break; \
+    }
+        switch (chunks) {
+            case 1: W4_XLDS1_T(1); break;
+            case 2: W4_XLDS1_T(2); break;
+            case 3: W4_XLDS1_T(3); break;
+            default: W4_XLDS1_T(4); break;
+        }
+#undef W4_XLDS1_T
+#undef W4_XLDS1
+        return;
+    }
 #define W4_XLDS(T, MB) hipLaunchKernelGGL((qmv_affine4_xlds_kernel<T, MB>), grid, block, 0, s, w, scales, biases, x, y, M, K, N)
     switch (chunks * 8 + mb) {
-        case 1 * 8 + 1: W4_XLDS(1, 1); break;
-        case 2 * 8 + 1: W4_XLDS(2, 1); break;
-        case 3 * 8 + 1: W4_XLDS(3, 1); break;
-        case 4 * 8 + 1: W4_XLDS(4, 1); break;
         case 1 * 8 + 2: W4_XLDS(1, 2); break;
         case 2 * 8 + 2: W4_XLDS(2, 2); break;
         case 3 * 8 + 2: W4_XLDS(3, 2); break;
