@@ -45,6 +45,8 @@ TRAFFIC = {
     "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 114229054 + 5767168),
     "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 13134050 + 45088),
     "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 14099609 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "", 0),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "", 0),
 }
 
 
@@ -434,7 +436,7 @@ def main():
                 "workload": f"qmm_lut4_f32 M=4 K=4096 N=11008 block 64, W {layout}, f32 x/scales/y",
                 "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
                 "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": None}}
+                             "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic(f"lut_f32_t{t8}")}}
     if "small" in result:
         comps["affine_small_batch"] = {"workload": f"qmm_affine4 M=2..64 K={K} N={N} (decode weights)",
                                        "unit": "GB/s weights", "points": result["small"]}

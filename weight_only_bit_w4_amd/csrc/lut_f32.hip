@@ -334,11 +334,14 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
             for (int t = lane; t < kF32XChunk; t += 64)
                 xw[m * kF32XChunk + t] = (t < len && m0 + m < M) ? x[(size_t)(m0 + m) * K + c0 + t] : 0.f;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wavefront's own LDS writes are done
-        uint32_t byte[kF32Tile], nbyte_[kF32Tile];
-        float sc[kF32Tile], nsc[kF32Tile];
-        auto load = [&](int t0, uint32_t (&bt)[kF32Tile], float (&st)[kF32Tile]) {
+        // Codes and scales go 8 steps at a time, the next 8 loaded before the
+        // current 8 are used; every second batch closes a 16-product tile.
+        constexpr int kB = kF32Tile / 2;
+        uint32_t byte[kB], nbyte_[kB];
+        float sc[kB], nsc[kB];
+        auto load = [&](int t0, uint32_t (&bt)[kB], float (&st)[kB]) {
 #pragma unroll
-            for (int u = 0; u < kF32Tile; ++u) {
+            for (int u = 0; u < kB; ++u) {
                 const int k = c0 + t0 + u;
                 const bool v = nv && t0 + u < len;
                 bt[u] = v ? packed[(size_t)k * nbyte + (n >> 1)] : 0u;
@@ -346,10 +349,10 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
             }
         };
         load(0, byte, sc);
-        for (int t0 = 0; t0 < len; t0 += kF32Tile) {
-            if (t0 + kF32Tile < len) load(t0 + kF32Tile, nbyte_, nsc);
+        for (int t0 = 0; t0 < len; t0 += kB) {
+            if (t0 + kB < len) load(t0 + kB, nbyte_, nsc);
 #pragma unroll
-            for (int u = 0; u < kF32Tile; u += 4) {
+            for (int u = 0; u < kB; u += 4) {
                 f32x4 xv[kF32M];
 #pragma unroll
                 for (int m = 0; m < kF32M; ++m) xv[m] = *reinterpret_cast<const f32x4*>(xw + m * kF32XChunk + t0 + u);
@@ -363,20 +366,29 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
                     }
                 }
             }
+            if ((t0 / kB) & 1) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int m = 0; m < kF32M; ++m) {
-                    kahan_add(acc[c][m], cor[c][m], part[c][m]);
-                    part[c][m] = 0.f;
-                }
+                    for (int m = 0; m < kF32M; ++m) {
+                        kahan_add(acc[c][m], cor[c][m], part[c][m]);
+                        part[c][m] = 0.f;
+                    }
+            }
 #pragma unroll
-            for (int u = 0; u < kF32Tile; ++u) {
+            for (int u = 0; u < kB; ++u) {
                 byte[u] = nbyte_[u];
                 sc[u] = nsc[u];
             }
         }
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int m = 0; m < kF32M; ++m) {
+            kahan_add(acc[c][m], cor[c][m], part[c][m]);
+            part[c][m] = 0.f;
+        }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
