@@ -90,8 +90,11 @@ w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t*
  * book    HOST pointer to 16 f32 codebook values (copied at the call).
  * Contract: M >= 0, K > 0, N > 0, block > 0 and even ([P2] recognize).
  * This library implements transpose != 0 with K % 32 == 0, K % block == 0 and
- * block % 8 == 0; other valid shapes return W4_EUNSUPPORTED. M == 0 is a no-op.
- * Accumulation is f32; y is the round-to-nearest-even fp16 of it.
+ * block % 8 == 0 (matrix cores; x 16-byte and packed 4-byte aligned), and
+ * transpose == 0 for any K and N with M up to 262,140 (vector ALU, K tiles
+ * added with compensation); other valid requests return W4_EUNSUPPORTED.
+ * M == 0 is a no-op. Accumulation is f32; y is the round-to-nearest-even fp16
+ * of it.
  * ---------------------------------------------------------------------- */
 w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const uint16_t* scales,
                    const float* book, uint16_t* y, int64_t M, int64_t K, int64_t N,

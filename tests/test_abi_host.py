@@ -64,7 +64,9 @@ def test_affine_contract(args, status, needle):
     ((5, 128, 48, 63, 1), B.W4_EINVAL),          # block must be even
     ((5, 128, 48, 0, 1), B.W4_EINVAL),
     ((5, 0, 48, 64, 1), B.W4_EINVAL),
-    ((5, 128, 48, 64, 0), B.W4_EUNSUPPORTED),    # non-transposed layout
+    ((5, 128, 48, 64, 0), B.W4_OK),              # [K, N] layout (vector-ALU column kernels)
+    ((5, 5, 3, 64, 0), B.W4_OK),                 # [K, N] with blocks across rows
+    ((262141, 32, 32, 2, 0), B.W4_EUNSUPPORTED), # [K, N] past 4 rows x 65535 workgroups
     ((5, 96, 48, 64, 1), B.W4_EUNSUPPORTED),     # K not a multiple of the block
     ((5, 128, 48, 2, 1), B.W4_EUNSUPPORTED),     # block not a multiple of 8
 ])

@@ -186,6 +186,28 @@ def test_qmm_lut4_small(M, K, N, block):
                    float(np.abs(oracle.f16_to_f32(c["scales"])).max()), f"lut M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,block", [
+    (4, 256, 96, 64),      # aligned column form: N a multiple of the block
+    (3, 100, 70, 6),       # blocks straddle rows: element-by-element form
+    (130, 64, 256, 16),    # more than 128 rows of x: 33 row groups of 4
+    (2, 5000, 40, 10),     # K split over 16 wavefronts with a ragged last range
+])
+def test_qmm_lut4_weight_stored_k_by_n(M, K, N, block):
+    # Half-precision path with transpose == 0 (W stored [K, N], flat = k * N + n).
+    rng = np.random.default_rng(M + K)
+    count = N * K
+    packed = rng.integers(0, 256, (count + 1) // 2, dtype=np.uint16).astype(np.uint8)
+    scales = oracle.f32_to_f16(rng.uniform(0.01, 0.05, -(-count // block)).astype(np.float32))
+    x = oracle.f32_to_f16(rng.standard_normal((M, K)).astype(np.float32))
+    book = synth.normal_codebook()
+    y = B.qmm_lut4(_t(x.view(np.int16)).view(torch.float16), _t(packed), _t(scales.view(np.int16)).view(torch.float16),
+                   book, N, block, transpose=0)
+    acc, _ = oracle.lut4(x, packed, scales, book, M, K, N, block, transpose=False, round_half=True)
+    got = y.float().cpu().numpy().astype(np.float64)
+    _assert_within(got, acc, K, float(np.abs(oracle.f16_to_f32(x)).max()),
+                   float(np.abs(oracle.f16_to_f32(scales)).max()), f"lut [K,N] M={M} K={K} N={N} block={block}")
+
+
 def test_qmm_lut4_full_size_sampled():
     c = synth.lut_matmul_case()
     M, K, N, block = c["M"], c["K"], c["N"], c["block"]

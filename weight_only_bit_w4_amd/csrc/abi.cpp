@@ -90,7 +90,14 @@ w4_status w4_check_lut(int64_t M, int64_t K, int64_t N, int32_t block, int32_t t
     if (block <= 0 || block % 2 != 0) return fail(W4_EINVAL, "qmm_lut4: block must be positive and even, got %d", block);
     if (M > INT32_MAX || K > INT32_MAX || N > INT32_MAX || N * K > (int64_t)1 << 40)
         return fail(W4_EINVAL, "qmm_lut4: dimensions too large");
-    if (!transpose) return fail(W4_EUNSUPPORTED, "qmm_lut4: only the transposed weight layout ([N, K]) is implemented");
+    if (!transpose) {
+        // [K, N]: any K, N and even block; rows of x go 4 per workgroup (grid y).
+        if (M > 4ll * 65535)
+            return fail(W4_EUNSUPPORTED, "qmm_lut4: the [K, N] layout is implemented for M up to 262140, got %lld",
+                        (long long)M);
+        clear_error();
+        return W4_OK;
+    }
     if (K % 32 != 0 || K % block != 0 || block % 8 != 0)
         return fail(W4_EUNSUPPORTED, "qmm_lut4: implemented for K %% 32 == 0, K %% block == 0, block %% 8 == 0 "
                                      "(K=%lld block=%d)", (long long)K, block);

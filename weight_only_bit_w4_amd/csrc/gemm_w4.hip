@@ -922,6 +922,13 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
     if (st != W4_OK) return st;
     if (M == 0) return W4_OK;
     if (!x || !packed || !scales || !book || !y) return fail(W4_EINVAL, "qmm_lut4: null pointer argument");
+    if (!transpose) {
+        // Weight stored [K, N]: column kernels in the vector ALU (lut_f32.hip).
+        if (((uintptr_t)x & 1u) || ((uintptr_t)scales & 1u) || ((uintptr_t)y & 1u))
+            return fail(W4_EINVAL, "qmm_lut4: x, scales and y must be 2-byte aligned");
+        launch_lut4_kn_f16(x, packed, scales, book, y, M, K, N, block, as_stream(stream));
+        return launch_status("qmm_lut4");
+    }
     if (!aligned16(x) || ((uintptr_t)packed & 3u)) return fail(W4_EINVAL, "qmm_lut4: x must be 16-byte and packed 4-byte aligned");
     Book16 b;
     for (int i = 0; i < 16; ++i) b.v[i] = book[i];

@@ -37,6 +37,32 @@ struct LutBook {
     float v[16];
 };
 
+// Operand formats: single precision (the f32 path), or binary16 x, scales and
+// y with the decoded weight rounded to binary16 before the products (the
+// half-precision path's [K, N] layout; lut4 page, rounded_weight).
+template <bool H>
+struct LutIO;
+template <>
+struct LutIO<false> {
+    using X = float;
+    using S = float;
+    using Y = float;
+    __device__ __forceinline__ static float x(X v) { return v; }
+    __device__ __forceinline__ static float s(S v) { return v; }
+    __device__ __forceinline__ static float w(float v) { return v; }
+    __device__ __forceinline__ static Y y(float v) { return v; }
+};
+template <>
+struct LutIO<true> {
+    using X = uint16_t;
+    using S = uint16_t;
+    using Y = uint16_t;
+    __device__ __forceinline__ static float x(X v) { return f16_bits_to_f32(v); }
+    __device__ __forceinline__ static float s(S v) { return f16_bits_to_f32(v); }
+    __device__ __forceinline__ static float w(float v) { return (float)(_Float16)v; }
+    __device__ __forceinline__ static Y y(float v) { return f32_to_f16_bits(v); }
+};
+
 // acc += part with the running correction cor (the page's compensated step:
 // a non-finite sum leaves no correction).
 __device__ __forceinline__ void kahan_add(float& acc, float& cor, float part) {
@@ -64,11 +90,13 @@ struct BlockCursor {
     }
 };
 
-__device__ __forceinline__ float lut_weight(const uint8_t* __restrict__ packed, const float* __restrict__ scales,
-                                            const float* book_s, int64_t flat, int64_t scale_index) {
+template <bool H = false>
+__device__ __forceinline__ float lut_weight(const uint8_t* __restrict__ packed,
+                                            const typename LutIO<H>::S* __restrict__ scales, const float* book_s,
+                                            int64_t flat, int64_t scale_index) {
     const uint32_t byte = packed[flat >> 1];
     const uint32_t code = (flat & 1) ? (byte & 15u) : (byte >> 4);
-    return book_s[code] * scales[scale_index];
+    return LutIO<H>::w(book_s[code] * LutIO<H>::s(scales[scale_index]));
 }
 
 __global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows_kernel(const float* __restrict__ x,
@@ -131,11 +159,13 @@ __global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows_kernel(const 
         }
 }
 
-__global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const float* __restrict__ x,
+template <bool H>
+__global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const typename LutIO<H>::X* __restrict__ x,
                                                                             const uint8_t* __restrict__ packed,
-                                                                            const float* __restrict__ scales,
-                                                                            LutBook book, float* __restrict__ y,
+                                                                            const typename LutIO<H>::S* __restrict__ scales,
+                                                                            LutBook book, typename LutIO<H>::Y* __restrict__ y,
                                                                             int M, int K, int N, int block) {
+    using IO = LutIO<H>;
     __shared__ float book_s[16];
     __shared__ float red[kF32ColWaves][kF32M][64];
     if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
@@ -156,10 +186,10 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const 
     const int32_t sr = N % block;
     int it = 0;
     for (int k = kb; k < ke; ++k) {
-        const float w = nv ? lut_weight(packed, scales, book_s, (int64_t)k * N + n, cur.q) : 0.f;
+        const float w = nv ? lut_weight<H>(packed, scales, book_s, (int64_t)k * N + n, cur.q) : 0.f;
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) {
-            const float xv = m0 + m < M ? x[(size_t)(m0 + m) * K + k] : 0.f;  // the same for every lane
+            const float xv = m0 + m < M ? IO::x(x[(size_t)(m0 + m) * K + k]) : 0.f;  // the same for every lane
             part[m] = __builtin_fmaf(xv, w, part[m]);
         }
         cur.advance(sq, sr, block);
@@ -183,7 +213,7 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const 
         for (int m = 0; m < kF32M; ++m) {
             float a = 0.f, c = 0.f;
             for (int v = 0; v < kF32ColWaves; ++v) kahan_add(a, c, red[v][m][lane]);  // K order
-            if (nv && m0 + m < M) y[(size_t)(m0 + m) * N + n] = a;
+            if (nv && m0 + m < M) y[(size_t)(m0 + m) * N + n] = IO::y(a);
         }
     }
 }
@@ -301,11 +331,13 @@ __global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows8_kernel(const
 // its slice of x in LDS (its own region, 256 k at a time, read back as
 // broadcasts) and loads the codes and scales of 16 k before using them.
 constexpr int kF32XChunk = 256;
-__global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const float* __restrict__ x,
+template <bool H>
+__global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const typename LutIO<H>::X* __restrict__ x,
                                                                              const uint8_t* __restrict__ packed,
-                                                                             const float* __restrict__ scales,
-                                                                             LutBook book, float* __restrict__ y,
+                                                                             const typename LutIO<H>::S* __restrict__ scales,
+                                                                             LutBook book, typename LutIO<H>::Y* __restrict__ y,
                                                                              int M, int K, int N, int block) {
+    using IO = LutIO<H>;
     __shared__ float book_s[16];
     __shared__ __attribute__((aligned(16))) float xs[kF32ColWaves][kF32M][kF32XChunk];
     __shared__ float red[kF32ColWaves][2 * kF32M][64];
@@ -332,7 +364,7 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
 #pragma unroll
         for (int m = 0; m < kF32M; ++m)
             for (int t = lane; t < kF32XChunk; t += 64)
-                xw[m * kF32XChunk + t] = (t < len && m0 + m < M) ? x[(size_t)(m0 + m) * K + c0 + t] : 0.f;
+                xw[m * kF32XChunk + t] = (t < len && m0 + m < M) ? IO::x(x[(size_t)(m0 + m) * K + c0 + t]) : 0.f;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wavefront's own LDS writes are done
         // Codes and scales go 8 steps at a time, the next 8 loaded before the
         // current 8 are used; every second batch closes a 16-product tile.
@@ -345,7 +377,7 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
                 const int k = c0 + t0 + u;
                 const bool v = nv && t0 + u < len;
                 bt[u] = v ? packed[(size_t)k * nbyte + (n >> 1)] : 0u;
-                st[u] = v ? scales[(size_t)k * bpr + sidx] : 0.f;
+                st[u] = v ? IO::s(scales[(size_t)k * bpr + sidx]) : 0.f;
             }
         };
         load(0, byte, sc);
@@ -358,7 +390,8 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
                 for (int m = 0; m < kF32M; ++m) xv[m] = *reinterpret_cast<const f32x4*>(xw + m * kF32XChunk + t0 + u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float w0 = book_s[byte[u + e] >> 4] * sc[u + e], w1 = book_s[byte[u + e] & 15u] * sc[u + e];
+                    const float w0 = IO::w(book_s[byte[u + e] >> 4] * sc[u + e]);
+                    const float w1 = IO::w(book_s[byte[u + e] & 15u] * sc[u + e]);
 #pragma unroll
                     for (int m = 0; m < kF32M; ++m) {
                         part[0][m] = __builtin_fmaf(xv[m][e], w0, part[0][m]);
@@ -401,7 +434,7 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
             for (int m = 0; m < kF32M; ++m) {
                 float a = 0.f, e = 0.f;
                 for (int v = 0; v < kF32ColWaves; ++v) kahan_add(a, e, red[v][c * kF32M + m][lane]);  // K order
-                if (nv && m0 + m < M) y[(size_t)(m0 + m) * N + n + c] = a;
+                if (nv && m0 + m < M) y[(size_t)(m0 + m) * N + n + c] = IO::y(a);
             }
     }
 }
@@ -431,12 +464,34 @@ extern "C" w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const f
                                (int)M, (int)K, (int)N, (int)block);
     } else if (N % block == 0) {
         const dim3 grid((unsigned)((N + 127) / 128), my);
-        hipLaunchKernelGGL(lut4_f32_cols2_kernel, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
+        hipLaunchKernelGGL(lut4_f32_cols2_kernel<false>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
                            (int)M, (int)K, (int)N, (int)block);
     } else {
         const dim3 grid((unsigned)((N + 63) / 64), my);
-        hipLaunchKernelGGL(lut4_f32_cols_kernel, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y, (int)M,
-                           (int)K, (int)N, (int)block);
+        hipLaunchKernelGGL(lut4_f32_cols_kernel<false>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
+                           (int)M, (int)K, (int)N, (int)block);
     }
     return launch_status("qmm_lut4_f32");
 }
+
+namespace w4mi {
+
+// The half-precision lookup matmul with the weight stored [K, N] (qmm_lut4,
+// transpose == 0): the column kernels above in binary16.
+void launch_lut4_kn_f16(const uint16_t* x, const uint8_t* packed, const uint16_t* scales, const float* book, uint16_t* y,
+                        int64_t M, int64_t K, int64_t N, int32_t block, hipStream_t s) {
+    LutBook b;
+    for (int i = 0; i < 16; ++i) b.v[i] = book[i];
+    const unsigned my = (unsigned)((M + kF32M - 1) / kF32M);
+    if (N % block == 0) {
+        const dim3 grid((unsigned)((N + 127) / 128), my);
+        hipLaunchKernelGGL(lut4_f32_cols2_kernel<true>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
+                           (int)M, (int)K, (int)N, (int)block);
+    } else {
+        const dim3 grid((unsigned)((N + 63) / 64), my);
+        hipLaunchKernelGGL(lut4_f32_cols_kernel<true>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
+                           (int)M, (int)K, (int)N, (int)block);
+    }
+}
+
+}  // namespace w4mi

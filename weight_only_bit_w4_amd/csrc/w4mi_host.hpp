@@ -38,6 +38,11 @@ constexpr int64_t kAffineBatchMaxK = 8192;
 void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, const uint16_t* x, uint16_t* y,
                  int M, int K, int N, hipStream_t s);
 
+// Half-precision lookup matmul with the weight stored [K, N] (lut_f32.hip),
+// any K, N and even block, M up to 4 * 65535.
+void launch_lut4_kn_f16(const uint16_t* x, const uint8_t* packed, const uint16_t* scales, const float* book, uint16_t* y,
+                        int64_t M, int64_t K, int64_t N, int32_t block, hipStream_t s);
+
 // Largest expert count the grouping kernel keeps in its LDS histogram.
 constexpr uint32_t kMaxExperts = 8192;
 
