@@ -245,6 +245,7 @@ def _max_d(c):
     (2, 64, 64, 100, 2),     # 100 routed rows per expert: two passes of 64
     (8, 200, 320, 40, 3),    # K not a multiple of the 256 window
     (16, 96, 256, 32, 9),    # 32 tokens but 288 routed rows: past the mat-vec id scan
+    (2500, 16, 64, 40, 2),   # more experts than grouping threads: 3 experts per scan segment
     # mat-vec route (at most 32 tokens)
     (4, 40, 128, 3, 2),      # tiny, N not a multiple of the 32-row tile
     (8, 200, 320, 9, 3),     # 10 blocks: a ragged first chunk

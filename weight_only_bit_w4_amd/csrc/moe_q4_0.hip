@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
         return;
     }
     extern __shared__ uint32_t cnt[];  // [n_experts], counts then cursors
-    __shared__ uint32_t part[kGroupThreads];
+    __shared__ uint32_t part[kGroupThreads / 64];
     __shared__ uint32_t bad_s;
     const int tid = threadIdx.x;
     uint32_t* counts = reinterpret_cast<uint32_t*>(scratch + lay.counts);
@@ -62,21 +62,25 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
             atomicAdd(&bad_s, 1u);
     }
     __syncthreads();
-    // Exclusive scan: each thread sums a contiguous segment, then a scan of
-    // the per-thread partial sums.
+    // Exclusive scan: each thread sums a contiguous segment of experts; the
+    // segment sums are scanned within each wavefront (lane shifts, no
+    // barrier), then across the 16 wavefront totals.
     const int seg = (n_experts + kGroupThreads - 1) / kGroupThreads;
     const int e0 = tid * seg, e1 = min(n_experts, e0 + seg);
+    const int lane = tid & 63, wave = tid >> 6;
     uint32_t local = 0u;
     for (int e = e0; e < e1; ++e) local += cnt[e];
-    part[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < kGroupThreads; off <<= 1) {
-        const uint32_t v = tid >= off ? part[tid - off] : 0u;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
     }
-    uint32_t run = part[tid] - local;  // exclusive prefix of this segment
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0u;
+    for (int w = 0; w < wave; ++w) base += part[w];
+    uint32_t run = base + incl - local;  // exclusive prefix of this segment
     for (int e = e0; e < e1; ++e) {
         const uint32_t c = cnt[e];
         counts[e] = c;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
         cnt[e] = run;  // becomes the scatter cursor
         run += c;
     }
-    if (tid == kGroupThreads - 1) offsets[n_experts] = part[kGroupThreads - 1];
+    if (tid == kGroupThreads - 1) offsets[n_experts] = base + incl;
     __syncthreads();
     for (int r = tid; r < n_rows; r += kGroupThreads) {
         const uint32_t e = ids[r];
