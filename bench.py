@@ -7,10 +7,12 @@ copies are rotated (>= 512 MiB in total) so the 256 MB Infinity Cache cannot
 serve them. The same JSON line carries the other kernels of the path, each
 timed over its own back-to-back launches: the prefill GEMM (M=2048,
 K=N=4096, TFLOP/s), the lookup-codebook GEMM (M=512, K=4096, N=11008) and the
+single-precision lookup GEMM at 4 rows of x in both weight layouts, and the
 expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8; and one
 decode token, top-8, on the mat-vec route, plain and with the fused SwiGLU
-activation), each with its roofline fraction,
-plus the CPU oracle timed on a bounded sample.
+activation), each with its roofline fraction, plus the CPU oracle timed on a
+bounded sample. --only small times qmm_affine4 at M = 2..64 on the decode
+weights (not part of the default line).
 
 Launches are captured in HIP graphs (torch.cuda.CUDAGraph over the library's
 own launches on the capture stream) and replayed, so the host-side cost of a
