@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows8_kernel(const
 // its slice of x in LDS (its own region, 256 k at a time, read back as
 // broadcasts) and loads the codes and scales of 16 k before using them.
 constexpr int kF32XChunk = 256;
-template <bool H>
+template <bool H, int C>
 __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const typename LutIO<H>::X* __restrict__ x,
                                                                              const uint8_t* __restrict__ packed,
                                                                              const typename LutIO<H>::S* __restrict__ scales,
@@ -340,20 +340,22 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
     using IO = LutIO<H>;
     __shared__ float book_s[16];
     __shared__ __attribute__((aligned(16))) float xs[kF32ColWaves][kF32M][kF32XChunk];
-    __shared__ float red[kF32ColWaves][2 * kF32M][64];
+    __shared__ float red[kF32ColWaves][C * kF32M][64];
     if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = blockIdx.x * 128 + 2 * lane;  // and n + 1
-    const bool nv = n < N;                      // N is even: both or neither
+    // C = 2: lane l owns columns 2l, 2l + 1 (its own byte); C = 1: column l
+    // (two lanes read each byte).
+    const int n = blockIdx.x * 64 * C + C * lane;
+    const bool nv = n < N;  // with C = 2, N is even: both columns or neither
     const int m0 = blockIdx.y * kF32M;
     const int span = (K + kF32ColWaves - 1) / kF32ColWaves;
     const int kb = min(K, wave * span), ke = min(K, kb + span);
     const int bpr = N / block;
-    float acc[2][kF32M], cor[2][kF32M], part[2][kF32M];
+    float acc[C][kF32M], cor[C][kF32M], part[C][kF32M];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) acc[c][m] = cor[c][m] = part[c][m] = 0.f;
     const int nbyte = N / 2, sidx = nv ? n / block : 0;
@@ -390,18 +392,25 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
                 for (int m = 0; m < kF32M; ++m) xv[m] = *reinterpret_cast<const f32x4*>(xw + m * kF32XChunk + t0 + u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float w0 = IO::w(book_s[byte[u + e] >> 4] * sc[u + e]);
-                    const float w1 = IO::w(book_s[byte[u + e] & 15u] * sc[u + e]);
+                    if constexpr (C == 2) {
+                        const float w0 = IO::w(book_s[byte[u + e] >> 4] * sc[u + e]);
+                        const float w1 = IO::w(book_s[byte[u + e] & 15u] * sc[u + e]);
 #pragma unroll
-                    for (int m = 0; m < kF32M; ++m) {
-                        part[0][m] = __builtin_fmaf(xv[m][e], w0, part[0][m]);
-                        part[1][m] = __builtin_fmaf(xv[m][e], w1, part[1][m]);
+                        for (int m = 0; m < kF32M; ++m) {
+                            part[0][m] = __builtin_fmaf(xv[m][e], w0, part[0][m]);
+                            part[C - 1][m] = __builtin_fmaf(xv[m][e], w1, part[C - 1][m]);
+                        }
+                    } else {
+                        const uint32_t code = (n & 1) ? (byte[u + e] & 15u) : (byte[u + e] >> 4);
+                        const float w0 = IO::w(book_s[code] * sc[u + e]);
+#pragma unroll
+                        for (int m = 0; m < kF32M; ++m) part[0][m] = __builtin_fmaf(xv[m][e], w0, part[0][m]);
                     }
                 }
             }
             if ((t0 / kB) & 1) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < C; ++c)
 #pragma unroll
                     for (int m = 0; m < kF32M; ++m) {
                         kahan_add(acc[c][m], cor[c][m], part[c][m]);
@@ -416,20 +425,20 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
         }
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) {
             kahan_add(acc[c][m], cor[c][m], part[c][m]);
             part[c][m] = 0.f;
         }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) red[wave][c * kF32M + m][lane] = acc[c][m];
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < C; ++c)
 #pragma unroll
             for (int m = 0; m < kF32M; ++m) {
                 float a = 0.f, e = 0.f;
@@ -463,9 +472,9 @@ extern "C" w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const f
             hipLaunchKernelGGL(lut4_f32_rows_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y,
                                (int)M, (int)K, (int)N, (int)block);
     } else if (N % block == 0) {
-        const dim3 grid((unsigned)((N + 127) / 128), my);
-        hipLaunchKernelGGL(lut4_f32_cols2_kernel<false>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
-                           (int)M, (int)K, (int)N, (int)block);
+        const dim3 grid((unsigned)((N + 63) / 64), my);
+        hipLaunchKernelGGL((lut4_f32_cols2_kernel<false, 1>), grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b,
+                           y, (int)M, (int)K, (int)N, (int)block);
     } else {
         const dim3 grid((unsigned)((N + 63) / 64), my);
         hipLaunchKernelGGL(lut4_f32_cols_kernel<false>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
@@ -484,9 +493,9 @@ void launch_lut4_kn_f16(const uint16_t* x, const uint8_t* packed, const uint16_t
     for (int i = 0; i < 16; ++i) b.v[i] = book[i];
     const unsigned my = (unsigned)((M + kF32M - 1) / kF32M);
     if (N % block == 0) {
-        const dim3 grid((unsigned)((N + 127) / 128), my);
-        hipLaunchKernelGGL(lut4_f32_cols2_kernel<true>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
-                           (int)M, (int)K, (int)N, (int)block);
+        const dim3 grid((unsigned)((N + 63) / 64), my);
+        hipLaunchKernelGGL((lut4_f32_cols2_kernel<true, 1>), grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b,
+                           y, (int)M, (int)K, (int)N, (int)block);
     } else {
         const dim3 grid((unsigned)((N + 63) / 64), my);
         hipLaunchKernelGGL(lut4_f32_cols_kernel<true>, grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b, y,
