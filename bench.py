@@ -41,14 +41,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "e39dd6ce9117e166", 36822903 + 28676),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "ac1d231c67af13f0", 100826107 + 16800724),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "ac1d231c67af13f0", 81614018 + 11291200),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 114229054 + 5767168),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 13134050 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "46558843d27d1135", 14099609 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "", 0),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "", 0),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "4fbeb2b607bb7f8e", 36831156 + 57347),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "8a69411c591488f2", 100826117 + 16801303),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "8a69411c591488f2", 81614016 + 11290926),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "ee689bd942a9f5fe", 114160303 + 5767168),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "ee689bd942a9f5fe", 13134047 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "ee689bd942a9f5fe", 14103706 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "601002c8d3e96e21", 26034627 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "601002c8d3e96e21", 113361948 + 176128),
 }
 
 
