@@ -39,7 +39,6 @@ constexpr int kXWaves = 8;    // wavefronts per workgroup of the shared-x form
 constexpr int kXRows = 2;     // output rows per wavefront of the shared-x form
 constexpr int kXChunks = 4;   // the shared-x form covers up to 4 x 64 groups
 constexpr int kXStride = 20;  // LDS dwords per group: 16 pairs, the sum, pad (80 B: conflict-free 16-byte reads)
-constexpr int kCUs = 256;     // compute units of the MI355X
 
 // Lane view of one quantisation group of x: bf16 pairs matching the nibble
 // pairs (i, i + 4) of each of the group's four words, and the group sum.

@@ -8,12 +8,14 @@
 //     htpe / hids); the other workgroups store x as binary16 (the matrix-core
 //     operand type), each 32-wide K block in the order the weight decode
 //     produces it. Stream order makes both visible to launch 2.
-//  2. moe_gemm_kernel: one workgroup per (expert, 128 weight rows) reads that
-//     slice of the expert's weights exactly once per 32 routed rows and
-//     applies it with v_mfma_f32_32x32x16_f16, f32 accumulation. Weights and
-//     the routed rows' x stream through LDS rings by buffer-to-LDS DMA, one
-//     256-wide K window (8 Q4_0 blocks, 144 bytes of each weight row) per
-//     step; each lane decodes two qs dwords per block into fp16 (q - 8) d.
+//  2. moe_gemm_kernel: workgroups split each expert's weight rows into
+//     contiguous ranges of 32-row tiles (enough workgroups to fill the chip);
+//     a range is read exactly once per 32 routed rows and applied with
+//     v_mfma_f32_32x32x16_f16, f32 accumulation, one tile per wavefront.
+//     Weights and the routed rows' x stream through a 5-slot LDS ring by
+//     buffer-to-LDS DMA, one 64-wide K window (2 Q4_0 blocks, 36 bytes of
+//     each weight row) per step; each lane decodes two qs dwords per block
+//     into fp16 (q - 8) d.
 #include <type_traits>
 
 #include "w4mi_device.hpp"
@@ -29,8 +31,9 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
                                                                   IdScratchLayout lay) {
     if (blockIdx.x > 0) {
         // x -> binary16, 8 values per thread per step: output positions
-        // 8c .. 8c + 7 of a 32-wide block hold k = 4c .. 4c + 3 and
-        // 16 + 4c .. 16 + 4c + 3 (the order q4_0_operand yields weights in).
+        // 8c .. 8c + 7 of a 32-wide block hold k = 4c, 4c + 2, 16 + 4c,
+        // 16 + 4c + 2, 4c + 1, 4c + 3, 16 + 4c + 1, 16 + 4c + 3 (the order
+        // q4_0_operand yields weights in).
         uint16_t* xh = reinterpret_cast<uint16_t*>(scratch + lay.xh);
         const int64_t stride = (int64_t)(gridDim.x - 1) * kGroupThreads * 8;
         for (int64_t i = ((int64_t)(blockIdx.x - 1) * kGroupThreads + threadIdx.x) * 8; i < x_count; i += stride) {
@@ -38,8 +41,8 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
             const int c = (int)((i & 31) >> 3);
             const f32x4 a = *reinterpret_cast<const f32x4*>(x + blk + 4 * c);
             const f32x4 b = *reinterpret_cast<const f32x4*>(x + blk + 16 + 4 * c);
-            *reinterpret_cast<u32x4*>(xh + i) = u32x4{pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]),
-                                                      pack_f16x2(b[0], b[1]), pack_f16x2(b[2], b[3])};
+            *reinterpret_cast<u32x4*>(xh + i) = u32x4{pack_f16x2(a[0], a[2]), pack_f16x2(b[0], b[2]),
+                                                      pack_f16x2(a[1], a[3]), pack_f16x2(b[1], b[3])};
         }
         return;
     }
@@ -101,19 +104,25 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
     if (tid == 0) *reinterpret_cast<uint32_t*>(scratch + lay.bad_ids) = bad_s;
 }
 
-constexpr int kMoeWaves = 16;          // 2 halves of 64 weight rows x 8 blocks of a window
+// Grouped GEMM layout. A workgroup of 12 wavefronts takes one expert and a
+// contiguous range of its 32-row weight tiles (the expert's tiles are split
+// over enough workgroups to fill the chip) and streams them in chunks of up
+// to 12 tiles, one tile per wavefront, over K in windows of 64 (two Q4_0
+// blocks, 36 bytes of each weight row). A wavefront owns its tile for the
+// whole of K, so its accumulators hold finished sums and no partial sums
+// cross wavefronts.
+constexpr int kMoeWaves = 12;                         // three to a SIMD: 168 registers each
 constexpr int kMoeThreads = kMoeWaves * 64;
-constexpr int kMoeKSplit = 8;          // wavefronts per 64 weight rows, one block of each window each
-constexpr int kMoeBN = 128;            // weight rows per workgroup: 4 x 32
-constexpr int kMoeMR = 32;             // routed rows per pass (one 32x32 MFMA tile)
-constexpr int kMoeWinBlocks = 8;       // Q4_0 blocks per K window
-constexpr int kMoeWRow = kMoeWinBlocks * 18;            // 144 bytes of a weight row per window
-constexpr int kMoeWSlot = kMoeBN * kMoeWRow;            // 18 KB
-constexpr int kMoeWDma = kMoeWSlot / 1024;              // 18 DMA instructions per W window
-constexpr int kMoeXRow = kMoeWinBlocks * 32 * 2;        // 512 bytes of a routed row's x per window
-constexpr int kMoeXSlot = kMoeMR * kMoeXRow;            // 16 KB
-constexpr int kMoeXDma = kMoeXSlot / 1024;              // 16 DMA instructions per x window
-constexpr int kMoeWStages = 4, kMoeXStages = 3;
+constexpr int kMoeTile = 32;                          // weight rows per wavefront (one 32x32 MFMA tile)
+constexpr int kMoeMR = 32;                            // routed rows per pass
+constexpr int kMoeChunkRows = kMoeTile * kMoeWaves;   // 384
+constexpr int kMoeWinBytes = 36;                      // two blocks of a weight row per window
+constexpr int kMoeSpan = 48;                          // ... moved as three 16-byte pieces (12 bytes read ahead)
+constexpr int kMoeWSlot = kMoeChunkRows * kMoeSpan;   // 18 KB
+constexpr int kMoeXRow = 128;                         // 64 binary16 of a routed row per window
+constexpr int kMoeXSlot = kMoeMR * kMoeXRow;          // 4 KB
+constexpr int kMoeXDma = kMoeXSlot / 1024;            // 4 DMA instructions per x window
+constexpr int kMoeStages = 4;                         // ring depth: windows j + 1 .. j + 3 in flight at window j
 constexpr uint32_t kMoeOob = 0x80000000u;
 
 __device__ __forceinline__ uint32_t moe_lds_addr(const void* p) {
@@ -133,249 +142,311 @@ __device__ __forceinline__ void moe_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ __forceinline__ void moe_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// A scalar-cache load of one dword at a wave-uniform address. It is counted by
-// lgkmcnt, so waiting for it does not wait for the DMA in flight.
-// The address is passed through readfirstlane so that it is in scalar
-// registers even where the compiler cannot prove it uniform.
-__device__ __forceinline__ uint32_t moe_sload(const uint32_t* p) {
+// Eight dwords at a wave-uniform address by one scalar-cache load (counted
+// by lgkmcnt, so waiting for it does not wait for the DMA in flight). The
+// address goes through readfirstlane so that it is in scalar registers even
+// where the compiler cannot prove it uniform.
+__device__ __forceinline__ void moe_sload8(const uint32_t* p, uint32_t (&v)[8]) {
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
     const uint64_t a = (uint64_t)(uintptr_t)p;
     // readfirstlane returns int: widen through uint32_t, or the low word would sign-extend.
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
-    uint32_t v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa) : "memory");
-    return v;
+    u32x8 r;
+    asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(sa) : "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = r[i];
 }
-
-// One lane's B operand for one Q4_0 block: qs dword c (elements 4c .. 4c + 3
-// in the low nibbles, 16 + 4c .. 16 + 4c + 3 in the high ones) as fp16
-// (q - 8) d, in the order (4c, 4c+1) (4c+2, 4c+3) (16+4c, 16+4c+1)
-// (16+4c+2, 16+4c+3). Low nibbles become binary16 1024 + q and high ones
-// 64 + q (the nibble in mantissa bits 4..7 under exponent 2^6); subtracting
-// 1032 or 72 is exact and leaves q - 8, and the product with d rounds once.
+// One lane's B operand for one Q4_0 block: qs dword c as fp16 (q - 8) d in
+// the pair order of q4_0_dot_pairs, (4c, 4c+2) (16+4c, 16+4c+2) (4c+1, 4c+3)
+// (16+4c+1, 16+4c+3): low nibbles arrive as binary16 1024 + q and high ones
+// as 64 + q; subtracting 1032 or 72 is exact and leaves q - 8, and the
+// product with d rounds once.
 struct Q4Consts {
     uint32_t m_lo, m_hi, magic_lo, magic_hi;  // held in VGPRs so each mask-and-insert is one v_and_or_b32
 };
 __device__ __forceinline__ u32x4 q4_0_operand(uint32_t qs, f16x2 dd, const Q4Consts& k) {
-    const uint32_t t0 = __builtin_amdgcn_perm(0u, qs, 0x0C010C00u);  // [b0, 0, b1, 0]
-    const uint32_t t1 = __builtin_amdgcn_perm(0u, qs, 0x0C030C02u);  // [b2, 0, b3, 0]
+    uint32_t p[4];
+    q4_0_dot_pairs(qs, k.m_lo, k.m_hi, k.magic_lo, k.magic_hi, p);
     const f16x2 lo_bias = as_f16x2(0xE408E408u), hi_bias = as_f16x2(0xD480D480u);  // -1032, -72
     u32x4 o;
-    o[0] = as_u32((as_f16x2(and_or_u32(t0, k.m_lo, k.magic_lo)) + lo_bias) * dd);
-    o[1] = as_u32((as_f16x2(and_or_u32(t1, k.m_lo, k.magic_lo)) + lo_bias) * dd);
-    o[2] = as_u32((as_f16x2(and_or_u32(t0, k.m_hi, k.magic_hi)) + hi_bias) * dd);
-    o[3] = as_u32((as_f16x2(and_or_u32(t1, k.m_hi, k.magic_hi)) + hi_bias) * dd);
+    o[0] = as_u32((as_f16x2(p[0]) + lo_bias) * dd);
+    o[1] = as_u32((as_f16x2(p[1]) + hi_bias) * dd);
+    o[2] = as_u32((as_f16x2(p[2]) + lo_bias) * dd);
+    o[3] = as_u32((as_f16x2(p[3]) + hi_bias) * dd);
     return o;
 }
 
-// Block b of one K window (ODD = b % 2) for a wavefront's 64 weight rows
-// (two 32-row tiles) against the 32 routed rows. Lane (n, h) = (lane % 32,
-// lane / 32) feeds MFMA k-step s with qs dword 2 s + h of row n of each tile;
-// the x operand of lane (m, h) is the same eight elements of routed row m,
-// which the xh order stores as 16 contiguous bytes (chunk 4 b + 2 s + h of
-// the window row, kept at slot chunk ^ (m % 32)); one x read serves both
-// tiles. A block past the row's end (a partial last window) gets d = 0, which
-// zeroes its weights whatever the ring holds there.
-template <int ODD>
-__device__ __forceinline__ void moe_block(const uint8_t* wrows, const uint8_t* xs, int lane, int b, bool live,
-                                          const Q4Consts& k, f32x16 (&acc)[2]) {
-    const int h = lane >> 5, m = lane & 31;
-    const uint8_t* xr = xs + m * kMoeXRow;
-    uint32_t dd[2];
+// One 64-wide K window for a wavefront's 32 weight rows against the pass's
+// 32 routed rows: two blocks b, two MFMA k-steps s each. Lane (n, h) =
+// (lane % 32, lane / 32) feeds step s of block b with qs dword 2 s + h of
+// weight row n; the x operand of lane (m, h) is the same eight elements of
+// routed row m, which the xh order stores as the 16-byte chunk 4 b + 2 s + h
+// of the window row (kept at slot chunk ^ ((m / 2) % 8), which keeps the
+// 32-row reads conflict-free). The window's LDS reads (moe_read) are issued a
+// window ahead of its arithmetic (moe_apply), so they overlap the previous
+// window's decode and matrix work instead of following each barrier.
+struct MoeOps {
+    u32x4 x[2][2];      // x operands [block][step]
+    uint32_t d0, d1;    // block scales (binary16)
+    uint32_t w[4];      // block 0: the four dwords that cover the lane's two qs dwords
+    uint32_t q1[2];     // block 1: the lane's two qs dwords
+};
+// A lane's LDS read addresses in slot 0 of the rings (slot s adds s slot
+// sizes, folded into the instructions' offsets).
+struct MoeLane {
+    const uint8_t* w;        // the lane's weight row: d of block 0 at +0, of block 1 at +18
+    const uint8_t* wq;       // + 4 h: block 0's covering dwords at +0..+12, block 1's qs at +20, +28
+    const uint8_t* x[2][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
+};
+__device__ __forceinline__ MoeLane moe_lane(const uint8_t* wring, const uint8_t* xring, int nl, int lane) {
+    const int h = lane >> 5, m = lane & 31, sw = (m >> 1) & 7;
+    MoeLane l;
+    l.w = wring + nl * kMoeSpan;
+    l.wq = l.w + 4 * h;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint32_t draw = *reinterpret_cast<const uint16_t*>(wrows + t * 32 * kMoeWRow + 18 * b);
-        dd[t] = (live ? draw : 0u) * 0x10001u;
-    }
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const u32x4 xop = *reinterpret_cast<const u32x4*>(xr + 16 * ((4 * b + 2 * s + h) ^ m));
+        for (int s = 0; s < 2; ++s) l.x[b][s] = xring + m * kMoeXRow + 16 * ((4 * b + 2 * s + h) ^ sw);
+    return l;
+}
+template <int SLOT>
+__device__ __forceinline__ MoeOps moe_read(const MoeLane& l) {
+    MoeOps o;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint8_t* blk = wrows + t * 32 * kMoeWRow + 18 * b;
-            // qs dword 2 s + h: 4-byte aligned for odd b, else two bytes past
-            // an aligned dword.
-            uint32_t qs;
-            if (ODD) {
-                qs = *reinterpret_cast<const uint32_t*>(blk + 2 + 8 * s + 4 * h);
-            } else {
-                const uint32_t lo = *reinterpret_cast<const uint32_t*>(blk + 8 * s + 4 * h);
-                const uint32_t hi = *reinterpret_cast<const uint32_t*>(blk + 8 * s + 4 * h + 4);
-                qs = __builtin_amdgcn_alignbyte(hi, lo, 2);
-            }
-            const u32x4 wop = q4_0_operand(qs, as_f16x2(dd[t]), k);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, xop), __builtin_bit_cast(f16x8, wop),
-                                                            acc[t], 0, 0, 0);
-        }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) o.x[b][s] = *reinterpret_cast<const u32x4*>(l.x[b][s] + SLOT * kMoeXSlot);
+    // Block 0 at byte 0 of the row's window (d, then qs two bytes past a
+    // dword boundary), block 1 at byte 18 (qs dword-aligned).
+    const uint8_t* w = l.w + SLOT * kMoeWSlot;
+    const uint8_t* wq = l.wq + SLOT * kMoeWSlot;
+    o.d0 = *reinterpret_cast<const uint16_t*>(w);
+    o.d1 = *reinterpret_cast<const uint16_t*>(w + 18);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.w[i] = reinterpret_cast<const uint32_t*>(wq)[i];
+    o.q1[0] = *reinterpret_cast<const uint32_t*>(wq + 20);
+    o.q1[1] = *reinterpret_cast<const uint32_t*>(wq + 28);
+    return o;
+}
+__device__ __forceinline__ void moe_apply(const MoeOps& o, const Q4Consts& k, f32x16& acc) {
+    uint32_t qs[2][2];
+    qs[0][0] = __builtin_amdgcn_alignbyte(o.w[1], o.w[0], 2);
+    qs[0][1] = __builtin_amdgcn_alignbyte(o.w[3], o.w[2], 2);
+    qs[1][0] = o.q1[0];
+    qs[1][1] = o.q1[1];
+    const f16x2 dd[2] = {as_f16x2(o.d0 * 0x10001u), as_f16x2(o.d1 * 0x10001u)};
+    u32x4 wop[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) wop[b][s] = q4_0_operand(qs[b][s], dd[b], k);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.x[b][s]),
+                                                         __builtin_bit_cast(f16x8, wop[b][s]), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void moe_wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS: kMoeStages slots of W [384 rows x 48 B] (row r's window bytes, as
+// stored, at 48 r) and of x [32 rows x 128 B] (routed row m's chunk c at
+// slot c ^ ((m / 2) % 8)), then the pass's 32 output row indices.
+// DMA roles: x instruction i (rows 8 i .. 8 i + 7) is issued by wavefront i,
+// W instruction i (16-byte pieces 64 i .. 64 i + 63 of the slot: row q / 3,
+// piece q % 3) by wavefront (i + 4) % 12, so no wavefront issues more than
+// two per window. Window j + 4 is issued after barrier j into the slot of
+// window j - 1, which every wavefront finished reading before barrier j; each
+// wavefront waits for its own DMA of window j before barrier j, after which
+// every wavefront may read it. All DMA offsets are per-lane (no scalar
+// offset), so the descriptors' range checks cover every byte read: the 12
+// bytes read past a row's last window are the next row's (unused) or, past the
+// chunk's last row, zeros.
+constexpr int kMoeLds = kMoeStages * (kMoeWSlot + kMoeXSlot) + kMoeMR * 4;
+
+template <int N>
+__device__ __forceinline__ void moe_wait_window(int per_window) {
+    // windows j + 1 .. j + N may still be in flight
+    switch (per_window) {
+        case 0: moe_wait_vmcnt<0>(); break;
+        case 1: moe_wait_vmcnt<N>(); break;
+        case 2: moe_wait_vmcnt<2 * N>(); break;
+        default: moe_wait_vmcnt<3 * N>(); break;
     }
 }
 
-// LDS (one array, so that the end-of-pass exchange can use all of it):
-//   W  kMoeWStages x [128 rows x 144 B]: the window's 8 blocks of each row,
-//      as stored (d then qs, 18 bytes a block);
-//   x  kMoeXStages x [32 rows x 512 B]: routed row r's 16-byte chunk p
-//      (xh order) at chunk slot p ^ (r % 32), which keeps the A-operand
-//      reads of 32 rows conflict-free.
-// Each of the 16 wavefronts issues its share of every window's DMA (W
-// kMoeWStages - 1 windows ahead, x kMoeXStages - 1 ahead) and waits for its
-// own DMA of window j before barrier j, after which every wavefront may read
-// window j and the slots of window j - 1 are free. Wavefront w takes weight
-// rows 64 (w % 2) .. + 63 and block w / 2 of each window (so each wavefront
-// runs at least 4 to a SIMD, as the decode's vector-ALU work needs); the eight
-// partial sums of a row half meet in LDS at the end of a pass.
-constexpr int kMoeLds = kMoeWStages * kMoeWSlot + kMoeXStages * kMoeXSlot;
-
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ scratch,
                                                                float* __restrict__ out, int N, int K, int top_k,
-                                                               uint64_t expert_stride, IdScratchLayout lay, int n_tokens) {
+                                                               uint64_t expert_stride, IdScratchLayout lay, int n_tokens,
+                                                               int splits) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kMoeLds];
     uint8_t* const wring = lds;
-    uint8_t* const xring = lds + kMoeWStages * kMoeWSlot;
-    const int tiles_n = (N + kMoeBN - 1) / kMoeBN;
-    const int e = blockIdx.x / tiles_n;
-    const int n0 = (blockIdx.x % tiles_n) * kMoeBN;
+    uint8_t* const xring = lds + kMoeStages * kMoeWSlot;
+    uint32_t* const pass_rows = reinterpret_cast<uint32_t*>(xring + kMoeStages * kMoeXSlot);
+    const int e = blockIdx.x / splits, part = blockIdx.x % splits;
+    const int tiles = (N + kMoeTile - 1) / kMoeTile;
+    const int t_begin = (int)((int64_t)part * tiles / splits), t_end = (int)((int64_t)(part + 1) * tiles / splits);
     const uint32_t cnt = reinterpret_cast<const uint32_t*>(scratch + lay.counts)[e];
-    if (cnt == 0u) return;
+    if (cnt == 0u || t_begin >= t_end) return;
     const uint32_t* rows =
         reinterpret_cast<const uint32_t*>(scratch + lay.rows) + reinterpret_cast<const uint32_t*>(scratch + lay.offsets)[e];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nb = K / 32;
-    const int nwin = (nb + kMoeWinBlocks - 1) / kMoeWinBlocks;
-    const uint32_t row_bytes = (uint32_t)nb * 18u;
-    const int nrows = min(kMoeBN, N - n0);
-    const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(w + (size_t)e * expert_stride + (size_t)n0 * row_bytes, (uint32_t)nrows * row_bytes);
+    const int nwin = K / 64;
+    const uint32_t row_bytes = (uint32_t)(K / 32) * 18u;
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(scratch + lay.xh, (uint32_t)((size_t)n_tokens * (size_t)K * 2u));
     const Q4Consts k{vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u), vreg(0x54005400u)};
-    float* const red = reinterpret_cast<float*>(lds);  // pass-end exchange
-    static_assert((kMoeKSplit - 1) * 2 * 2 * 16 * 64 * 4 <= kMoeLds, "exchange area fits the rings");
-
-    // DMA plan: W instruction i (lane l covers 16-byte chunk q = 64 i + l of
-    // the window: row q / 9, chunk q % 9) goes to wavefront i % 16, x
-    // instruction i (routed rows 2 i, 2 i + 1) to wavefront i.
-    static_assert(kMoeXDma == kMoeWaves, "one x DMA instruction per wavefront");
-    constexpr int kWPer = (kMoeWDma + kMoeWaves - 1) / kMoeWaves;
-    const int nw_dma = wave < kMoeWDma % kMoeWaves ? kWPer : kMoeWDma / kMoeWaves;
-    uint32_t wo[kWPer];
-#pragma unroll
-    for (int t = 0; t < kWPer; ++t) {
-        const int q = 64 * (wave + kMoeWaves * t) + lane, r = q / 9, j = q % 9;
-        wo[t] = r < nrows ? (uint32_t)r * row_bytes + 16u * (uint32_t)j : kMoeOob;
-    }
-    const int rh = wave & 1, b = wave >> 1;
-    const int nl = 64 * rh + (lane & 31);  // this lane's weight row in tile 0 (tile 1: + 32)
+    const bool x_dma = wave < kMoeXDma;
+    const int wi0 = (wave + kMoeWaves - kMoeXDma) % kMoeWaves;  // this wavefront's W instructions: wi0, wi0 + 16
+    uint32_t xo = kMoeOob;  // x DMA lane offset of the pass's routed row (set per pass)
 
     for (uint32_t m0 = 0; m0 < cnt; m0 += kMoeMR) {
-        // Routed rows past cnt are not loaded: their (stale) x only feeds
-        // output rows that are never stored.
-        const bool x_rows = m0 + 2u * (uint32_t)wave < cnt;
-        // Iteration j issues W(j + 3) and x(j + 2); the prologue runs the
-        // issues of iterations -3 .. -1 (x(-1) is all zeros, so every
-        // iteration of a wavefront issues the same count).
-        auto issue_w = [&](int j) {
-            const int win = j + kMoeWStages - 1;
-            const bool live = win < nwin;
-            uint8_t* slot = wring + (win % kMoeWStages) * kMoeWSlot;
-            const int soff = __builtin_amdgcn_readfirstlane(live ? win * kMoeWRow : 0);
-#pragma unroll
-            for (int t = 0; t < kWPer; ++t)
-                if (t < nw_dma) moe_dma16(wsrc, slot + 1024 * (wave + kMoeWaves * t), live ? wo[t] : kMoeOob, soff);
-        };
-        // W(0), W(1) need no row ids, so they go out first.
-        issue_w(-3);
-        issue_w(-2);
-        // This wavefront's x rows 2 wave, 2 wave + 1: their ids come by scalar
-        // loads, which do not wait behind the DMA in flight.
-        uint32_t xo;
-        {
-            const uint32_t r0 = __builtin_amdgcn_readfirstlane(min(m0 + 2u * (uint32_t)wave, cnt - 1u));
-            const uint32_t r1 = __builtin_amdgcn_readfirstlane(min(r0 + 1u, cnt - 1u));
-            const uint32_t id0 = moe_sload(rows + r0), id1 = moe_sload(rows + r1);
-            const uint32_t rid = (lane >> 5) ? id1 : id0;
-            const uint32_t r = m0 + 2 * wave + (lane >> 5);
-            const int p = (lane & 31) ^ (2 * wave + (lane >> 5));
-            xo = r < cnt ? (rid / (uint32_t)top_k) * (uint32_t)K * 2u + 16u * (uint32_t)p : kMoeOob;
-        }
-        auto issue_x = [&](int j) {
-            if (x_rows) {
-                const int win = j + kMoeXStages - 1;
-                const bool live = win >= 0 && win < nwin;
-                uint8_t* slot = xring + ((win + kMoeXStages) % kMoeXStages) * kMoeXSlot;
-                const int soff = __builtin_amdgcn_readfirstlane(live ? win * kMoeXRow : 0);
-                moe_dma16(xsrc, slot + 1024 * wave, live ? xo : kMoeOob, soff);
-            }
-        };
-        auto issue = [&](int j) {
-            issue_w(j);
-            issue_x(j);
-        };
-        static_assert(kMoeWStages - 1 == 3 && kMoeXStages - 1 == 2, "prologue below assumes 3 and 2 windows ahead");
-        // Order W(0) W(1) x(-1) x(0) W(2) x(1): at window 0 only the last
-        // iteration's issue (W(2), x(1)) may still be in flight.
-        issue_x(-3);
-        issue_x(-2);
-        issue(-1);
-        f32x16 acc[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
-        // The window loop is specialised on the block parity once per pass
-        // (a branch per window would make the compiler copy the accumulators).
-        auto windows = [&](auto odd) {
-            for (int win = 0; win < nwin; ++win) {
-                // Everything but the last iteration's issue has landed: W(win), x(win).
-                if (nw_dma == kWPer) {
-                    if (x_rows)
-                        moe_wait_vmcnt<kWPer + 1>();
-                    else
-                        moe_wait_vmcnt<kWPer>();
-                } else {
-                    if (x_rows)
-                        moe_wait_vmcnt<kMoeWDma / kMoeWaves + 1>();
-                    else
-                        moe_wait_vmcnt<kMoeWDma / kMoeWaves>();
-                }
-                moe_barrier();
-                moe_block<decltype(odd)::value>(wring + (win % kMoeWStages) * kMoeWSlot + nl * kMoeWRow,
-                                                xring + (win % kMoeXStages) * kMoeXSlot, lane, b,
-                                                b < nb - kMoeWinBlocks * win, k, acc);
-                // After the window's matrix work, so that the 16 wavefronts' DMA
-                // issues (which queue behind one another in the memory pipe) do
-                // not all stall the compute at the start of the window.
-                issue(win);
-            }
-        };
-        if (b & 1)
-            windows(std::integral_constant<int, 1>{});
-        else
-            windows(std::integral_constant<int, 0>{});
-        moe_wait_vmcnt<0>();  // the trailing (all-zero) DMA has landed
-        moe_barrier();        // every wavefront is done with the rings
-        // Blocks 1 .. 7 hand their sums to block 0.
-        if (b) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) red[((((b - 1) * 2 + rh) * 2 + t) * 16 + i) * 64 + lane] = acc[t][i];
-        }
-        moe_barrier();
-        if (!b) {
-            // Lane (n, h) of tile t holds routed rows 8 (i / 4) + 4 h + i % 4 of weight row n.
+        const uint32_t mcnt = min((uint32_t)kMoeMR, cnt - m0);
+        moe_barrier();  // the previous pass's stores have read pass_rows
+        for (int tc = t_begin; tc < t_end; tc += kMoeWaves) {
+            const int n0 = tc * kMoeTile;
+            const int crow = min(min(t_end - tc, kMoeWaves) * kMoeTile, N - n0);
+            const __amdgpu_buffer_rsrc_t wsrc =
+                make_rsrc(w + (size_t)e * expert_stride + (size_t)n0 * row_bytes, (uint32_t)crow * row_bytes);
+            const int n_wi = (crow * 3 + 63) / 64;  // W DMA instructions per window
+            const int nw = (wi0 < n_wi ? 1 : 0) + (wi0 + kMoeWaves < n_wi ? 1 : 0);
+            uint32_t wo[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int ncol = n0 + nl + 32 * t;
+                const int q = 64 * (wi0 + kMoeWaves * t) + lane, r = q / 3, j = q % 3;
+                wo[t] = r < crow ? (uint32_t)r * row_bytes + 16u * (uint32_t)j : kMoeOob;
+            }
+            // DMA of window win into ring slot SLOT (= win % kMoeStages).
+            auto issue_w = [&](auto slot_c, int win) {
+                constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t idx = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    float v = acc[t][i];
+                for (int t = 0; t < 2; ++t)
+                    if (t < nw)
+                        moe_dma16(wsrc, wring + slot * kMoeWSlot + 1024 * (wi0 + kMoeWaves * t),
+                                  wo[t] + (uint32_t)(kMoeWinBytes * win), 0);
+            };
+            auto issue_x = [&](auto slot_c, int win) {
+                constexpr int slot = decltype(slot_c)::value;
+                if (x_dma) moe_dma16(xsrc, xring + slot * kMoeXSlot + 1024 * wave, xo + (uint32_t)(kMoeXRow * win), 0);
+            };
+            using S0 = std::integral_constant<int, 0>;
+            using S1 = std::integral_constant<int, 1>;
+            using S2 = std::integral_constant<int, 2>;
+            using S3 = std::integral_constant<int, 3>;
+            static_assert(kMoeStages == 4, "the slot sequence below is written for four slots");
+            // Prologue, windows 0 .. 2: the weights need no routing ids, so
+            // W(0) and W(1) go out before the ids are read; then x(0), x(1),
+            // W(2), x(2).
+            const bool full = nwin >= kMoeStages - 1;
+            issue_w(S0{}, 0);
+            if (nwin > 1) issue_w(S1{}, 1);
+            if (tc == t_begin) {
+                // This pass's routed rows: x DMA wavefront i (rows 8 i .. 8 i + 7)
+                // reads its eight ids by one scalar load (not counted by vmcnt,
+                // so it does not wait behind the DMA) and records them for the
+                // stores. Ids past the pass's count are not used.
+                if (x_dma) {
+                    const uint32_t* ids8 = rows + m0 + 8 * wave;
+                    uint32_t id[8];
+                    moe_sload8(ids8, id);
+                    const int r = lane >> 3;
+                    uint32_t rid = id[0];
 #pragma unroll
-                    for (int q = 0; q < kMoeKSplit - 1; ++q) v += red[(((q * 2 + rh) * 2 + t) * 16 + i) * 64 + lane];
-                    if (idx < cnt && ncol < N) out[(size_t)rows[idx] * N + ncol] = v;
+                    for (int i = 1; i < 8; ++i) rid = r == i ? id[i] : rid;
+                    const int m = 8 * wave + r;
+                    const int c = (lane & 7) ^ ((m >> 1) & 7);
+                    xo = (uint32_t)m < mcnt ? (rid / (uint32_t)top_k) * (uint32_t)K * 2u + 16u * (uint32_t)c : kMoeOob;
+                    uint32_t own = id[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) own = lane == i ? id[i] : own;
+                    if (lane < 8) pass_rows[8 * wave + lane] = own;
                 }
             }
+            issue_x(S0{}, 0);
+            if (nwin > 1) issue_x(S1{}, 1);
+            if (full) {
+                issue_w(S2{}, 2);
+                issue_x(S2{}, 2);
+            }
+            const int per_window = nw + (x_dma ? 1 : 0);
+            f32x16 acc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+            const bool busy = kMoeTile * wave < crow;
+            const int nl = kMoeTile * wave + (lane & 31);  // this lane's weight row in the chunk
+            const MoeLane ln = moe_lane(wring, xring, nl, lane);
+            // Two operand sets alternate (the loop is unrolled by four, the ring
+            // depth, so that neither set is copied and every slot offset is a
+            // constant): after barrier j a wavefront reads window j into one
+            // set, then decodes and multiplies window j - 1 from the other.
+            MoeOps ops[2];
+            // Window 0: W(0), W(1), x(0) have landed once at most x(1), W(2),
+            // x(2) (this wavefront's share) are in flight.
+            if (!full) {
+                moe_wait_vmcnt<0>();
+            } else if (x_dma) {
+                if (nw == 0) moe_wait_vmcnt<2>(); else if (nw == 1) moe_wait_vmcnt<3>(); else moe_wait_vmcnt<4>();
+            } else {
+                if (nw == 0) moe_wait_vmcnt<0>(); else if (nw == 1) moe_wait_vmcnt<2>(); else moe_wait_vmcnt<4>();
+            }
+            moe_barrier();
+            if (busy) ops[0] = moe_read<0>(ln);
+            if (kMoeStages - 1 < nwin) {
+                issue_w(S3{}, kMoeStages - 1);
+                issue_x(S3{}, kMoeStages - 1);
+            }
+            auto step = [&](auto slot_c, int j, MoeOps& into, const MoeOps& from) {
+                constexpr int slot = decltype(slot_c)::value;
+                // Windows j + 1 .. j + kMoeStages - 2 may still be in flight
+                // (from window 1 on, each window's W then x went out in window
+                // order).
+                if (j + kMoeStages - 2 < nwin)
+                    moe_wait_window<kMoeStages - 2>(per_window);
+                else
+                    moe_wait_vmcnt<0>();
+                moe_wait_lgkm();  // this wavefront's reads of window j - 1 are done: its slot is reused below
+                moe_barrier();
+                if (busy) {
+                    into = moe_read<slot>(ln);
+                    __builtin_amdgcn_sched_barrier(0);  // the reads go out before the arithmetic below
+                    moe_apply(from, k, acc);
+                }
+                if (j + kMoeStages - 1 < nwin) {
+                    using Next = std::integral_constant<int, (slot + kMoeStages - 1) % kMoeStages>;
+                    issue_w(Next{}, j + kMoeStages - 1);
+                    issue_x(Next{}, j + kMoeStages - 1);
+                }
+            };
+            int j = 1;  // j % 4 == 1 at the top of each round
+            for (; j + 3 < nwin; j += 4) {
+                step(S1{}, j, ops[1], ops[0]);
+                step(S2{}, j + 1, ops[0], ops[1]);
+                step(S3{}, j + 2, ops[1], ops[0]);
+                step(S0{}, j + 3, ops[0], ops[1]);
+            }
+            if (j < nwin) step(S1{}, j, ops[1], ops[0]);
+            if (j + 1 < nwin) step(S2{}, j + 1, ops[0], ops[1]);
+            if (j + 2 < nwin) step(S3{}, j + 2, ops[1], ops[0]);
+            const bool last_in_1 = (nwin - 1) & 1;  // the last window's set
+            if (busy) {
+                if (last_in_1)
+                    moe_apply(ops[1], k, acc);
+                else
+                    moe_apply(ops[0], k, acc);
+                // Lane (n, h) holds routed rows 8 (i / 4) + 4 h + i % 4 of weight row n.
+                const int ncol = n0 + nl;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t mm = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    if (mm < mcnt && ncol < N) out[(size_t)pass_rows[mm] * N + ncol] = acc[i];
+                }
+            }
+            moe_wait_vmcnt<0>();  // stores done: the next chunk's DMA waits count only DMA
+            moe_wait_lgkm();
+            moe_barrier();        // every wavefront is done with the ring before the next chunk's DMA
         }
-        moe_barrier();  // the exchange area is free again
     }
 }
 
@@ -692,9 +763,10 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
                     "qmm_id_q4_0: above 32 tokens, implemented for K %% 64 == 0 (whole 36-byte block pairs), got %u", p->k);
     if (((uintptr_t)w & 3u) || (p->expert_stride & 3u))
         return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: above 32 tokens, implemented for 4-byte-aligned w and expert_stride");
-    // Buffer descriptors cover the binary16 x copy and one 128-row weight slice in 32 bits.
-    if ((uint64_t)p->n_tokens * p->k * 2u >= (1ull << 32) || 128ull * (p->k / 32) * 18u >= (1ull << 32))
-        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for n_tokens * K * 2 < 2^32 bytes");
+    // Buffer descriptors cover the binary16 x copy and one 384-row weight chunk
+    // in 32 bits, with in-range offsets below the out-of-range marker 2^31.
+    if ((uint64_t)p->n_tokens * p->k * 2u >= (1ull << 32) || (uint64_t)kMoeChunkRows * (p->k / 32) * 18u >= (1ull << 31))
+        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for n_tokens * K * 2 < 2^32 bytes and 384-row weight chunks below 2^31 bytes");
     const int n_rows = (int)(p->n_tokens * p->top_k);
     const int64_t x_count = (int64_t)p->n_tokens * p->k;
     const int conv_blocks = (int)std::min<int64_t>(1024, (x_count / 8 + kGroupThreads - 1) / kGroupThreads);
@@ -702,10 +774,12 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
                        ids, x, (uint8_t*)scratch, out, n_rows, (int)p->n_experts, (int)p->n, x_count, lay);
     st = launch_status("qmm_id_q4_0 (group)");
     if (st != W4_OK) return st;
-    const int tiles_n = (int)((p->n + kMoeBN - 1) / kMoeBN);
-    hipLaunchKernelGGL(moe_gemm_kernel, dim3((unsigned)(p->n_experts * tiles_n)), dim3(kMoeThreads), 0, s, w,
-                       (const uint8_t*)scratch, out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay,
-                       (int)p->n_tokens);
+    // Each expert's 32-row tiles are split over enough workgroups that the
+    // experts together fill the CUs once (one workgroup per CU fits).
+    const uint32_t tiles = (p->n + kMoeTile - 1) / kMoeTile;
+    const uint32_t splits = std::max(1u, std::min(tiles, ((uint32_t)kCUs + p->n_experts - 1) / p->n_experts));
+    hipLaunchKernelGGL(moe_gemm_kernel, dim3(p->n_experts * splits), dim3(kMoeThreads), 0, s, w, (const uint8_t*)scratch,
+                       out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay, (int)p->n_tokens, (int)splits);
     return launch_status("qmm_id_q4_0 (grouped GEMM)");
 }
 

@@ -50,21 +50,24 @@ __global__ void unpack_q4_0_kernel(const uint8_t* __restrict__ w, uint8_t* __res
     uint8_t* qo = q + row * K + pr * 64;
     d[i * 2] = (uint16_t)dA;
     d[i * 2 + 1] = (uint16_t)dB;
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, m_lo = 0x64006400u, m_hi = 0x54005400u;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int dw = 0; dw < 4; ++dw) {
+            // the grouped GEMM's and the mat-vec route's decode: 1024 + q for
+            // low nibbles, 64 + q (nibble in mantissa bits 4..7) for high ones
             uint32_t pairs[4];
-            q4_0_biased_pairs(b == 0 ? qsA[dw] : qsB[dw], pairs);
+            q4_0_dot_pairs(b == 0 ? qsA[dw] : qsB[dw], lo, hi, m_lo, m_hi, pairs);
             uint8_t* o = qo + b * 32;
             o[4 * dw + 0] = pairs[0] & 0xFu;
-            o[4 * dw + 1] = (pairs[0] >> 16) & 0xFu;
-            o[4 * dw + 2] = pairs[1] & 0xFu;
-            o[4 * dw + 3] = (pairs[1] >> 16) & 0xFu;
-            o[16 + 4 * dw + 0] = pairs[2] & 0xFu;
-            o[16 + 4 * dw + 1] = (pairs[2] >> 16) & 0xFu;
-            o[16 + 4 * dw + 2] = pairs[3] & 0xFu;
-            o[16 + 4 * dw + 3] = (pairs[3] >> 16) & 0xFu;
+            o[4 * dw + 2] = (pairs[0] >> 16) & 0xFu;
+            o[16 + 4 * dw + 0] = (pairs[1] >> 4) & 0xFu;
+            o[16 + 4 * dw + 2] = (pairs[1] >> 20) & 0xFu;
+            o[4 * dw + 1] = pairs[2] & 0xFu;
+            o[4 * dw + 3] = (pairs[2] >> 16) & 0xFu;
+            o[16 + 4 * dw + 1] = (pairs[3] >> 4) & 0xFu;
+            o[16 + 4 * dw + 3] = (pairs[3] >> 20) & 0xFu;
         }
 }
 

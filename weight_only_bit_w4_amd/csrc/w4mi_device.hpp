@@ -103,23 +103,11 @@ __device__ __forceinline__ uint32_t lut_code(uint32_t byte, uint32_t i) {
 }
 
 // GGML Q4_0 block: element i < 16 is the low nibble of qs[i], element i + 16
-// its high nibble. From one qs dword (bytes 4i..4i+3 of a block) this yields
-// four fp16 pairs holding 1024 + q (exact in binary16) for the elements
-//   out[0] = (4i, 4i+1)  out[1] = (4i+2, 4i+3)     (low nibbles)
-//   out[2] = (16+4i, 16+4i+1)  out[3] = (16+4i+2, 16+4i+3)  (high nibbles).
-__device__ __forceinline__ void q4_0_biased_pairs(uint32_t qs, uint32_t (&out)[4]) {
-    const uint32_t t0 = __builtin_amdgcn_perm(0u, qs, 0x0C010C00u);  // [b0, 0, b1, 0]
-    const uint32_t t1 = __builtin_amdgcn_perm(0u, qs, 0x0C030C02u);  // [b2, 0, b3, 0]
-    out[0] = (t0 & 0x000F000Fu) | 0x64006400u;
-    out[1] = (t1 & 0x000F000Fu) | 0x64006400u;
-    out[2] = ((t0 >> 4) & 0x000F000Fu) | 0x64006400u;
-    out[3] = ((t1 >> 4) & 0x000F000Fu) | 0x64006400u;
-}
-
-// The same qs dword as four fp16 pairs for a dot product against x pairs in
-// the matching order, one shift and four AND-ORs: low nibbles sit at bits
-// 0..3 of a binary16 whose exponent makes 1024 + q, high nibbles at bits 4..7
-// of one whose exponent makes 64 + q (ulp 1/16, so 16 q / 16 = q); all exact.
+// its high nibble. One qs dword (bytes 4i..4i+3 of a block) as four fp16
+// pairs for products against x pairs in the matching order, one shift and
+// four AND-ORs: low nibbles sit at bits 0..3 of a binary16 whose exponent
+// makes 1024 + q, high nibbles at bits 4..7 of one whose exponent makes
+// 64 + q (ulp 1/16, so 16 q / 16 = q); all exact.
 //   out[0] = (4i, 4i+2)        as 1024 + q
 //   out[1] = (16+4i, 16+4i+2)  as 64 + q
 //   out[2] = (4i+1, 4i+3)      as 1024 + q

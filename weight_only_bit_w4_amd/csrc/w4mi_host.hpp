@@ -8,6 +8,8 @@
 
 namespace w4mi {
 
+constexpr int kCUs = 256;  // compute units of the MI355X (launch shapes that fill the chip once)
+
 // Records a formatted message for w4_last_error() and returns `status`.
 w4_status fail(w4_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
