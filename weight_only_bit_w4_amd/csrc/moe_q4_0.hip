@@ -193,23 +193,34 @@ struct MoeOps {
     uint32_t w[4];      // block 0: the four dwords that cover the lane's two qs dwords
     uint32_t q1[2];     // block 1: the lane's two qs dwords
 };
-// A lane's LDS read addresses in slot 0 of the rings (slot s adds s slot
-// sizes, folded into the instructions' offsets).
+// A lane's LDS read addresses (byte addresses) in slot 0 of the rings; slot
+// s adds s slot sizes, folded into the instructions' 16-bit offsets. The
+// register fence keeps each address whole in one register (otherwise the
+// compiler folds the ring base into the offset, overflows the field and
+// adds it back per read).
 struct MoeLane {
-    const uint8_t* w;        // the lane's weight row: d of block 0 at +0, of block 1 at +18
-    const uint8_t* wq;       // + 4 h: block 0's covering dwords at +0..+12, block 1's qs at +20, +28
-    const uint8_t* x[2][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
+    uint32_t w;        // the lane's weight row: d of block 0 at +0, of block 1 at +18
+    uint32_t wq;       // + 4 h: block 0's covering dwords at +0..+12, block 1's qs at +20, +28
+    uint32_t x[2][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
 };
 __device__ __forceinline__ MoeLane moe_lane(const uint8_t* wring, const uint8_t* xring, int nl, int lane) {
     const int h = lane >> 5, m = lane & 31, sw = (m >> 1) & 7;
     MoeLane l;
-    l.w = wring + nl * kMoeSpan;
+    l.w = moe_lds_addr(wring) + nl * kMoeSpan;
     l.wq = l.w + 4 * h;
+    asm volatile("" : "+v"(l.w), "+v"(l.wq));
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) l.x[b][s] = xring + m * kMoeXRow + 16 * ((4 * b + 2 * s + h) ^ sw);
+        for (int s = 0; s < 2; ++s) {
+            l.x[b][s] = moe_lds_addr(xring) + m * kMoeXRow + 16 * ((4 * b + 2 * s + h) ^ sw);
+            asm volatile("" : "+v"(l.x[b][s]));
+        }
     return l;
+}
+template <typename T>
+__device__ __forceinline__ T moe_lds_load(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
 }
 template <int SLOT>
 __device__ __forceinline__ MoeOps moe_read(const MoeLane& l) {
@@ -217,17 +228,16 @@ __device__ __forceinline__ MoeOps moe_read(const MoeLane& l) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) o.x[b][s] = *reinterpret_cast<const u32x4*>(l.x[b][s] + SLOT * kMoeXSlot);
+        for (int s = 0; s < 2; ++s) o.x[b][s] = moe_lds_load<u32x4>(l.x[b][s] + SLOT * kMoeXSlot);
     // Block 0 at byte 0 of the row's window (d, then qs two bytes past a
     // dword boundary), block 1 at byte 18 (qs dword-aligned).
-    const uint8_t* w = l.w + SLOT * kMoeWSlot;
-    const uint8_t* wq = l.wq + SLOT * kMoeWSlot;
-    o.d0 = *reinterpret_cast<const uint16_t*>(w);
-    o.d1 = *reinterpret_cast<const uint16_t*>(w + 18);
+    const uint32_t w = l.w + SLOT * kMoeWSlot, wq = l.wq + SLOT * kMoeWSlot;
+    o.d0 = moe_lds_load<uint16_t>(w);
+    o.d1 = moe_lds_load<uint16_t>(w + 18);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.w[i] = reinterpret_cast<const uint32_t*>(wq)[i];
-    o.q1[0] = *reinterpret_cast<const uint32_t*>(wq + 20);
-    o.q1[1] = *reinterpret_cast<const uint32_t*>(wq + 28);
+    for (int i = 0; i < 4; ++i) o.w[i] = moe_lds_load<uint32_t>(wq + 4 * i);
+    o.q1[0] = moe_lds_load<uint32_t>(wq + 20);
+    o.q1[1] = moe_lds_load<uint32_t>(wq + 28);
     return o;
 }
 __device__ __forceinline__ void moe_apply(const MoeOps& o, const Q4Consts& k, f32x16& acc) {
@@ -437,10 +447,13 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
                     moe_apply(ops[0], k, acc);
                 // Lane (n, h) holds routed rows 8 (i / 4) + 4 h + i % 4 of weight row n.
                 const int ncol = n0 + nl;
+                uint32_t pr = moe_lds_addr(pass_rows) + 16u * (uint32_t)(lane >> 5);  // row 4 h's id
+                asm volatile("" : "+v"(pr));  // one base register, the rest in offsets
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const uint32_t mm = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    if (mm < mcnt && ncol < N) out[(size_t)pass_rows[mm] * N + ncol] = acc[i];
+                    const uint32_t row = moe_lds_load<uint32_t>(pr + 4u * (8 * (i >> 2) + (i & 3)));
+                    if (mm < mcnt && ncol < N) out[(size_t)row * N + ncol] = acc[i];
                 }
             }
             moe_wait_vmcnt<0>();  // stores done: the next chunk's DMA waits count only DMA
