@@ -12,8 +12,8 @@
 //     contiguous ranges of 32-row tiles (enough workgroups to fill the chip);
 //     a range is read exactly once per 32 routed rows and applied with
 //     v_mfma_f32_32x32x16_f16, f32 accumulation, one tile per wavefront.
-//     Weights and the routed rows' x stream through a 5-slot LDS ring by
-//     buffer-to-LDS DMA, one 64-wide K window (2 Q4_0 blocks, 36 bytes of
+//     Weights and the routed rows' x stream through a 3-slot LDS ring by
+//     buffer-to-LDS DMA, one 128-wide K window (4 Q4_0 blocks, 72 bytes of
 //     each weight row) per step; each lane decodes two qs dwords per block
 //     into fp16 (q - 8) d.
 #include <type_traits>
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
 // Grouped GEMM layout. A workgroup of 12 wavefronts takes one expert and a
 // contiguous range of its 32-row weight tiles (the expert's tiles are split
 // over enough workgroups to fill the chip) and streams them in chunks of up
-// to 12 tiles, one tile per wavefront, over K in windows of 64 (two Q4_0
-// blocks, 36 bytes of each weight row). A wavefront owns its tile for the
+// to 12 tiles, one tile per wavefront, over K in windows of 128 (four Q4_0
+// blocks, 72 bytes of each weight row). A wavefront owns its tile for the
 // whole of K, so its accumulators hold finished sums and no partial sums
 // cross wavefronts.
 constexpr int kMoeWaves = 12;                         // three to a SIMD: 168 registers each
@@ -116,13 +116,15 @@ constexpr int kMoeThreads = kMoeWaves * 64;
 constexpr int kMoeTile = 32;                          // weight rows per wavefront (one 32x32 MFMA tile)
 constexpr int kMoeMR = 32;                            // routed rows per pass
 constexpr int kMoeChunkRows = kMoeTile * kMoeWaves;   // 384
-constexpr int kMoeWinBytes = 36;                      // two blocks of a weight row per window
-constexpr int kMoeSpan = 48;                          // ... moved as three 16-byte pieces (12 bytes read ahead)
-constexpr int kMoeWSlot = kMoeChunkRows * kMoeSpan;   // 18 KB
-constexpr int kMoeXRow = 128;                         // 64 binary16 of a routed row per window
-constexpr int kMoeXSlot = kMoeMR * kMoeXRow;          // 4 KB
-constexpr int kMoeXDma = kMoeXSlot / 1024;            // 4 DMA instructions per x window
-constexpr int kMoeStages = 4;                         // ring depth: windows j + 1 .. j + 3 in flight at window j
+constexpr int kMoeWinBlocks = 4;                      // Q4_0 blocks of a row per window (128 of K)
+constexpr int kMoeWinBytes = 18 * kMoeWinBlocks;      // 72 bytes of a weight row per window
+constexpr int kMoeSpan = 80;                          // ... moved as five 16-byte pieces (8 bytes read ahead)
+constexpr int kMoeWDma = (kMoeChunkRows * kMoeSpan / 16 + 63) / 64;  // 30 DMA instructions per W window
+constexpr int kMoeWSlot = kMoeWDma * 1024;            // 30 KB
+constexpr int kMoeXRow = 32 * kMoeWinBlocks * 2;      // 256 bytes: 128 binary16 of a routed row per window
+constexpr int kMoeXSlot = kMoeMR * kMoeXRow;          // 8 KB
+constexpr int kMoeXDma = kMoeXSlot / 1024;            // 8 DMA instructions per x window
+constexpr int kMoeStages = 3;                         // ring depth: window j + 1 in flight at window j
 constexpr uint32_t kMoeOob = 0x80000000u;
 
 __device__ __forceinline__ uint32_t moe_lds_addr(const void* p) {
@@ -178,20 +180,20 @@ __device__ __forceinline__ u32x4 q4_0_operand(uint32_t qs, f16x2 dd, const Q4Con
     return o;
 }
 
-// One 64-wide K window for a wavefront's 32 weight rows against the pass's
-// 32 routed rows: two blocks b, two MFMA k-steps s each. Lane (n, h) =
+// One 128-wide K window for a wavefront's 32 weight rows against the pass's
+// 32 routed rows: four blocks b, two MFMA k-steps s each. Lane (n, h) =
 // (lane % 32, lane / 32) feeds step s of block b with qs dword 2 s + h of
 // weight row n; the x operand of lane (m, h) is the same eight elements of
 // routed row m, which the xh order stores as the 16-byte chunk 4 b + 2 s + h
-// of the window row (kept at slot chunk ^ ((m / 2) % 8), which keeps the
-// 32-row reads conflict-free). The window's LDS reads (moe_read) are issued a
-// window ahead of its arithmetic (moe_apply), so they overlap the previous
-// window's decode and matrix work instead of following each barrier.
+// of the window row (kept at slot chunk ^ (m % 16), which keeps the 32-row
+// reads conflict-free). The window's LDS reads (moe_read) are issued a window
+// ahead of its arithmetic (moe_apply), so they overlap the previous window's
+// decode and matrix work instead of following each barrier.
 struct MoeOps {
-    u32x4 x[2][2];      // x operands [block][step]
-    uint32_t d0, d1;    // block scales (binary16)
-    uint32_t w[4];      // block 0: the four dwords that cover the lane's two qs dwords
-    uint32_t q1[2];     // block 1: the lane's two qs dwords
+    u32x4 x[kMoeWinBlocks][2];       // x operands [block][step]
+    uint32_t d[kMoeWinBlocks];       // block scales (binary16)
+    uint32_t we[kMoeWinBlocks / 2][4];  // even blocks: the four dwords that cover the lane's two qs dwords
+    uint32_t wo[kMoeWinBlocks / 2][2];  // odd blocks: the lane's two qs dwords
 };
 // A lane's LDS read addresses (byte addresses) in slot 0 of the rings; slot
 // s adds s slot sizes, folded into the instructions' 16-bit offsets. The
@@ -199,18 +201,18 @@ struct MoeOps {
 // compiler folds the ring base into the offset, overflows the field and
 // adds it back per read).
 struct MoeLane {
-    uint32_t w;        // the lane's weight row: d of block 0 at +0, of block 1 at +18
-    uint32_t wq;       // + 4 h: block 0's covering dwords at +0..+12, block 1's qs at +20, +28
-    uint32_t x[2][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
+    uint32_t w;        // the lane's weight row in the window: block b's d at +18 b
+    uint32_t wq;       // + 4 h: even block b's covering dwords at +18 b .. +18 b + 12, odd block b's qs at +18 b + 2, +10
+    uint32_t x[kMoeWinBlocks][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
 };
 __device__ __forceinline__ MoeLane moe_lane(const uint8_t* wring, const uint8_t* xring, int nl, int lane) {
-    const int h = lane >> 5, m = lane & 31, sw = (m >> 1) & 7;
+    const int h = lane >> 5, m = lane & 31, sw = m & 15;
     MoeLane l;
     l.w = moe_lds_addr(wring) + nl * kMoeSpan;
     l.wq = l.w + 4 * h;
     asm volatile("" : "+v"(l.w), "+v"(l.wq));
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kMoeWinBlocks; ++b)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             l.x[b][s] = moe_lds_addr(xring) + m * kMoeXRow + 16 * ((4 * b + 2 * s + h) ^ sw);
@@ -226,52 +228,57 @@ template <int SLOT>
 __device__ __forceinline__ MoeOps moe_read(const MoeLane& l) {
     MoeOps o;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kMoeWinBlocks; ++b)
 #pragma unroll
         for (int s = 0; s < 2; ++s) o.x[b][s] = moe_lds_load<u32x4>(l.x[b][s] + SLOT * kMoeXSlot);
-    // Block 0 at byte 0 of the row's window (d, then qs two bytes past a
-    // dword boundary), block 1 at byte 18 (qs dword-aligned).
+    // Block b at byte 18 b of the row's window: d, then qs, which starts two
+    // bytes past a dword boundary for even b and on one for odd b.
     const uint32_t w = l.w + SLOT * kMoeWSlot, wq = l.wq + SLOT * kMoeWSlot;
-    o.d0 = moe_lds_load<uint16_t>(w);
-    o.d1 = moe_lds_load<uint16_t>(w + 18);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.w[i] = moe_lds_load<uint32_t>(wq + 4 * i);
-    o.q1[0] = moe_lds_load<uint32_t>(wq + 20);
-    o.q1[1] = moe_lds_load<uint32_t>(wq + 28);
+    for (int b = 0; b < kMoeWinBlocks; ++b) o.d[b] = moe_lds_load<uint16_t>(w + 18 * b);
+#pragma unroll
+    for (int e = 0; e < kMoeWinBlocks / 2; ++e) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.we[e][i] = moe_lds_load<uint32_t>(wq + 36 * e + 4 * i);
+        o.wo[e][0] = moe_lds_load<uint32_t>(wq + 36 * e + 20);
+        o.wo[e][1] = moe_lds_load<uint32_t>(wq + 36 * e + 28);
+    }
     return o;
 }
-__device__ __forceinline__ void moe_apply(const MoeOps& o, const Q4Consts& k, f32x16& acc) {
-    uint32_t qs[2][2];
-    qs[0][0] = __builtin_amdgcn_alignbyte(o.w[1], o.w[0], 2);
-    qs[0][1] = __builtin_amdgcn_alignbyte(o.w[3], o.w[2], 2);
-    qs[1][0] = o.q1[0];
-    qs[1][1] = o.q1[1];
-    const f16x2 dd[2] = {as_f16x2(o.d0 * 0x10001u), as_f16x2(o.d1 * 0x10001u)};
-    u32x4 wop[2][2];
+// Blocks at or past `live` (the half last window when K % 128 == 64) get
+// d = 0, which zeroes their weights whatever the ring holds there; their x
+// chunks were loaded as zeros.
+__device__ __forceinline__ void moe_apply(const MoeOps& o, const Q4Consts& k, f32x16& acc, int live) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) wop[b][s] = q4_0_operand(qs[b][s], dd[b], k);
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kMoeWinBlocks; ++b) {
+        uint32_t qs[2];
+        if (b % 2 == 0) {
+            qs[0] = __builtin_amdgcn_alignbyte(o.we[b / 2][1], o.we[b / 2][0], 2);
+            qs[1] = __builtin_amdgcn_alignbyte(o.we[b / 2][3], o.we[b / 2][2], 2);
+        } else {
+            qs[0] = o.wo[b / 2][0];
+            qs[1] = o.wo[b / 2][1];
+        }
+        const f16x2 dd = as_f16x2((b < kMoeWinBlocks / 2 || b < live ? o.d[b] : 0u) * 0x10001u);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.x[b][s]),
-                                                         __builtin_bit_cast(f16x8, wop[b][s]), acc, 0, 0, 0);
+                                                         __builtin_bit_cast(f16x8, q4_0_operand(qs[s], dd, k)), acc, 0, 0, 0);
+    }
 }
 __device__ __forceinline__ void moe_wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// LDS: kMoeStages slots of W [384 rows x 48 B] (row r's window bytes, as
-// stored, at 48 r) and of x [32 rows x 128 B] (routed row m's chunk c at
-// slot c ^ ((m / 2) % 8)), then the pass's 32 output row indices.
-// DMA roles: x instruction i (rows 8 i .. 8 i + 7) is issued by wavefront i,
-// W instruction i (16-byte pieces 64 i .. 64 i + 63 of the slot: row q / 3,
-// piece q % 3) by wavefront (i + 4) % 12, so no wavefront issues more than
-// two per window. Window j + 4 is issued after barrier j into the slot of
+// LDS: kMoeStages slots of W [384 rows x 80 B] (row r's window bytes, as
+// stored, at 80 r) and of x [32 rows x 256 B] (routed row m's chunk c at
+// slot c ^ (m % 16)), then the pass's 32 output row indices.
+// DMA roles: x instruction i (rows 4 i .. 4 i + 3) is issued by wavefront i,
+// W instruction i (16-byte pieces 64 i .. 64 i + 63 of the slot: row q / 5,
+// piece q % 5) by wavefront (i + 8) % 12, so no wavefront issues more than
+// four per window. Window j + 2 is issued after barrier j into the slot of
 // window j - 1, which every wavefront finished reading before barrier j; each
 // wavefront waits for its own DMA of window j before barrier j, after which
 // every wavefront may read it. All DMA offsets are per-lane (no scalar
-// offset), so the descriptors' range checks cover every byte read: the 12
+// offset), so the descriptors' range checks cover every byte read: the 8
 // bytes read past a row's last window are the next row's (unused) or, past the
 // chunk's last row, zeros.
 constexpr int kMoeLds = kMoeStages * (kMoeWSlot + kMoeXSlot) + kMoeMR * 4;
@@ -304,13 +311,24 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
         reinterpret_cast<const uint32_t*>(scratch + lay.rows) + reinterpret_cast<const uint32_t*>(scratch + lay.offsets)[e];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwin = K / 64;
-    const uint32_t row_bytes = (uint32_t)(K / 32) * 18u;
+    const int nb = K / 32;
+    const int nwin = (nb + kMoeWinBlocks - 1) / kMoeWinBlocks;
+    const int last_live = nb - kMoeWinBlocks * (nwin - 1);  // blocks in the last window (2 or 4)
+    const uint32_t row_bytes = (uint32_t)nb * 18u;
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(scratch + lay.xh, (uint32_t)((size_t)n_tokens * (size_t)K * 2u));
     const Q4Consts k{vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u), vreg(0x54005400u)};
     const bool x_dma = wave < kMoeXDma;
-    const int wi0 = (wave + kMoeWaves - kMoeXDma) % kMoeWaves;  // this wavefront's W instructions: wi0, wi0 + 16
-    uint32_t xo = kMoeOob;  // x DMA lane offset of the pass's routed row (set per pass)
+    const int wi0 = (wave + kMoeWaves - kMoeXDma) % kMoeWaves;  // this wavefront's W instructions: wi0 + 12 t
+    // x DMA lane (wavefronts 0 .. 7): routed row m = 4 wave + lane / 16, LDS
+    // position lane % 16 of that row holds chunk c = (lane % 16) ^ (m % 16),
+    // from K block 4 w + c / 4 of window w.
+    const int xm = 4 * wave + (lane >> 4);
+    const int xc = (lane & 15) ^ (xm & 15);
+    uint32_t xo = kMoeOob;  // the pass's routed row's lane offset (set per pass)
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    static_assert(kMoeStages == 3, "the slot sequences below are written for three slots");
 
     for (uint32_t m0 = 0; m0 < cnt; m0 += kMoeMR) {
         const uint32_t mcnt = min((uint32_t)kMoeMR, cnt - m0);
@@ -320,108 +338,102 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
             const int crow = min(min(t_end - tc, kMoeWaves) * kMoeTile, N - n0);
             const __amdgpu_buffer_rsrc_t wsrc =
                 make_rsrc(w + (size_t)e * expert_stride + (size_t)n0 * row_bytes, (uint32_t)crow * row_bytes);
-            const int n_wi = (crow * 3 + 63) / 64;  // W DMA instructions per window
-            const int nw = (wi0 < n_wi ? 1 : 0) + (wi0 + kMoeWaves < n_wi ? 1 : 0);
-            uint32_t wo[2];
+            const int n_wi = (crow * (kMoeSpan / 16) + 63) / 64;  // W DMA instructions per window
+            const int nw = (wi0 < n_wi ? 1 : 0) + (wi0 + kMoeWaves < n_wi ? 1 : 0) + (wi0 + 2 * kMoeWaves < n_wi ? 1 : 0);
+            uint32_t wo[3];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int q = 64 * (wi0 + kMoeWaves * t) + lane, r = q / 3, j = q % 3;
+            for (int t = 0; t < 3; ++t) {
+                const int q = 64 * (wi0 + kMoeWaves * t) + lane, r = q / 5, j = q % 5;
                 wo[t] = r < crow ? (uint32_t)r * row_bytes + 16u * (uint32_t)j : kMoeOob;
             }
             // DMA of window win into ring slot SLOT (= win % kMoeStages).
             auto issue_w = [&](auto slot_c, int win) {
                 constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 3; ++t)
                     if (t < nw)
                         moe_dma16(wsrc, wring + slot * kMoeWSlot + 1024 * (wi0 + kMoeWaves * t),
                                   wo[t] + (uint32_t)(kMoeWinBytes * win), 0);
             };
             auto issue_x = [&](auto slot_c, int win) {
                 constexpr int slot = decltype(slot_c)::value;
-                if (x_dma) moe_dma16(xsrc, xring + slot * kMoeXSlot + 1024 * wave, xo + (uint32_t)(kMoeXRow * win), 0);
+                // Chunks of blocks past K (a half last window) land as zeros.
+                if (x_dma)
+                    moe_dma16(xsrc, xring + slot * kMoeXSlot + 1024 * wave,
+                              kMoeWinBlocks * win + (xc >> 2) < nb ? xo + (uint32_t)(kMoeXRow * win) : kMoeOob, 0);
             };
-            using S0 = std::integral_constant<int, 0>;
-            using S1 = std::integral_constant<int, 1>;
-            using S2 = std::integral_constant<int, 2>;
-            using S3 = std::integral_constant<int, 3>;
-            static_assert(kMoeStages == 4, "the slot sequence below is written for four slots");
-            // Prologue, windows 0 .. 2: the weights need no routing ids, so
-            // W(0) and W(1) go out before the ids are read; then x(0), x(1),
-            // W(2), x(2).
-            const bool full = nwin >= kMoeStages - 1;
+            // Prologue, windows 0 and 1: the weights need no routing ids, so
+            // W(0) goes out before the ids are read; then x(0), W(1), x(1).
             issue_w(S0{}, 0);
-            if (nwin > 1) issue_w(S1{}, 1);
             if (tc == t_begin) {
-                // This pass's routed rows: x DMA wavefront i (rows 8 i .. 8 i + 7)
-                // reads its eight ids by one scalar load (not counted by vmcnt,
-                // so it does not wait behind the DMA) and records them for the
-                // stores. Ids past the pass's count are not used.
+                // This pass's routed rows: x DMA wavefront i (rows 4 i .. 4 i + 3)
+                // reads its ids by one scalar load (not counted by vmcnt, so it
+                // does not wait behind the DMA) and records them for the stores.
+                // Ids past the pass's count are not used.
                 if (x_dma) {
-                    const uint32_t* ids8 = rows + m0 + 8 * wave;
                     uint32_t id[8];
-                    moe_sload8(ids8, id);
-                    const int r = lane >> 3;
-                    uint32_t rid = id[0];
+                    moe_sload8(rows + m0 + 4 * wave, id);
+                    const int r = lane >> 4;
+                    uint32_t rid = id[0], own = id[0];
 #pragma unroll
-                    for (int i = 1; i < 8; ++i) rid = r == i ? id[i] : rid;
-                    const int m = 8 * wave + r;
-                    const int c = (lane & 7) ^ ((m >> 1) & 7);
-                    xo = (uint32_t)m < mcnt ? (rid / (uint32_t)top_k) * (uint32_t)K * 2u + 16u * (uint32_t)c : kMoeOob;
-                    uint32_t own = id[0];
-#pragma unroll
-                    for (int i = 1; i < 8; ++i) own = lane == i ? id[i] : own;
-                    if (lane < 8) pass_rows[8 * wave + lane] = own;
+                    for (int i = 1; i < 4; ++i) {
+                        rid = r == i ? id[i] : rid;
+                        own = lane == i ? id[i] : own;
+                    }
+                    xo = (uint32_t)xm < mcnt ? (rid / (uint32_t)top_k) * (uint32_t)K * 2u + 16u * (uint32_t)xc : kMoeOob;
+                    if (lane < 4) pass_rows[4 * wave + lane] = own;
                 }
             }
             issue_x(S0{}, 0);
-            if (nwin > 1) issue_x(S1{}, 1);
-            if (full) {
-                issue_w(S2{}, 2);
-                issue_x(S2{}, 2);
+            if (nwin > 1) {
+                issue_w(S1{}, 1);
+                issue_x(S1{}, 1);
             }
             const int per_window = nw + (x_dma ? 1 : 0);
+            // At window j (>= 0) only this wavefront's DMA of window j + 1 may
+            // still be in flight (each window's W then x, in window order).
+            auto wait_window = [&](int j) {
+                if (j + 1 >= nwin) {
+                    moe_wait_vmcnt<0>();
+                    return;
+                }
+                switch (per_window) {
+                    case 0: moe_wait_vmcnt<0>(); break;
+                    case 1: moe_wait_vmcnt<1>(); break;
+                    case 2: moe_wait_vmcnt<2>(); break;
+                    case 3: moe_wait_vmcnt<3>(); break;
+                    default: moe_wait_vmcnt<4>(); break;
+                }
+            };
             f32x16 acc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = 0.f;
             const bool busy = kMoeTile * wave < crow;
             const int nl = kMoeTile * wave + (lane & 31);  // this lane's weight row in the chunk
             const MoeLane ln = moe_lane(wring, xring, nl, lane);
-            // Two operand sets alternate (the loop is unrolled by four, the ring
-            // depth, so that neither set is copied and every slot offset is a
-            // constant): after barrier j a wavefront reads window j into one
-            // set, then decodes and multiplies window j - 1 from the other.
+            // Two operand sets alternate (the loop is unrolled by six, a multiple
+            // of the ring depth, so that neither set is copied and every slot
+            // offset is a constant): after barrier j a wavefront reads window j
+            // into one set, then decodes and multiplies window j - 1 from the
+            // other.
             MoeOps ops[2];
-            // Window 0: W(0), W(1), x(0) have landed once at most x(1), W(2),
-            // x(2) (this wavefront's share) are in flight.
-            if (!full) {
-                moe_wait_vmcnt<0>();
-            } else if (x_dma) {
-                if (nw == 0) moe_wait_vmcnt<2>(); else if (nw == 1) moe_wait_vmcnt<3>(); else moe_wait_vmcnt<4>();
-            } else {
-                if (nw == 0) moe_wait_vmcnt<0>(); else if (nw == 1) moe_wait_vmcnt<2>(); else moe_wait_vmcnt<4>();
-            }
+            wait_window(0);
+            moe_wait_lgkm();  // pass_rows written
             moe_barrier();
             if (busy) ops[0] = moe_read<0>(ln);
             if (kMoeStages - 1 < nwin) {
-                issue_w(S3{}, kMoeStages - 1);
-                issue_x(S3{}, kMoeStages - 1);
+                issue_w(S2{}, kMoeStages - 1);
+                issue_x(S2{}, kMoeStages - 1);
             }
             auto step = [&](auto slot_c, int j, MoeOps& into, const MoeOps& from) {
                 constexpr int slot = decltype(slot_c)::value;
-                // Windows j + 1 .. j + kMoeStages - 2 may still be in flight
-                // (from window 1 on, each window's W then x went out in window
-                // order).
-                if (j + kMoeStages - 2 < nwin)
-                    moe_wait_window<kMoeStages - 2>(per_window);
-                else
-                    moe_wait_vmcnt<0>();
+                wait_window(j);
                 moe_wait_lgkm();  // this wavefront's reads of window j - 1 are done: its slot is reused below
                 moe_barrier();
                 if (busy) {
                     into = moe_read<slot>(ln);
                     __builtin_amdgcn_sched_barrier(0);  // the reads go out before the arithmetic below
-                    moe_apply(from, k, acc);
+                    moe_apply(from, k, acc, kMoeWinBlocks);
                 }
                 if (j + kMoeStages - 1 < nwin) {
                     using Next = std::integral_constant<int, (slot + kMoeStages - 1) % kMoeStages>;
@@ -429,22 +441,25 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
                     issue_x(Next{}, j + kMoeStages - 1);
                 }
             };
-            int j = 1;  // j % 4 == 1 at the top of each round
-            for (; j + 3 < nwin; j += 4) {
+            int j = 1;  // j % 6 == 1 at the top of each round
+            for (; j + 5 < nwin; j += 6) {
                 step(S1{}, j, ops[1], ops[0]);
                 step(S2{}, j + 1, ops[0], ops[1]);
-                step(S3{}, j + 2, ops[1], ops[0]);
-                step(S0{}, j + 3, ops[0], ops[1]);
+                step(S0{}, j + 2, ops[1], ops[0]);
+                step(S1{}, j + 3, ops[0], ops[1]);
+                step(S2{}, j + 4, ops[1], ops[0]);
+                step(S0{}, j + 5, ops[0], ops[1]);
             }
             if (j < nwin) step(S1{}, j, ops[1], ops[0]);
             if (j + 1 < nwin) step(S2{}, j + 1, ops[0], ops[1]);
-            if (j + 2 < nwin) step(S3{}, j + 2, ops[1], ops[0]);
-            const bool last_in_1 = (nwin - 1) & 1;  // the last window's set
+            if (j + 2 < nwin) step(S0{}, j + 2, ops[1], ops[0]);
+            if (j + 3 < nwin) step(S1{}, j + 3, ops[0], ops[1]);
+            if (j + 4 < nwin) step(S2{}, j + 4, ops[1], ops[0]);
             if (busy) {
-                if (last_in_1)
-                    moe_apply(ops[1], k, acc);
+                if ((nwin - 1) & 1)  // the last window's set
+                    moe_apply(ops[1], k, acc, last_live);
                 else
-                    moe_apply(ops[0], k, acc);
+                    moe_apply(ops[0], k, acc, last_live);
                 // Lane (n, h) holds routed rows 8 (i / 4) + 4 h + i % 4 of weight row n.
                 const int ncol = n0 + nl;
                 uint32_t pr = moe_lds_addr(pass_rows) + 16u * (uint32_t)(lane >> 5);  // row 4 h's id
