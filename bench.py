@@ -41,14 +41,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "4fbeb2b607bb7f8e", 36831156 + 57347),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "8a69411c591488f2", 100826117 + 16801303),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "8a69411c591488f2", 81614016 + 11290926),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "ee689bd942a9f5fe", 114160303 + 5767168),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "ee689bd942a9f5fe", 13134047 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "ee689bd942a9f5fe", 14103706 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "601002c8d3e96e21", 26034627 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "601002c8d3e96e21", 113361948 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "500af2f7dc0eccda", 36831109 + 57344),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "be2285be2ab1dacd", 100826021 + 16802611),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "be2285be2ab1dacd", 81613943 + 11291443),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123741520 + 5767168),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 13134025 + 45089),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 14099597 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 26034603 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 113361840 + 176128),
 }
 
 
