@@ -108,19 +108,32 @@ def test_qmv_affine4(K, N, seed):
     (300, 128, 256),                      # 2 K steps (producer loop tail of 2)
     (257, 256, 160),                      # 4 K steps (one unrolled round + a tail of 1)
     (384, 1024, 384),                     # 16 K steps, several tiles each way
-    # at most 16 rows of x with K <= 8192: the GEMV form, every weight row read once for all rows
+    # the GEMV form (every weight row read once for all rows): fewer than 6 rows, or up to 16
+    # rows when K % 256 != 0 (K <= 8192)
     (2, 4096, 14336),                     # the decode workload's weights, two rows (batches of 2)
     (3, 96, 64),                          # 3 groups, one batch of 4 with a missing row
-    (8, 4096, 256),                       # 2 chunks, two batches of 4
     (5, 2080, 160),                       # ragged second chunk, a 1-row second batch
-    (8, 8192, 64),                        # 4 chunks: batches of 2
-    (6, 6144, 96),                        # 3 chunks: batches of 2
-    (16, 4096, 160),                      # 2 chunks, four batches of 4
-    (13, 8192, 32),                       # 4 chunks, batches of 2, a 1-row last batch
+    (8, 4160, 256),                       # 3 chunks: batches of 2
+    (12, 2112, 96),                       # 2 chunks, batches of 4
+    (16, 4128, 160),                      # 3 chunks, batches of 2
+    (13, 8160, 32),                       # 4 chunks, batches of 2, a 1-row last batch
     (6, 8224, 32),                        # one group past the GEMV form: the matrix-core path
-    (17, 4096, 14336),                    # one row past it: the small-M matrix-core kernel, 128 K steps
     (40, 96, 96),                         # 3 K steps: the load ring's prologue covers all of K
     (64, 544, 256),                       # 17 K steps: ring wrap with a partial last round
+    # 6 <= M <= 64 with K % 256 == 0: weight tiles streamed once (256-wide K windows; a
+    # 6-slot ring for up to 32 rows of x, 3 slots above)
+    (6, 256, 64),                         # the smallest M of the tile form, one window
+    (8, 4096, 256),                       # 16 windows: two rounds of 6 and a tail of 4
+    (8, 8192, 64),                        # 32 windows, one workgroup
+    (6, 6144, 96),                        # 24 windows (four full rounds), a half workgroup
+    (16, 4096, 160),                      # ragged last workgroup (32 rows)
+    (13, 8192, 32),                       # one tile: the second tile's rows are past N
+    (17, 4096, 14336),                    # the decode workload's weights, 17 rows
+    (20, 1536, 224),                      # 6 windows (exactly one round), 3.5 workgroups
+    (31, 3328, 32),                       # 13 windows, one tile
+    (33, 768, 160),                       # two x tiles (3-slot ring): 3 windows, 2.5 workgroups
+    (48, 512, 4096),                      # two x tiles, 2 windows, 64 workgroups
+    (64, 2816, 96),                       # two x tiles, 11 windows: three rounds and a tail of 2
 ])
 def test_qmm_affine4_small(M, K, N):
     c = synth.affine_case(M, K, N, seed=M + K + N)
@@ -130,6 +143,25 @@ def test_qmm_affine4_small(M, K, N):
     acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
     ms, mx = _affine_scales(c)
     _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"qmm M={M} K={K} N={N}")
+
+
+@pytest.mark.gpu
+def test_qmm_affine4_small_unaligned_scales():
+    """Scales and biases only 2-byte aligned: the weight-tile form (4-byte DMA offsets) is not
+    taken; the 64x128-tile matrix-core kernel gives the same result."""
+    M, K, N = 24, 512, 96
+    c = synth.affine_case(M, K, N, seed=5)
+    w, s, b, x = _affine_dev(c)
+    s2 = torch.empty(s.numel() + 1, dtype=torch.bfloat16, device="cuda")[1:].view(N, K // 32)
+    b2 = torch.empty(b.numel() + 1, dtype=torch.bfloat16, device="cuda")[1:].view(N, K // 32)
+    s2.copy_(s)
+    b2.copy_(b)
+    assert s2.data_ptr() % 4 == 2 and b2.data_ptr() % 4 == 2
+    y = B.qmm_affine4(w, s2, b2, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, "qmm unaligned scales")
 
 
 def _sample_points(M, N, count, seed, tile_m=256, tile_n=128):

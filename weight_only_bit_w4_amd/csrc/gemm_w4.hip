@@ -876,6 +876,284 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
     }
 }
 
+// ---------------------------------------------------------------- small batches, weight tiles
+// qmm_affine4 for a few dozen rows of x (M <= 64, K % 256 == 0): the weights
+// are read exactly once and every row of x is applied to them on the matrix
+// cores. A workgroup of 16 wavefronts takes two 32-row weight tiles; wavefront
+// (t, p) = (w / 8, w % 8) owns tile t and k-steps 2 p, 2 p + 1 (quantisation
+// group p) of each 256-wide K window, against all M rows (MT 32-row tiles of
+// x); at the end each of a tile's eight wavefronts sums two of the 16
+// accumulator registers over the eight partial sums (through LDS) and stores
+// them. Each lane decodes its own
+// weight word straight into a matrix-core operand (affine_word_bf16: bf16
+// q s + b in k order). Weights (128 packed bytes, 16 bytes of scales and 16 of
+// biases per row per window) and x (M rows x 512 bytes per window, from L2)
+// stream through one LDS ring (6 slots for up to 32 rows of x, 3 for up to
+// 64) by buffer-to-LDS DMA that all 16 wavefronts issue.
+constexpr int kTlWaves = 16, kTlThreads = kTlWaves * 64;
+constexpr int kTlMinM = 6;                           // fewer rows take the shared-x GEMV form
+constexpr int kTlTiles = 2;                          // 32-row weight tiles per workgroup
+constexpr int kTlParts = kTlWaves / kTlTiles;        // 8 wavefronts share a tile's K
+constexpr int kTlSteps = 16 / kTlParts;              // k-steps (16 of K) per wavefront per window
+constexpr int kTlWinK = 256;
+constexpr int kTlRows = 32 * kTlTiles;               // 64 weight rows
+constexpr int kTlWRow = kTlWinK / 2;                 // 128 packed bytes of a row per window
+constexpr int kTlWBytes = kTlRows * kTlWRow;         // 8 KB
+constexpr int kTlSBytes = kTlRows * 16;              // 1 KB: 8 groups' bf16 scales per row
+constexpr int kTlWSlot = kTlWBytes + 2 * kTlSBytes;  // 10 KB: packed, scales, biases
+constexpr int kTlXRow = kTlWinK * 2;                 // 512 bytes of an x row per window
+constexpr int kTlWDma = kTlWBytes / 1024 + 2;        // 10 weight DMA instructions per window
+template <int MT> struct TlShape {
+    static constexpr int kXSlot = MT * 32 * kTlXRow;          // 16 or 32 KB
+    static constexpr int kXDma = kXSlot / 1024;               // 16 or 32 x DMA instructions per window
+    static constexpr int kDma = kTlWDma + kXDma;              // 26 or 42 per window
+    static constexpr int kStages = MT == 1 ? 6 : 3;           // as deep as 160 KB of LDS allows
+    static constexpr int kLds = kStages * (kTlWSlot + kXSlot);
+};
+
+// lds_dma16 with the LDS address forced into a scalar register (the compiler
+// cannot always prove the slot arithmetic wave-uniform).
+__device__ __forceinline__ void tl_dma16(const __amdgpu_buffer_rsrc_t& rsrc, const void* lds, uint32_t voff) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(rsrc));
+}
+// A load from an LDS byte address.
+template <typename T>
+__device__ __forceinline__ T lds_ld(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
+}
+// s_waitcnt vmcnt(n) for a run-time n (0 .. 23; larger waits for everything).
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+    switch (n) {
+        case 16: wait_vmcnt<16>(); break;
+        case 17: wait_vmcnt<17>(); break;
+        case 18: wait_vmcnt<18>(); break;
+        case 19: wait_vmcnt<19>(); break;
+        case 20: wait_vmcnt<20>(); break;
+        case 21: wait_vmcnt<21>(); break;
+        case 22: wait_vmcnt<22>(); break;
+        case 23: wait_vmcnt<23>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 15: wait_vmcnt<15>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
+// DMA instruction i of a window (issued by wavefront i % 16), lane l:
+//   i < 8: packed weights, 16-byte piece q = 64 i + l of the slot: row q / 8,
+//          slot position q % 8 holding the row's piece (q % 8) ^ (row % 8)
+//          (the swizzle spreads the 32-row word reads of a k-step over the
+//          banks);
+//   i = 8, 9: the 64 rows' 16 bytes of scales, of biases;
+//   i >= 10: x, piece q = 64 (i - 10) + l: row q / 32, slot position q % 32
+//          holding chunk (q % 32) ^ (row % 16).
+// Window j + S - 1 (S slots) goes out after barrier j into the slot of window
+// j - 1, which every wavefront finished with before barrier j; each wavefront
+// waits for its own DMA of window j before barrier j. All offsets are per-lane, so the descriptors' range checks cover every
+// byte (rows past N or M read zeros).
+template <int MT>
+__global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
+    const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
+    using Sh = TlShape<MT>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Sh::kLds];
+    constexpr int kS = Sh::kStages;
+    uint8_t* const wring = lds;
+    uint8_t* const xring = lds + kS * kTlWSlot;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * kTlRows;
+    const int rows = min(kTlRows, N - n0);
+    const int G = K / 32, nwin = K / kTlWinK;
+    const uint32_t wrow = (uint32_t)K / 2u, srow = (uint32_t)G * 2u;
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * wrow, (uint32_t)rows * wrow);
+    const __amdgpu_buffer_rsrc_t ssrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow, (uint32_t)rows * srow);
+    const __amdgpu_buffer_rsrc_t bsrc =
+        make_rsrc(reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow, (uint32_t)rows * srow);
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+
+    // This wavefront's DMA: instructions wave + 16 u.
+    constexpr int kU = (Sh::kDma + kTlWaves - 1) / kTlWaves;
+    const int per_window = (Sh::kDma - wave + kTlWaves - 1) / kTlWaves;
+    uint32_t off[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int i = wave + kTlWaves * u;
+        if (i < kTlWDma - 2) {
+            const int q = 64 * i + lane, r = q >> 3, pc = (q & 7) ^ (r & 7);
+            off[u] = r < rows ? (uint32_t)r * wrow + 16u * (uint32_t)pc : kOob;
+        } else if (i < kTlWDma) {
+            off[u] = lane < rows ? (uint32_t)lane * srow : kOob;
+        } else {
+            const int q = 64 * (i - kTlWDma) + lane, m = q >> 5, c = (q & 31) ^ (m & 15);
+            off[u] = m < M ? (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)c : kOob;
+        }
+    }
+    auto issue = [&](int win) {
+        const int slot = win % kS;
+        uint8_t* const ws = wring + slot * kTlWSlot;
+        uint8_t* const xs = xring + slot * Sh::kXSlot;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = wave + kTlWaves * u;
+            if (i >= Sh::kDma) break;
+            if (i < kTlWDma - 2)
+                tl_dma16(wsrc, ws + 1024 * i, off[u] + (uint32_t)(kTlWRow * win));
+            else if (i == kTlWDma - 2)
+                tl_dma16(ssrc, ws + kTlWBytes, off[u] + 16u * (uint32_t)win);
+            else if (i == kTlWDma - 1)
+                tl_dma16(bsrc, ws + kTlWBytes + kTlSBytes, off[u] + 16u * (uint32_t)win);
+            else
+                tl_dma16(xsrc, xs + 1024 * (i - kTlWDma), off[u] + (uint32_t)(kTlXRow * win));
+        }
+    };
+    for (int win = 0; win < kS - 1 && win < nwin; ++win) issue(win);
+
+    const int t = wave / kTlParts, part = wave % kTlParts;
+    const int h = lane >> 5, n = lane & 31, row = 32 * t + n;
+    const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
+    // The lane's LDS read addresses in slot 0 (k-step u of the wavefront is
+    // 2 p + u, its word of the row wd = 2 (2 p + u) + h, its group p),
+    // kept whole in registers so that slot offsets fold into the instructions.
+    uint32_t wa[kTlSteps], xa[kTlSteps][MT], xa2[kTlSteps][MT];
+    const uint32_t sa = lds_addr(wring) + kTlWBytes + row * 16 + 2 * part;
+#pragma unroll
+    for (int u = 0; u < kTlSteps; ++u) {
+        const int wd = 2 * (kTlSteps * part + u) + h;
+        wa[u] = lds_addr(wring) + row * kTlWRow + 16 * ((wd >> 2) ^ (row & 7)) + 4 * (wd & 3);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            xa[u][mt] = lds_addr(xring) + (32 * mt + n) * kTlXRow + 16 * (wd ^ (n & 15));
+            xa2[u][mt] = xa[u][mt] + 2 * Sh::kXSlot;  // slot 2: past the 16-bit offset field when MT = 2
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kTlSteps; ++u) {
+        asm volatile("" : "+v"(wa[u]));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            asm volatile("" : "+v"(xa[u][mt]));
+            if (MT > 1) asm volatile("" : "+v"(xa2[u][mt]));
+        }
+    }
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+    // Window j in slot j % S (a constant: the loop below is unrolled by S).
+    auto step = [&](auto ws_c, int j) {
+        constexpr int WS = decltype(ws_c)::value, XS = WS;
+        // Windows j + 1 .. min(j + S - 2, nwin - 1) may still be in flight.
+        wait_vmcnt_rt(min(kS - 2, nwin - 1 - j) * per_window);
+        raw_barrier();
+        if (j + kS - 1 < nwin) issue(j + kS - 1);
+        // Every LDS read of the window first (one wait), then the decodes,
+        // then the matrix work.
+        uint32_t word[kTlSteps];
+        u32x4 aop[kTlSteps][MT];
+        const uint32_t sraw = lds_ld<uint16_t>(sa + WS * kTlWSlot);
+        const uint32_t braw = lds_ld<uint16_t>(sa + WS * kTlWSlot + kTlSBytes);
+#pragma unroll
+        for (int u = 0; u < kTlSteps; ++u) {
+            word[u] = lds_ld<uint32_t>(wa[u] + WS * kTlWSlot);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                aop[u][mt] = (MT > 1 && XS == 2) ? lds_ld<u32x4>(xa2[u][mt]) : lds_ld<u32x4>(xa[u][mt] + XS * Sh::kXSlot);
+        }
+        const float sc = bf16_bits_to_f32(sraw), bi = bf16_bits_to_f32(braw);
+        const float c = __builtin_fmaf(-1024.f, sc, bi), s16 = 0.0625f * sc, c16 = __builtin_fmaf(-64.f, sc, bi);
+        u32x4 bop[kTlSteps];
+#pragma unroll
+        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_bf16(word[u], sc, c, s16, c16, m_lo, m_hi, magic);
+#pragma unroll
+        for (int u = 0; u < kTlSteps; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aop[u][mt]),
+                                                                  __builtin_bit_cast(bf16x8, bop[u]), acc[mt], 0, 0, 0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    int j = 0;
+    if constexpr (kS == 6) {
+        for (; j + 5 < nwin; j += 6) {
+            step(I0{}, j);
+            step(I1{}, j + 1);
+            step(I2{}, j + 2);
+            step(I3{}, j + 3);
+            step(I4{}, j + 4);
+            step(I5{}, j + 5);
+        }
+        if (j < nwin) step(I0{}, j);
+        if (j + 1 < nwin) step(I1{}, j + 1);
+        if (j + 2 < nwin) step(I2{}, j + 2);
+        if (j + 3 < nwin) step(I3{}, j + 3);
+        if (j + 4 < nwin) step(I4{}, j + 4);
+    } else {
+        static_assert(kS == 3, "slot sequences for 6 and 3 slots");
+        for (; j + 2 < nwin; j += 3) {
+            step(I0{}, j);
+            step(I1{}, j + 1);
+            step(I2{}, j + 2);
+        }
+        if (j < nwin) step(I0{}, j);
+        if (j + 1 < nwin) step(I1{}, j + 1);
+    }
+    // The rings are free (every DMA landed before the last barrier, and the
+    // barrier below waits for every wavefront's last reads). Wavefront p of a
+    // tile owns accumulator registers 2 p, 2 p + 1 (of each x tile): it writes
+    // the other 14, then adds the seven partial sums of its own two.
+    raw_barrier();
+    float* const red = reinterpret_cast<float*>(lds);
+    // red[tile][writer][mt][slot][lane], 14 slots: writer q's register i (not
+    // its own 2 q, 2 q + 1) at slot i < 2 q ? i : i - 2.
+    static_assert(kTlTiles * kTlParts * MT * 14 * 64 * 4 <= Sh::kLds, "exchange area fits the rings");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((i >> 1) != part)
+                red[(((t * kTlParts + part) * MT + mt) * 14 + (i < 2 * part ? i : i - 2)) * 64 + lane] = acc[mt][i];
+    raw_barrier();
+    const int col = n0 + row;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int i = 2 * part + e;
+            // the wavefront's own partial sum of register i (a run-time index)
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v = r == i ? acc[mt][r] : v;
+#pragma unroll
+            for (int q = 0; q < kTlParts; ++q)
+                if (q != part) v += red[(((t * kTlParts + q) * MT + mt) * 14 + (i < 2 * q ? i : i - 2)) * 64 + lane];
+            // Lane (n, h) holds x rows 8 (i / 4) + 4 h + i % 4 of the tile, weight row n.
+            const int m = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (m < M && col < N) y[(size_t)m * N + col] = f32_to_bf16_bits(v);
+        }
+}
+
 }  // namespace w4mi
 
 using namespace w4mi;
@@ -895,8 +1173,20 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
         return fail(W4_EUNSUPPORTED, "qmm_affine4: implemented for K and N up to 2097152 (K=%lld N=%lld)", (long long)K,
                     (long long)N);
     hipStream_t s = as_stream(stream);
-    if (M <= kAffineBatchRows && K <= kAffineBatchMaxK) {
+    const bool tiles_ok = K % kTlWinK == 0 && ((uintptr_t)scales & 3u) == 0 && ((uintptr_t)biases & 3u) == 0;
+    if (M < kTlMinM && K <= kAffineBatchMaxK) {
         // A few rows: the GEMV form (each weight row read once for all of them).
+        launch_xlds(w, scales, biases, x, y, (int)M, (int)K, (int)N, s);
+    } else if (M <= 64 && tiles_ok) {
+        // Up to 64 rows: weight tiles streamed once through the matrix cores.
+        const dim3 grid((unsigned)((N + kTlRows - 1) / kTlRows));
+        if (M <= 32)
+            hipLaunchKernelGGL(qmm_affine4_tiles_kernel<1>, grid, dim3(kTlThreads), 0, s, w, scales, biases, x, y, (int)M,
+                               (int)K, (int)N);
+        else
+            hipLaunchKernelGGL(qmm_affine4_tiles_kernel<2>, grid, dim3(kTlThreads), 0, s, w, scales, biases, x, y, (int)M,
+                               (int)K, (int)N);
+    } else if (M <= kAffineBatchRows && K <= kAffineBatchMaxK) {
         launch_xlds(w, scales, biases, x, y, (int)M, (int)K, (int)N, s);
     } else if (M <= 64) {
         constexpr int BM = 64, BN = 128;
