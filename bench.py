@@ -10,9 +10,10 @@ K=N=4096, TFLOP/s), the lookup-codebook GEMM (M=512, K=4096, N=11008) and the
 single-precision lookup GEMM at 4 rows of x in both weight layouts, and the
 expert-routed Q4_0 MoE (64 experts, N=1408, K=2048, 128 tokens, top-8; and one
 decode token, top-8, on the mat-vec route, plain and with the fused SwiGLU
-activation), each with its roofline fraction, plus the CPU oracle timed on a
-bounded sample. --only small times qmm_affine4 at M = 2..64 on the decode
-weights (not part of the default line).
+activation), and qmm_affine4 with 32 rows of x on the decode weights (the
+small-batch weight-tile form), each with its roofline fraction, plus the CPU
+oracle timed on a bounded sample. --only small times qmm_affine4 at
+M = 2..64 on the decode weights.
 
 Launches are captured in HIP graphs (torch.cuda.CUDAGraph over the library's
 own launches on the capture stream) and replayed, so the host-side cost of a
@@ -41,14 +42,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "500af2f7dc0eccda", 36831109 + 57344),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "be2285be2ab1dacd", 100826021 + 16802611),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "be2285be2ab1dacd", 81613943 + 11291443),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123741520 + 5767168),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 13134025 + 45089),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 14099597 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 26034603 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 113361840 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "500af2f7dc0eccda", 36831260 + 57348),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "49ba97b3bd272815", 100809793 + 16799747),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "49ba97b3bd272815", 81624846 + 11291116),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "49ba97b3bd272815", 39070678 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123767910 + 5767168),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 13134031 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 14099603 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 26034615 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 113361885 + 176128),
 }
 
 
@@ -57,6 +59,8 @@ def traffic(name: str):
     import hashlib
     import os
 
+    if name not in TRAFFIC:
+        return None
     sources, digest, nbytes = TRAFFIC[name]
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_bit_w4_amd", "csrc")
     h = hashlib.sha256()
@@ -325,6 +329,25 @@ def main():
         result["moe_swiglu_decode"] = {"ms": ms, "GBps": wbytes6 / (ms * 1e-3) / 1e9, "launches": n6}
         del w6, x6, sets, out6, scratch6, g7, u7
 
+    # ------------------------------------------------------------ small batch (32 rows of x)
+    if args.only is None:
+        # qmm_affine4 with 32 rows of x on the decode weights: the weight-tile form.
+        ncopy = rotation(wbytes2)
+        ws = [to_dev(c2["w"].view(np.int32))]
+        ss = [to_dev(c2["scales"].view(np.int16), torch.bfloat16)]
+        bs = [to_dev(c2["biases"].view(np.int16), torch.bfloat16)]
+        for _ in range(ncopy - 1):
+            ws.append(ws[0].clone())
+            ss.append(ss[0].clone())
+            bs.append(bs[0].clone())
+        xs = to_dev(np.random.default_rng(7).standard_normal((32, K)).astype(np.float32)).to(torch.bfloat16)
+        ys = torch.empty((32, N), dtype=torch.bfloat16, device=dev)
+        log(f"small batch: qmm_affine4 M=32 K={K} N={N}, {ncopy} weight copies, 600 launches")
+        ms = timer.run(lambda i: B.qmm_affine4(ws[i % ncopy], ss[i % ncopy], bs[i % ncopy], xs, ys), 600, 30,
+                       chunk=ncopy * 4)
+        result["small32"] = {"ms": ms, "GBps": wbytes2 / (ms * 1e-3) / 1e9}
+        del ws, ss, bs, xs, ys
+
     # ------------------------------------------------------------ small batches (on request only)
     if args.only == "small":
         # qmm_affine4 with a few rows of x on the decode weights (not part of the default line).
@@ -439,6 +462,13 @@ def main():
                 "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
                 "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic(f"lut_f32_t{t8}")}}
+    if "small32" in result:
+        p = result["small32"]
+        comps["small_batch_gemm"] = {
+            "workload": f"qmm_affine4 M=32 K={K} N={N} (decode weights, weight-tile form)",
+            "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("small32")}}
     if "small" in result:
         comps["affine_small_batch"] = {"workload": f"qmm_affine4 M=2..64 K={K} N={N} (decode weights)",
                                        "unit": "GB/s weights", "points": result["small"]}
