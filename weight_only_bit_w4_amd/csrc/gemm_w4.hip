@@ -954,9 +954,9 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
 
 // DMA instruction i of a window (issued by wavefront i % 16), lane l:
 //   i < 8: packed weights, 16-byte piece q = 64 i + l of the slot: row q / 8,
-//          slot position q % 8 holding the row's piece (q % 8) ^ (row % 8)
-//          (the swizzle spreads the 32-row word reads of a k-step over the
-//          banks);
+//          slot position q % 8 holding the row's piece (q % 8) ^ ((row / 2) % 8)
+//          (rows are 128 bytes, half the banks: with the swizzle the 32 rows'
+//          word reads of a k-step fall on 32 different banks, 2-way at most);
 //   i = 8, 9: the 64 rows' 16 bytes of scales, of biases;
 //   i >= 10: x, piece q = 64 (i - 10) + l: row q / 32, slot position q % 32
 //          holding chunk (q % 32) ^ (row % 16).
@@ -995,7 +995,7 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
     for (int u = 0; u < kU; ++u) {
         const int i = wave + kTlWaves * u;
         if (i < kTlWDma - 2) {
-            const int q = 64 * i + lane, r = q >> 3, pc = (q & 7) ^ (r & 7);
+            const int q = 64 * i + lane, r = q >> 3, pc = (q & 7) ^ ((r >> 1) & 7);
             off[u] = r < rows ? (uint32_t)r * wrow + 16u * (uint32_t)pc : kOob;
         } else if (i < kTlWDma) {
             off[u] = lane < rows ? (uint32_t)lane * srow : kOob;
@@ -1035,7 +1035,7 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
 #pragma unroll
     for (int u = 0; u < kTlSteps; ++u) {
         const int wd = 2 * (kTlSteps * part + u) + h;
-        wa[u] = lds_addr(wring) + row * kTlWRow + 16 * ((wd >> 2) ^ (row & 7)) + 4 * (wd & 3);
+        wa[u] = lds_addr(wring) + row * kTlWRow + 16 * ((wd >> 2) ^ ((row >> 1) & 7)) + 4 * (wd & 3);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             xa[u][mt] = lds_addr(xring) + (32 * mt + n) * kTlXRow + 16 * (wd ^ (n & 15));
