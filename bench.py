@@ -43,10 +43,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # as null once those sources change.
 TRAFFIC = {
     "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "500af2f7dc0eccda", 36831260 + 57348),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "49ba97b3bd272815", 100809793 + 16799747),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "49ba97b3bd272815", 81624846 + 11291116),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "49ba97b3bd272815", 39070678 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123767910 + 5767168),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 100809736 + 16800123),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 81624874 + 11291098),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 39070400 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123933311 + 5767168),
     "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 13134031 + 45088),
     "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 14099603 + 45056),
     "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 26034615 + 176128),
