@@ -223,6 +223,8 @@ def test_qmm_lut4_small(M, K, N, block):
     (3, 100, 70, 6),       # blocks straddle rows: element-by-element form
     (130, 64, 256, 16),    # more than 128 rows of x: 33 row groups of 4
     (2, 5000, 40, 10),     # K split over 16 wavefronts with a ragged last range
+    (5, 1000, 200, 8),     # dword form: a partial last 64-column group, ragged K
+    (4, 4096, 11008, 64),  # dword form on the LUT workload's weights
 ])
 def test_qmm_lut4_weight_stored_k_by_n(M, K, N, block):
     # Half-precision path with transpose == 0 (W stored [K, N], flat = k * N + n).
@@ -418,6 +420,12 @@ def _lut_f32_case(M, K, N, block, transpose, seed):
     (5, 520, 72, 8, 1),          # aligned [N, K] form: 65 groups of 8 (a partial 64-lane step)
     (6, 72, 260, 4, 0),          # aligned [K, N] form: 3 column groups of 128, the last partial
     (1, 4096, 11008, 64, 0),     # one row, [K, N], the LUT workload's weights
+    # [K, N] dword form (block % 8 == 0, N % block == 0): 64-column groups, 128-row chunks
+    (5, 1000, 72, 8, 0),         # a partial last group, K not a multiple of the chunk, 2 row groups
+    (9, 300, 4128, 32, 0),       # 65 groups: the XCD numbering's unused workgroups
+    (3, 17, 64, 64, 0),          # one chunk: only the first wavefront has rows
+    (4, 3000, 128, 64, 0),       # 24 chunks over 16 wavefronts (2 each for 12, none for 4)
+    (2, 2304, 11008, 16, 0),     # 18 chunks over 16 wavefronts (2 each for 9)
 ])
 def test_qmm_lut4_f32(M, K, N, block, transpose):
     x, packed, scales, book = _lut_f32_case(M, K, N, block, transpose, seed=M + K + N)

@@ -19,6 +19,8 @@
 //  - [K, N]: lane l owns column n0 + l; 16 wavefronts split K into contiguous
 //    ranges; x[m][k] is the same for every lane (scalar loads); the 16
 //    wavefronts' sums meet in LDS and are added in K order, compensated.
+//    When every dword of codes lies in one block, a dword form reads one dword
+//    (8 columns) per lane instead (lut4_kn8_kernel, below).
 // Rows of x are taken 4 at a time (the grid's y dimension). Aligned shapes
 // (8 codes along the contiguous axis within one block; [K, N] with N a
 // multiple of the block) read a dword or a byte of codes and one scale at a
@@ -447,6 +449,191 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols2_kernel(const
             }
     }
 }
+
+// [K, N] with block % 8 == 0 and N % block == 0: each dword of codes holds 8
+// consecutive columns of one k row under one scale. A workgroup owns 8D
+// columns (D dwords of each row) for all of K; in each step lane l reads
+// dword l % D of row l / D, so one load instruction covers 64 / D rows. The
+// workgroups that share a 128-byte line of a row are numbered so that they run
+// on one XCD at the same time and the line is fetched once into its L2.
+// Wavefronts split K into contiguous ranges of whole 16-step chunks. For each
+// chunk a wavefront stages x in its own LDS region as [k][m] (16 bytes per k),
+// loads the chunk's 16 code dwords and scales, and sums the lane's 16 products
+// of each of its 32 outputs (8 columns x 4 rows of x). The 64 / D lanes that
+// hold the same outputs then reduce-scatter them, so that each lane ends with
+// the chunk's sums of D / 2 outputs, which it adds to its running totals with
+// compensation. At the end the lanes' and then the wavefronts' totals are
+// merged as (sum, error) pairs, the wavefronts in K order.
+// The group width is a trade: every workgroup makes one L2 request per k row
+// for its codes and one for its scale, so narrow groups multiply the requests
+// (16 columns: twice as slow as 64 at M = 4, K = 4096, N = 11008), while wide
+// groups leave CUs idle (64 columns: 172 workgroups there).
+constexpr int kKnWaves = 16;  // wavefronts per workgroup, splitting K
+constexpr int kKnDwords = 8;  // code dwords per row per workgroup: 64 columns
+
+// (hi, lo) += (bhi, blo), the rounding error of hi + bhi kept in lo (Knuth's
+// two-sum); a non-finite sum carries no error term.
+__device__ __forceinline__ void two_sum_merge(float& hi, float& lo, float bhi, float blo) {
+    const float s = hi + bhi;
+    const float bb = s - hi;
+    const float err = (hi - (s - bb)) + (bhi - bb);
+    lo = __builtin_isfinite(s) ? lo + blo + err : 0.f;
+    hi = s;
+}
+
+template <bool H, int D>
+__global__ __launch_bounds__(kKnWaves * 64, 4) void lut4_kn8_kernel(const typename LutIO<H>::X* __restrict__ x,
+                                                                     const uint8_t* __restrict__ packed,
+                                                                     const typename LutIO<H>::S* __restrict__ scales,
+                                                                     LutBook book, typename LutIO<H>::Y* __restrict__ y,
+                                                                     int M, int K, int N, int block, int groups) {
+    using IO = LutIO<H>;
+    constexpr int R = 64 / D;           // rows per step; lanes that share outputs
+    constexpr int CH = 16 * R;          // rows per chunk
+    constexpr int S = 32 / D;           // workgroups per 128-byte line of a row
+    constexpr int NO = 8 * kF32M;       // outputs per lane in a step
+    constexpr int KEEP = NO / R;        // outputs each lane keeps after the reduce-scatter
+    static_assert(D == 1 || D == 2 || D == 4 || D == 8, "1, 2, 4 or 8 dwords per row");
+    // Workgroup b runs on XCD b % 8; the S groups of one line get consecutive
+    // b / 8 on the same XCD.
+    const int b = blockIdx.x;
+    const int g = S * (8 * (b / (8 * S)) + b % 8) + (b / 8) % S;
+    if (g >= groups) return;  // the whole workgroup
+    __shared__ float book_s[16];
+    __shared__ __attribute__((aligned(16))) float xs[kKnWaves][CH][kF32M];
+    __shared__ float red[kKnWaves][2][D * NO];
+    if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane % D, r = lane / D;
+    const int n0 = g * 8 * D + 8 * j;
+    const bool nv = n0 < N;  // N % 8 == 0: all 8 columns or none
+    const int m0 = blockIdx.y * kF32M;
+    const int chunks = (K + CH - 1) / CH, per_wave = (chunks + kKnWaves - 1) / kKnWaves;
+    const int cb = min(chunks, wave * per_wave), ce = min(chunks, cb + per_wave);
+    // Buffer loads return zero past the end of their buffer, which covers rows
+    // at or past K of the codes and scales and rows of x at or past M; lanes
+    // past N, and x columns at or past K, take an offset past every end.
+    constexpr uint32_t kOut = 0x80000000u;
+    constexpr uint32_t XB = sizeof(typename IO::X), SB = sizeof(typename IO::S);
+    const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(packed, (uint32_t)((int64_t)K * N / 2));
+    const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales, (uint32_t)((int64_t)K * (N / block) * SB));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)((int64_t)M * K * XB));
+    const uint32_t wrow = (uint32_t)N / 2, srow = (uint32_t)(N / block) * SB;  // bytes per k row
+    const uint32_t wcol = nv ? 4u * (uint32_t)(n0 >> 3) : kOut, scol = nv ? (uint32_t)(n0 / block) * SB : kOut;
+    // After the reduce-scatter lane r keeps outputs o0 .. o0 + KEEP - 1 of its
+    // 32 (output o = column 8j + o / 4, row of x m0 + o % 4): at the level
+    // that pairs lanes r and r ^ 2^t it keeps the upper half of what remains
+    // when bit t of r is set.
+    int o0 = 0;
+#pragma unroll
+    for (int t = 0, h = NO / 2; h >= KEEP; ++t, h /= 2) o0 += ((r >> t) & 1) ? h : 0;
+    float acc[KEEP], cor[KEEP];
+#pragma unroll
+    for (int e = 0; e < KEEP; ++e) acc[e] = cor[e] = 0.f;
+    float* xw = &xs[wave][0][0];
+    for (int ch = cb; ch < ce; ++ch) {
+        const int kc = ch * CH;
+        // x for rows [kc, kc + CH) of the chunk, zero past K or M.
+        f32x4 xin[CH / 64];
+#pragma unroll
+        for (int u = 0; u < CH / 64; ++u) {
+            const int k = kc + lane + 64 * u;
+            const uint32_t xo = k < K ? ((uint32_t)m0 * K + k) * XB : kOut;
+#pragma unroll
+            for (int m = 0; m < kF32M; ++m) {
+                const uint32_t off = xo + (uint32_t)(m * K) * XB;
+                if constexpr (H)
+                    xin[u][m] = IO::x(__builtin_amdgcn_raw_buffer_load_b16(xsrc, off, 0, 0));
+                else
+                    xin[u][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xsrc, off, 0, 0));
+            }
+        }
+        uint32_t word[16];
+        float sc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t k = (uint32_t)(kc + i * R + r);
+            word[i] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, k * wrow + wcol, 0, 0);
+            if constexpr (H)
+                sc[i] = IO::s(__builtin_amdgcn_raw_buffer_load_b16(ssrc, k * srow + scol, 0, 0));
+            else
+                sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ssrc, k * srow + scol, 0, 0));
+        }
+        // The previous chunk's LDS reads are done before its rows are written.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < CH / 64; ++u) *reinterpret_cast<f32x4*>(xw + (lane + 64 * u) * kF32M) = xin[u];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float part[NO];
+#pragma unroll
+        for (int o = 0; o < NO; ++o) part[o] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const f32x4 xv = *reinterpret_cast<const f32x4*>(xw + (i * R + r) * kF32M);
+            // Byte t of the dword holds columns 2t (high nibble) and 2t + 1.
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t code = (word[i] >> (8 * (c / 2) + ((c & 1) ? 0 : 4))) & 15u;
+                const float w = IO::w(book_s[code] * sc[i]);
+#pragma unroll
+                for (int m = 0; m < kF32M; ++m) part[c * kF32M + m] = __builtin_fmaf(xv[m], w, part[c * kF32M + m]);
+            }
+        }
+        // Reduce-scatter over the R lanes r (lane distance D * 2^t at level t).
+#pragma unroll
+        for (int t = 0, h = NO / 2; h >= KEEP; ++t, h /= 2) {
+            // All ones where this lane keeps the upper half; the halves are
+            // picked by bits (a conditional pick of two array elements turns
+            // into a run-time index into the whole array).
+            const uint32_t up = ((r >> t) & 1) ? ~0u : 0u;
+#pragma unroll
+            for (int e = 0; e < h; ++e) {
+                const uint32_t lo = __builtin_bit_cast(uint32_t, part[e]), hi = __builtin_bit_cast(uint32_t, part[e + h]);
+                const float send = __builtin_bit_cast(float, (lo & up) | (hi & ~up));
+                const float keep = __builtin_bit_cast(float, (hi & up) | (lo & ~up));
+                part[e] = keep + __shfl_xor(send, D << t, 64);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < KEEP; ++e) kahan_add(acc[e], cor[e], part[e]);
+    }
+    // The wavefront's totals: lane (j, r) holds outputs o0 .. o0 + KEEP - 1 of
+    // column group j.
+#pragma unroll
+    for (int e = 0; e < KEEP; ++e) {
+        red[wave][0][j * NO + o0 + e] = acc[e];
+        red[wave][1][j * NO + o0 + e] = -cor[e];  // kahan_add keeps the negated error
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < D * NO; t += kKnWaves * 64) {
+        float hi = red[0][0][t], lo = red[0][1][t];
+        for (int v = 1; v < kKnWaves; ++v) two_sum_merge(hi, lo, red[v][0][t], red[v][1][t]);  // K order
+        const int o = t % NO, m = o % kF32M, col = g * 8 * D + (t / NO) * 8 + o / kF32M;
+        if (col < N && m0 + m < M) y[(size_t)(m0 + m) * N + col] = IO::y(hi + lo);
+    }
+}
+
+// The dword form's conditions: 8 columns of a dword share a block, packed
+// dword-aligned, and every buffer offset it forms (up to one chunk past K, and
+// the out-of-range marker added to any of them) fits in 32 bits.
+inline bool kn8_ok(const void* packed, int64_t M, int64_t K, int64_t N, int32_t block, int64_t xb, int64_t sb) {
+    const int64_t lim = int64_t(1) << 31, kk = K + 256;
+    return N % block == 0 && block % 8 == 0 && ((uintptr_t)packed & 3u) == 0 && kk * (N / 2) < lim &&
+           kk * (N / block) * sb < lim && M * K * xb < lim;
+}
+
+template <bool H, int D>
+void launch_lut4_kn8(const typename LutIO<H>::X* x, const uint8_t* packed, const typename LutIO<H>::S* scales,
+                     const LutBook& b, typename LutIO<H>::Y* y, int64_t M, int64_t K, int64_t N, int32_t block,
+                     hipStream_t s) {
+    const int groups = (int)((N + 8 * D - 1) / (8 * D));
+    const int per = 8 * (32 / D);  // the numbering works in whole sets of 8 XCDs x S groups
+    const dim3 grid((unsigned)((groups + per - 1) / per * per), (unsigned)((M + kF32M - 1) / kF32M));
+    hipLaunchKernelGGL((lut4_kn8_kernel<H, D>), grid, dim3(kKnWaves * 64), 0, s, x, packed, scales, b, y, (int)M,
+                       (int)K, (int)N, (int)block, groups);
+}
 }  // namespace w4mi
 
 using namespace w4mi;
@@ -471,6 +658,8 @@ extern "C" w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const f
         else
             hipLaunchKernelGGL(lut4_f32_rows_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y,
                                (int)M, (int)K, (int)N, (int)block);
+    } else if (kn8_ok(packed, M, K, N, block, 4, 4)) {
+        launch_lut4_kn8<false, kKnDwords>(x, packed, scales, b, y, M, K, N, block, s);
     } else if (N % block == 0) {
         const dim3 grid((unsigned)((N + 63) / 64), my);
         hipLaunchKernelGGL((lut4_f32_cols2_kernel<false, 1>), grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b,
@@ -492,7 +681,9 @@ void launch_lut4_kn_f16(const uint16_t* x, const uint8_t* packed, const uint16_t
     LutBook b;
     for (int i = 0; i < 16; ++i) b.v[i] = book[i];
     const unsigned my = (unsigned)((M + kF32M - 1) / kF32M);
-    if (N % block == 0) {
+    if (kn8_ok(packed, M, K, N, block, 2, 2)) {
+        launch_lut4_kn8<true, kKnDwords>(x, packed, scales, b, y, M, K, N, block, s);
+    } else if (N % block == 0) {
         const dim3 grid((unsigned)((N + 63) / 64), my);
         hipLaunchKernelGGL((lut4_f32_cols2_kernel<true, 1>), grid, dim3(kF32ColWaves * 64), 0, s, x, packed, scales, b,
                            y, (int)M, (int)K, (int)N, (int)block);
