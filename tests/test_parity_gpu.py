@@ -418,6 +418,8 @@ def _lut_f32_case(M, K, N, block, transpose, seed):
     (130, 48, 20, 16, 1),        # more than 128 rows: 33 row groups of 4
     (2, 5000, 40, 10, 0),        # 16 wavefronts over K = 5000 with blocks across rows
     (5, 520, 72, 8, 1),          # aligned [N, K] form: 65 groups of 8 (a partial 64-lane step)
+    (3, 960, 40, 24, 1),         # aligned [N, K], block / 8 = 3 (not a power of two), a partial step
+    (2, 1536, 48, 64, 1),        # aligned [N, K]: 3 full steps (a pair and an odd last one)
     (6, 72, 260, 4, 0),          # aligned [K, N] form: 3 column groups of 128, the last partial
     (1, 4096, 11008, 64, 0),     # one row, [K, N], the LUT workload's weights
     # [K, N] dword form (block % 8 == 0, N % block == 0): 64-column groups, 128-row chunks

@@ -225,19 +225,30 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const 
 // When each 8 consecutive codes along the contiguous axis share one block
 // (block % 8 == 0 and the contiguous length a multiple of block), a lane reads
 // 8 codes (one dword) and one scale at a time and looks the codes up in an LDS
-// copy of the codebook.
-__device__ __forceinline__ void lut_decode8(uint32_t word, float s, const float* book_s, float (&w)[8]) {
-    // Byte i holds flat indices 2i (high nibble) and 2i + 1 (low nibble).
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t byte = (word >> (8 * i)) & 0xFFu;
-        w[2 * i] = book_s[byte >> 4] * s;
-        w[2 * i + 1] = book_s[byte & 15u] * s;
-    }
+// copy of the codebook. Byte t of the dword holds flat indices 2t (high
+// nibble) and 2t + 1 (low nibble); the lookup offsets are taken as bytes of two
+// masked copies of the dword, (word >> 2) and (word << 2) masked to 4 x code,
+// hidden from the compiler, which would otherwise fold each pick back into a
+// shift and a mask of the word.
+__device__ __forceinline__ void lut_offsets(uint32_t word, uint32_t& hi4, uint32_t& lo4) {
+    hi4 = (word >> 2) & 0x3C3C3C3Cu;
+    lo4 = (word << 2) & 0x3C3C3C3Cu;
+    asm("" : "+v"(hi4), "+v"(lo4));
+}
+// Codebook entry of column c (0..7) of a dword whose offsets are hi4 / lo4.
+__device__ __forceinline__ float lut_entry(const float* book_s, uint32_t hi4, uint32_t lo4, int c) {
+    const uint32_t off = (((c & 1) ? lo4 : hi4) >> (8 * (c / 2))) & 0xFFu;
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(book_s) + off);
 }
 
 // [N, K], K % block == 0, block % 8 == 0: a wavefront owns 4 weight rows, lane
 // l takes the 8-wide K groups l, l + 64, ... (one dword of codes per row).
+// Steps of 64 whole groups run without checks, a last partial step reads the
+// groups at or past K / 8 as zeros; rows at or past N (or M) are read as the
+// last row and not written. The codes, scales and x come through buffer loads
+// whose row offset is a scalar, and the next step's are loaded before this
+// step's are used. P2: block / 8 is a power of two.
+template <bool P2>
 __global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows8_kernel(const float* __restrict__ x,
                                                                              const uint8_t* __restrict__ packed,
                                                                              const float* __restrict__ scales,
@@ -246,79 +257,121 @@ __global__ __launch_bounds__(kF32RowWaves * 64) void lut4_f32_rows8_kernel(const
     __shared__ float book_s[16];
     if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = (blockIdx.x * kF32RowWaves + wave) * kF32Rows;
     const int m0 = blockIdx.y * kF32M;
-    const int G8 = K / 8, bpr = K / block;  // 8-wide groups and blocks per row
-    const int per8 = block / 8;
+    const int G8 = K / 8, bpr = K / block, per8 = block / 8;  // 8-wide groups and blocks per row
+    const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(packed, (uint32_t)((int64_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales, (uint32_t)((int64_t)N * bpr * 4));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)((int64_t)M * K * 4));
+    int wro[kF32Rows], sro[kF32Rows], xro[kF32M];  // byte offsets of the rows (uniform)
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r) {
+        const int n = min(nb + r, N - 1);
+        wro[r] = n * (K / 2);
+        sro[r] = n * bpr * 4;
+    }
+#pragma unroll
+    for (int m = 0; m < kF32M; ++m) xro[m] = min(m0 + m, M - 1) * K * 4;
     float acc[kF32Rows][kF32M], cor[kF32Rows][kF32M], part[kF32Rows][kF32M];
 #pragma unroll
     for (int r = 0; r < kF32Rows; ++r)
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) acc[r][m] = cor[r][m] = part[r][m] = 0.f;
-    const uint32_t* words = reinterpret_cast<const uint32_t*>(packed);
     // One step's operands: x (8 k of each row of x) and a dword of codes and a
-    // scale for each weight row. The next step's are loaded before this one
-    // is used.
+    // scale for each weight row.
     struct Step {
         f32x4 xa[kF32M], xb[kF32M];
         uint32_t word[kF32Rows];
         float sc[kF32Rows];
     };
-    auto load = [&](int g0, Step& st) {
+    // Block of group g within its row: g / per8, a shift when per8 is a power
+    // of two.
+    const int sh = __builtin_ctz((unsigned)per8);
+    // full: every lane's group is below K / 8 (no checks).
+    auto load = [&](auto full, int g0, Step& st) {
         const int g = g0 + lane;
-        const bool gv = g < G8;
+        const bool gv = decltype(full)::value || g < G8;
+        const int gc = gv ? g : G8 - 1;
+        const uint32_t gx = (uint32_t)gc, sq = (uint32_t)(P2 ? gc >> sh : gc / per8);
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) {
-            const bool v = gv && m0 + m < M;
-            const f32x4* xp = reinterpret_cast<const f32x4*>(x + (size_t)(m0 + m) * K + 8 * g);
-            st.xa[m] = v ? xp[0] : f32x4{0.f, 0.f, 0.f, 0.f};
-            st.xb[m] = v ? xp[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+            st.xa[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, 32u * gx, xro[m], 0));
+            st.xb[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xsrc, 32u * gx + 16u, xro[m], 0));
         }
 #pragma unroll
         for (int r = 0; r < kF32Rows; ++r) {
-            const int n = nb + r;
-            const bool v = gv && n < N;
-            st.word[r] = v ? words[(size_t)n * G8 + g] : 0u;
-            st.sc[r] = v ? scales[(size_t)n * bpr + g / per8] : 0.f;
+            st.word[r] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, 4u * gx, wro[r], 0);
+            st.sc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ssrc, 4u * sq, sro[r], 0));
+        }
+        if (!decltype(full)::value && !gv) {
+#pragma unroll
+            for (int m = 0; m < kF32M; ++m) st.xa[m] = st.xb[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < kF32Rows; ++r) {
+                st.word[r] = 0u;
+                st.sc[r] = 0.f;
+            }
         }
     };
-    Step cur, nxt;
-    load(0, cur);
-    int it = 0;
-    for (int g0 = 0; g0 < G8; g0 += 64) {
-        if (g0 + 64 < G8) load(g0 + 64, nxt);
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    auto use = [&](const Step& st) {
 #pragma unroll
         for (int r = 0; r < kF32Rows; ++r) {
-            float w[8];
-            lut_decode8(cur.word[r], cur.sc[r], book_s, w);
+            uint32_t hi4, lo4;
+            lut_offsets(st.word[r], hi4, lo4);
 #pragma unroll
             for (int m = 0; m < kF32M; ++m) {
                 float p = part[r][m];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) p = __builtin_fmaf(cur.xa[m][t], w[t], p);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) p = __builtin_fmaf(cur.xb[m][t], w[4 + t], p);
+                for (int t = 0; t < 8; ++t) {
+                    const float w = lut_entry(book_s, hi4, lo4, t) * st.sc[r];
+                    p = __builtin_fmaf(t < 4 ? st.xa[m][t] : st.xb[m][t - 4], w, p);
+                }
                 part[r][m] = p;
             }
         }
-        if (++it == kF32Tile / 8) {  // 16 products per lane and output per tile
-            it = 0;
+    };
+    auto close_tile = [&]() {
 #pragma unroll
-            for (int r = 0; r < kF32Rows; ++r)
+        for (int r = 0; r < kF32Rows; ++r)
 #pragma unroll
-                for (int m = 0; m < kF32M; ++m) {
-                    kahan_add(acc[r][m], cor[r][m], part[r][m]);
-                    part[r][m] = 0.f;
-                }
-        }
-        cur = nxt;
+            for (int m = 0; m < kF32M; ++m) {
+                kahan_add(acc[r][m], cor[r][m], part[r][m]);
+                part[r][m] = 0.f;
+            }
+    };
+    // Full steps in pairs, two operand sets in turn (no copies, no branches
+    // between loads and uses); each pair is one tile of 16 products per lane
+    // and output, added with compensation. The prefetch past the last full
+    // step rereads that step (in bounds, unused). Then an odd last full step
+    // and a partial step, one tile each.
+    const int nfull = G8 / 64;
+    Step s0, s1;
+    if (nfull > 0) load(Full{}, 0, s0);
+    int st = 0;
+    for (; st + 2 <= nfull; st += 2) {
+        load(Full{}, 64 * (st + 1), s1);
+        use(s0);
+        load(Full{}, 64 * min(st + 2, nfull - 1), s0);
+        use(s1);
+        close_tile();
+    }
+    if (st < nfull) {
+        use(s0);
+        close_tile();
+    }
+    if (64 * nfull < G8) {
+        load(Part{}, 64 * nfull, s1);
+        use(s1);
+        close_tile();
     }
 #pragma unroll
     for (int r = 0; r < kF32Rows; ++r)
 #pragma unroll
         for (int m = 0; m < kF32M; ++m) {
-            kahan_add(acc[r][m], cor[r][m], part[r][m]);
             float v = acc[r][m];
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -572,11 +625,19 @@ __global__ __launch_bounds__(kKnWaves * 64, 4) void lut4_kn8_kernel(const typena
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const f32x4 xv = *reinterpret_cast<const f32x4*>(xw + (i * R + r) * kF32M);
-            // Byte t of the dword holds columns 2t (high nibble) and 2t + 1.
+            // Byte t of the dword holds columns 2t (high nibble) and 2t + 1;
+            // each byte of hi4 / lo4 is 4 x the code, the LDS byte offset of
+            // its codebook entry.
+            uint32_t hi4 = (word[i] >> 2) & 0x3C3C3C3Cu, lo4 = (word[i] << 2) & 0x3C3C3C3Cu;
+            // Opaque to the compiler, which would otherwise fold each byte
+            // pick back into a shift and a mask of the word (two operations
+            // per code instead of one byte extract).
+            asm("" : "+v"(hi4), "+v"(lo4));
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const uint32_t code = (word[i] >> (8 * (c / 2) + ((c & 1) ? 0 : 4))) & 15u;
-                const float w = IO::w(book_s[code] * sc[i]);
+                const uint32_t off = (((c & 1) ? lo4 : hi4) >> (8 * (c / 2))) & 0xFFu;
+                const float bk = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(book_s) + off);
+                const float w = IO::w(bk * sc[i]);
 #pragma unroll
                 for (int m = 0; m < kF32M; ++m) part[c * kF32M + m] = __builtin_fmaf(xv[m], w, part[c * kF32M + m]);
             }
@@ -652,12 +713,19 @@ extern "C" w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const f
     const unsigned my = (unsigned)((M + kF32M - 1) / kF32M);
     if (transpose) {
         const dim3 grid((unsigned)((N + kF32RowWaves * kF32Rows - 1) / (kF32RowWaves * kF32Rows)), my);
-        if (block % 8 == 0 && K % block == 0 && ((uintptr_t)packed & 3u) == 0 && ((uintptr_t)x & 15u) == 0)
-            hipLaunchKernelGGL(lut4_f32_rows8_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y,
-                               (int)M, (int)K, (int)N, (int)block);
-        else
+        const int64_t lim = int64_t(1) << 31;  // buffer offsets of the dword form fit in 31 bits
+        if (block % 8 == 0 && K % block == 0 && ((uintptr_t)packed & 3u) == 0 && ((uintptr_t)x & 15u) == 0 &&
+            N * (K / 2) < lim && N * (K / block) * 4 < lim && M * K * 4 < lim) {
+            if (((block / 8) & (block / 8 - 1)) == 0)
+                hipLaunchKernelGGL(lut4_f32_rows8_kernel<true>, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales,
+                                   b, y, (int)M, (int)K, (int)N, (int)block);
+            else
+                hipLaunchKernelGGL(lut4_f32_rows8_kernel<false>, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales,
+                                   b, y, (int)M, (int)K, (int)N, (int)block);
+        } else {
             hipLaunchKernelGGL(lut4_f32_rows_kernel, grid, dim3(kF32RowWaves * 64), 0, s, x, packed, scales, b, y,
                                (int)M, (int)K, (int)N, (int)block);
+        }
     } else if (kn8_ok(packed, M, K, N, block, 4, 4)) {
         launch_lut4_kn8<false, kKnDwords>(x, packed, scales, b, y, M, K, N, block, s);
     } else if (N % block == 0) {
