@@ -46,11 +46,11 @@ TRAFFIC = {
     "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 100809736 + 16800123),
     "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 81624874 + 11291098),
     "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 39070400 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123933311 + 5767168),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123876020 + 5767168),
     "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 13134031 + 45088),
     "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 14099603 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 26034615 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "6f8aaf533b20a294", 113361885 + 176128),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "b7d0ed61d3475eed", 26047904 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "b7d0ed61d3475eed", 44816623 + 176128),
 }
 
 

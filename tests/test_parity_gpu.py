@@ -280,6 +280,8 @@ def _max_d(c):
     (8, 200, 320, 40, 3),    # K not a multiple of the 256 window
     (16, 96, 256, 32, 9),    # 32 tokens but 288 routed rows: past the mat-vec id scan
     (2500, 16, 64, 40, 2),   # more experts than grouping threads: 3 experts per scan segment
+    (16, 64, 128, 288, 8),   # 2304 routed rows, 144 per expert: five passes of 32
+    (5, 64, 128, 461, 5),    # 2305 routed rows over 5 experts: a last pass of 1 row for some
     # mat-vec route (at most 32 tokens)
     (4, 40, 128, 3, 2),      # tiny, N not a multiple of the 32-row tile
     (8, 200, 320, 9, 3),     # 10 blocks: a ragged first chunk
@@ -296,7 +298,7 @@ def test_qmm_id_q4_0_small(E, N, K, T, top_k):
     assert scratch[:4].view(torch.int32).item() == 0
 
 
-@pytest.mark.parametrize("T", [5, 40])  # mat-vec route, grouped GEMM route
+@pytest.mark.parametrize("T", [5, 40, 800])  # mat-vec route, grouped GEMM (few and many rows per expert)
 def test_qmm_id_q4_0_duplicate_and_out_of_range_ids(T):
     c = synth.moe_case(4, 32, 64, T, 3, seed=31)
     ids = c["ids"].copy()
