@@ -128,3 +128,51 @@ def test_points_match_full_and_brute_force():
     exact = sum(terms)
     assert abs(acc[m, n] - float(exact)) <= K * 2.0**-53 * float(sum(abs(t) for t in terms))
     assert y[m, n] == np.float16(np.float32(float(exact))).view(np.uint16)
+
+
+def test_single_precision_routine_reproduces_the_worked_example():
+    """lut4_f32 (the single-precision path's reference) on the page's worked example, both
+    layouts: the exact dyadic rows of tests/golden/lut4_worked_example.json."""
+    g = json.load(open(GOLDEN))
+    book = np.array([i * i / 32.0 for i in range(16)], np.float32)
+    rows, cols, block = g["rows"], g["cols"], g["block"]
+    for case in g["cases"]:
+        packed = np.full(g["packed_len"], case["byte"], np.uint8)
+        scales = np.array([case["scale"]], np.float32)
+        for transpose, key in ((False, "non_transposed"), (True, "transposed")):
+            K, N = (cols, rows) if transpose else (rows, cols)
+            x = np.full((g["x_rows"], K), g["x_value"], np.float32)
+            _, y = oracle.lut4_f32(x, packed, scales, book, g["x_rows"], K, N, block, transpose)
+            want = np.array([num / den for num, den in case[key]], np.float32)
+            for r in range(g["x_rows"]):
+                assert np.array_equal(y[r], want), (case["byte"], key, y[r], want)
+
+
+@pytest.mark.parametrize("transpose", [True, False])
+def test_single_precision_routine_exact_integers_non_square(transpose):
+    """book[i] = i, scale 1, integer x: y must equal the integer product with the weight read
+    in the stated layout (rows N, cols K when transposed, else rows K, cols N). K != N, so a
+    swapped layout or transposition fails."""
+    rng = np.random.default_rng(10)
+    M, K, N, block = 3, 24, 10, 8
+    packed = rng.integers(0, 256, N * K // 2, dtype=np.uint16).astype(np.uint8)
+    codes = np.array([(int(packed[i // 2]) >> 4) if i % 2 == 0 else (int(packed[i // 2]) & 15)
+                      for i in range(N * K)], np.int64)
+    xi = rng.integers(-3, 4, size=(M, K))
+    book = np.arange(16, dtype=np.float32)
+    scales = np.ones(N * K // block, np.float32)
+    acc, y = oracle.lut4_f32(xi.astype(np.float32), packed, scales, book, M, K, N, block, transpose)
+    Wi = codes.reshape(N, K) if transpose else codes.reshape(K, N).T
+    want = xi @ Wi.T
+    assert np.array_equal(acc, want.astype(np.float64))
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+def test_single_precision_routine_keeps_the_weight_unrounded():
+    """A product book[c] * scale that binary16 cannot hold must reach the sum unrounded."""
+    book = np.full(16, 1.0 + 2.0**-20, np.float32)     # not representable in binary16
+    packed = np.zeros(4, np.uint8)
+    scales = np.array([1.0], np.float32)
+    x = np.ones((1, 8), np.float32)
+    acc, _ = oracle.lut4_f32(x, packed, scales, book, 1, 8, 1, 8, True)
+    assert acc[0, 0] == 8 * float(np.float32(1.0 + 2.0**-20))

@@ -193,3 +193,44 @@ def test_swiglu_brute_force_and_degenerate_inputs():
     assert np.array_equal(out, acc.astype(np.float32))
     zero, _ = oracle.moe_swiglu_q4_0(gate, np.zeros_like(up), c["w"], c["ids"], rows, 5, 64, 4, c["expert_stride"])
     assert np.all(zero == 0.0)
+
+
+# ---------------------------------------------------------------- point form
+def test_points_equal_exact_integers_with_several_slots_and_a_bad_id():
+    """moe_q4_0_points (the reference for sampled checks at the MoE workload's size) against
+    exact integer arithmetic: d = 1, integer x, so every routed row must equal
+    sum_k x[r // top_k][k] * (q - 8) of expert ids[r]. n_tokens != top_k, so taking the
+    token as r % top_k (or the slot as the expert) gives different numbers; one id is out
+    of range and must give 0."""
+    rng = np.random.default_rng(7)
+    E, N, K, T, top_k = 5, 6, 96, 4, 3
+    qs = rng.integers(0, 256, size=(E, N, K // 32, 16), dtype=np.uint16).astype(np.uint8)
+    d_one = np.broadcast_to(np.array([0x00, 0x3C], np.uint8), (E, N, K // 32, 2))
+    w = np.concatenate([d_one, qs], axis=3).reshape(-1)
+    xi = rng.integers(-3, 4, size=(T, K))
+    ids = rng.integers(0, E, size=T * top_k).astype(np.uint32)
+    ids[4] = E + 2                                     # out of range
+    lo = (qs & 15).astype(np.int64)
+    hi = (qs >> 4).astype(np.int64)
+    Wq = np.concatenate([lo, hi], axis=3).reshape(E, N, K) - 8
+    rs = np.repeat(np.arange(T * top_k), N)
+    ns = np.tile(np.arange(N), T * top_k)
+    pick = rng.permutation(rs.size)[:40]
+    rs, ns = np.concatenate([rs[pick], [4, 4]]), np.concatenate([ns[pick], [0, N - 1]])
+    acc = oracle.moe_q4_0_points(xi.astype(np.float32), w, ids, top_k, K, E, N * (K // 32) * 18, rs, ns)
+    for i, (r, n) in enumerate(zip(rs, ns)):
+        e, t = int(ids[r]), int(r) // top_k
+        want = 0 if e >= E else int(Wq[e, n] @ xi[t])
+        assert acc[i] == float(want), (r, n)
+
+
+def test_points_match_the_full_routine_on_random_blocks():
+    c = synth.moe_case(6, 16, 64, 5, 3, seed=8)
+    ids = c["ids"].copy()
+    ids[7] = 99
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], ids, 5, 3, 16, 64, 6, c["expert_stride"])
+    rng = np.random.default_rng(9)
+    rs = rng.integers(0, 15, 60)
+    ns = rng.integers(0, 16, 60)
+    pa = oracle.moe_q4_0_points(c["x"], c["w"], ids, 3, 64, 6, c["expert_stride"], rs, ns)
+    assert np.array_equal(pa, acc[rs, ns])
