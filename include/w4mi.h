@@ -65,6 +65,19 @@ const char* w4_version(void);
  * requires M == 1 ([P1]: single-row decode takes the library qmv path).
  * This library implements qmm_affine4 for K and N up to 2^21 (2,097,152);
  * larger valid shapes return W4_EUNSUPPORTED.
+ *
+ * Operand precision. qmv_affine4, and qmm_affine4 below 6 rows (or up to 16
+ * rows when K % 256 != 0 and K <= 8192), multiply the bf16 x by the exact
+ * nibbles and apply scale and bias per group in f32: no range limit beyond
+ * f32's. Every other qmm_affine4 shape runs on the matrix cores in binary16,
+ * as [P1]'s kernel does (module doc "Algorithm"): x is converted bf16 ->
+ * binary16 (round to nearest even; exact for magnitudes 2^-14 .. 65504,
+ * binary16's subnormal step below) and each weight is q * scale + bias
+ * rounded once to binary16. A finite x (or weight) of magnitude 65520 or
+ * more overflows binary16: the outputs of its row of x (or weight row) come
+ * out as infinities or NaN, and the call adds one per affected output tile
+ * to the device's range-event count (w4_range_events). Infinite or NaN
+ * inputs propagate as in the definition and are not counted.
  * ---------------------------------------------------------------------- */
 w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
                       const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
@@ -73,6 +86,14 @@ w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t*
 w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
                       const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
                       int32_t group_size, int32_t bits, void* stream);
+
+/* Range events of qmm_affine4's binary16 matrix-core routes on the CURRENT
+ * device (each GPU counts its own): the number of output tiles, since the
+ * last reset, whose x or weights held a finite value binary16 cannot hold
+ * (see "Operand precision" above). *count (host) receives the count;
+ * reset != 0 then clears it. The call synchronises the device first, so it
+ * covers every call enqueued before it. */
+w4_status w4_range_events(uint32_t* count, int32_t reset);
 
 /* ------------------------------------------------------------------------
  * Lookup-codebook 4-bit matmul [P2], half-precision path.
@@ -221,9 +242,15 @@ w4_status w4_check_id_swiglu(const w4_id_params* p);
 /* ------------------------------------------------------------------------
  * Unpack exports: the codes the hot kernels decode, written out one byte
  * per weight by the same device decode routines the kernels use, so that a
- * caller can check them bit for bit. All pointers are device pointers.
- *   w4_unpack_affine: q [N, K] from w [N, K/8] ([P1] nibble order).
- *   w4_unpack_lut:    codes [count] from packed ([P2] high nibble first).
+ * caller can check them bit for bit. Where the kernels decode one format
+ * with several routines, every one of them is applied and a weight on which
+ * they disagree is written as 0xFF. All pointers are device pointers.
+ *   w4_unpack_affine: q [N, K] from w [N, K/8] ([P1] nibble order): the
+ *                     nibble extraction, the GEMV's biased bf16 pairs and the
+ *                     matrix-core kernels' binary16 word decode.
+ *   w4_unpack_lut:    codes [count] from packed ([P2] high nibble first):
+ *                     the per-element code, the matrix-core byte-plane table
+ *                     decode and the single-precision path's dword lookup.
  *   w4_unpack_q4_0:   q [rows, K] codes and d [rows, K/32] binary16 bits
  *                     from `rows` consecutive Q4_0 weight rows.
  * ---------------------------------------------------------------------- */

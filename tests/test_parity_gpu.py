@@ -52,7 +52,7 @@ def _affine_scales(c):
 
 
 # ---------------------------------------------------------------- unpack, bit-exact
-@pytest.mark.parametrize("N,K", [(256, 256), (96, 40), (14336, 4096)])
+@pytest.mark.parametrize("N,K", [(256, 256), (96, 40), (4096, 4096), (14336, 4096)])
 def test_unpack_affine_bit_exact(N, K):
     c = synth.affine_case(1, K, N, seed=11)
     q = B.w4_unpack_affine(_t(c["w"].view(np.int32)), N, K).cpu().numpy()
@@ -143,6 +143,90 @@ def test_qmm_affine4_small(M, K, N):
     acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
     ms, mx = _affine_scales(c)
     _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"qmm M={M} K={K} N={N}")
+
+
+# Short K on every route of qmm_affine4, element by element: the GEMV forms (M < 6, and M <= 16 with
+# K % 256 != 0), the 64x128-tile kernel (17 <= M <= 64 with K % 256 != 0), the register-staged prefill
+# kernel (M > 64, K % 64 == 32), the specialised-wavefront prefill kernel (M > 64, K % 64 == 0) and the
+# weight-tile kernel (6 <= M <= 64, K % 256 == 0). Small K is where operand rounding weighs most against
+# the bound (few products, small |ref|).
+@pytest.mark.parametrize("M,K,N", [(m, k, n) for k, n in ((32, 96), (64, 128), (96, 160))
+                                   for m in (2, 5, 6, 12, 16, 17, 40, 64, 65, 100, 300)]
+                         + [(6, 256, 96), (20, 256, 128), (40, 512, 64), (64, 256, 160)])
+def test_qmm_affine4_short_k_every_route(M, K, N):
+    c = synth.affine_case(M, K, N, seed=7 * M + K + N)
+    w, s, b, x = _affine_dev(c)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"qmm short K M={M} K={K} N={N}")
+
+
+# Operand range of the binary16 routes: a finite x (or weight) that binary16 cannot hold makes its output
+# row (or column) non-finite and is counted; an infinite x propagates and is not counted. The GEMV forms
+# (bf16 products, f32 scale and bias) hold such values exactly.
+_BF16_1E5 = 0x47C3      # 99840.0, finite in bf16, beyond binary16's 65504
+_BF16_INF = 0x7F80
+
+
+@pytest.mark.parametrize("M,K,N,route", [
+    (300, 256, 256, "specialised-wavefront prefill"),
+    (300, 96, 128, "register-staged prefill"),
+    (40, 96, 128, "64x128 tile"),
+    (20, 512, 128, "weight tile"),
+])
+def test_qmm_affine4_range_events(M, K, N, route):
+    c = synth.affine_case(M, K, N, seed=31)
+    x = c["x"].copy()
+    x[3, 17] = _BF16_1E5
+    x[5, 0] = _BF16_INF
+    scales = c["scales"].copy()
+    scales[7, 1] = 0x4600     # 8192: q * s + b reaches ~122880 for q = 15
+    biases = c["biases"].copy()
+    biases[7, 1] = 0
+    w, s, b, xd = _affine_dev(dict(c, x=x, scales=scales, biases=biases))
+    B.w4_range_events(reset=True)
+    y = B.qmm_affine4(w, s, b, xd)
+    events = B.w4_range_events(reset=True)
+    yf = _bf16_to_f64(y)
+    assert events >= 1, route
+    assert not np.isfinite(yf[3]).any() and not np.isfinite(yf[5]).any(), route
+    assert not np.isfinite(yf[:, 7]).any(), route
+    keep_m = np.setdiff1d(np.arange(M), [3, 5])
+    keep_n = np.setdiff1d(np.arange(N), [7])
+    acc, _ = oracle.affine(c["w"], scales, biases, x, M, K, N)
+    ms = float(np.abs(oracle.bf16_to_f32(c["scales"])).max())
+    mx = float(np.abs(oracle.bf16_to_f32(c["x"])).max())
+    _assert_within(yf[np.ix_(keep_m, keep_n)], acc[np.ix_(keep_m, keep_n)], K, mx, ms, f"range {route}")
+
+
+def test_qmm_affine4_range_clean_inputs_and_infinities_are_not_counted():
+    M, K, N = 300, 256, 256
+    c = synth.affine_case(M, K, N, seed=32)
+    x = c["x"].copy()
+    x[9, 40] = _BF16_INF
+    w, s, b, xd = _affine_dev(dict(c, x=x))
+    B.w4_range_events(reset=True)
+    y = B.qmm_affine4(w, s, b, xd)
+    assert B.w4_range_events(reset=True) == 0
+    yf = _bf16_to_f64(y)
+    assert not np.isfinite(yf[9]).any()
+    assert np.isfinite(np.delete(yf, 9, axis=0)).all()
+
+
+def test_qmm_affine4_gemv_forms_hold_large_x_exactly():
+    M, K, N = 3, 256, 96
+    c = synth.affine_case(M, K, N, seed=33)
+    x = c["x"].copy()
+    x[1, 5] = _BF16_1E5
+    w, s, b, xd = _affine_dev(dict(c, x=x))
+    B.w4_range_events(reset=True)
+    y = B.qmm_affine4(w, s, b, xd)
+    assert B.w4_range_events(reset=True) == 0
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], x, M, K, N)
+    ms, mx = _affine_scales(c)   # max |x| without the planted value: the bound stays as tight as for plain x
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, "GEMV form with a large x")
 
 
 @pytest.mark.gpu

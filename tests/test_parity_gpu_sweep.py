@@ -29,17 +29,7 @@ def _affine_shape(seed):
     return M, K, N
 
 
-# Seed 4 (M=47, K=64, N=128): one output of 6016 lies outside the stated
-# bound. Exact arithmetic on bf16-rounded dequantized weights (the matrix
-# cores' operand type) also leaves one output of this case outside it, by 4 %
-# (tests/test_tolerance_bf16_operands.py), so the case shows a limit of bf16
-# operands at small K, not a kernel fault.
-_BF16_LIMIT = {4}
-
-
-@pytest.mark.parametrize("seed", [pytest.param(s, marks=pytest.mark.xfail(
-    reason="bf16-rounded dequantized weights exceed the bound at 1 of 6016 outputs (K=64)", strict=False))
-    if s in _BF16_LIMIT else s for s in SEEDS])
+@pytest.mark.parametrize("seed", SEEDS)
 def test_sweep_affine(seed):
     M, K, N = _affine_shape(seed)
     c = synth.affine_case(M, K, N, seed=seed)

@@ -64,6 +64,7 @@ SIGNATURES = {
     "w4_unpack_affine": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
     "w4_unpack_lut": ([_P, _P, _I64, _P], ctypes.c_int),
     "w4_unpack_q4_0": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "w4_range_events": ([_P, _I32], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -224,6 +225,13 @@ def w4_check_id(params: IdParams, scratch_bytes: int) -> int:
 
 def w4_check_id_swiglu(params: IdParams) -> int:
     return int(lib().w4_check_id_swiglu(ctypes.byref(params)))
+
+
+def w4_range_events(reset: bool = False) -> int:
+    """Range events of qmm_affine4's binary16 routes on the current device (synchronises it)."""
+    n = ctypes.c_uint32(0)
+    _check(lib().w4_range_events(ctypes.byref(n), int(reset)))
+    return int(n.value)
 
 
 def last_error() -> str:

@@ -1,18 +1,33 @@
 // MFMA GEMMs with a fused 4-bit weight decode:
 //   qmm_affine4 - y[M,N] bf16 = x[M,K] bf16 . (q*s + b)^T   (INT4 MatMulNBits
-//                 page, prefill M > 1; bf16 operands, f32 accumulation)
+//                 page, prefill M > 1). The matrix cores take binary16
+//                 operands, as the page's kernel does: x is converted
+//                 bf16 -> binary16 on its way into LDS and each weight is
+//                 q*s + b rounded once to binary16; f32 accumulation, bf16
+//                 output.
 //   qmm_lut4    - y[M,N] fp16 = x[M,K] fp16 . fp16(book[c]*scale)^T
 //                 (lut4 page, decode + GEMM route; fp16 operands, f32 acc)
 //
-// One skeleton serves both: a workgroup of 4 wavefronts computes a BM x BN
-// output tile; per K-step of 32 (one affine quantisation group) it stages the
-// x tile (BM x 32) and the decoded weight tile (BN x 32, decoded once per
-// workgroup in registers and written as 16-bit operands) in LDS, double
-// buffered so the next step's global loads overlap this step's matrix-core
-// work, with one barrier per step. Each wavefront owns a (16 FM) x (16 FN)
-// sub-tile and issues v_mfma_f32_16x16x32_{bf16,f16}; LDS rows are padded
-// to 80 bytes so the 16-byte operand reads of a 16-lane group hit distinct
-// banks.
+// Operand range. A finite bf16 x of magnitude 65520 or more (or a weight
+// q*s + b that large) becomes an infinity in binary16, which makes every
+// output of its row of x (or of its weight row) an infinity or NaN, since
+// an infinity times any weight, zero included, is not finite. So each
+// affine kernel checks its finished outputs: only when one is not finite
+// does it scan the inputs of that output tile, and if an x or weight value
+// there is finite but out of binary16 range it adds one to a per-device
+// event counter (w4_range_events). Inputs that are already infinite or NaN
+// propagate as they would in the definition and are not counted.
+//
+// The small-shape kernels below share one skeleton: a workgroup of 4
+// wavefronts computes a BM x BN output tile; per K-step of 32 (one affine
+// quantisation group) it stages the x tile (BM x 32) and the decoded weight
+// tile (BN x 32, decoded once per workgroup in registers and written as
+// binary16 operands) in LDS, double buffered so the next step's global loads
+// overlap this step's matrix-core work, with one barrier per step. Each
+// wavefront owns a (16 FM) x (16 FN) sub-tile and issues
+// v_mfma_f32_16x16x32_f16; LDS rows are padded to 80 bytes so the 16-byte
+// operand reads of a 16-lane group hit distinct banks.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -26,16 +41,63 @@ constexpr int kBK = 32;          // K per step
 constexpr int kLds = kBK + 8;    // padded LDS row, in 16-bit elements
 constexpr int kSmallDepth = 8;   // steps of global loads in flight in the small-M kernels
 
+// ---------------------------------------------------------------- operand range events
+// Per-device count of affine output tiles whose binary16 operands
+// overflowed (see the top of this file). Read and reset by w4_range_events.
+__device__ uint32_t g_range_events;
+
+constexpr float kF16Overflow = 65520.f;  // smallest magnitude that rounds to infinity in binary16
+
+// True in every lane when any lane's accumulated value is not finite
+// (v * 0 is NaN exactly for infinities and NaN).
+template <int N>
+__device__ __forceinline__ bool any_nonfinite(const float (&v)[N]) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) t = __builtin_fmaf(v[i], 0.f, t);
+    return __builtin_amdgcn_ballot_w64(t != t) != 0;
+}
+__device__ __forceinline__ bool out_of_f16_range(float v) {
+    const float a = __builtin_fabsf(v);
+    return a >= kF16Overflow && a <= 3.4028235e38f;
+}
+// Run by one whole wavefront after its tile produced a non-finite output:
+// looks for a finite x in rows [m_lo, m_hi) or a finite weight q*s + b in
+// weight rows [n_lo, n_hi) that binary16 cannot hold, and counts the tile
+// once if it finds one. Slow (element by element) and only reached when
+// the output already shows the problem.
+__device__ __noinline__ void affine_range_scan(const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
+                                               const uint16_t* __restrict__ scales,
+                                               const uint16_t* __restrict__ biases, int M, int K, int N, int m_lo,
+                                               int m_hi, int n_lo, int n_hi, uint32_t* events) {
+    const int lane = threadIdx.x & 63;
+    m_hi = min(m_hi, M);
+    n_hi = min(n_hi, N);
+    bool found = false;
+    for (int64_t i = (int64_t)m_lo * K + lane; i < (int64_t)m_hi * K && !found; i += 64)
+        found = out_of_f16_range(bf16_bits_to_f32(x[i]));
+    const int G = K / 32;
+    for (int64_t i = (int64_t)n_lo * K + lane; i < (int64_t)n_hi * K && !found; i += 64) {
+        const int64_t n = i / K, k = i % K;
+        const float q = (float)affine_nibble(w[n * (K / 8) + k / 8], (int)(k % 8));
+        found = out_of_f16_range(__builtin_fmaf(q, bf16_bits_to_f32(scales[n * G + k / 32]),
+                                                bf16_bits_to_f32(biases[n * G + k / 32])));
+    }
+    if (__builtin_amdgcn_ballot_w64(found) != 0 && lane == 0) atomicAdd(events, 1u);
+}
+
 // ---------------------------------------------------------------- weight decoders
 // Each decoder fills, for one weight row n and the 8 consecutive k of
 // "piece" p (k = k0 + 8p .. +7), four u32 holding the 16-bit operand pairs
 // (k, k+1) (k+2, k+3) (k+4, k+5) (k+6, k+7).
 
 struct AffineB {
+    static constexpr bool kAffine = true;  // x arrives as bf16 (converted to binary16), y is bf16
     const uint32_t* w;
     const uint16_t* scales;
     const uint16_t* biases;
     int K;
+    uint32_t* events;
     struct Raw {
         uint32_t word, s, b;
     };
@@ -51,18 +113,19 @@ struct AffineB {
             r.b = 0u;
         }
     }
-    // w = q * s + b in f32 (one rounding), then RNE to bf16.
+    // w = q * s + b in f32 (one rounding), then RNE to binary16.
     __device__ __forceinline__ void decode(const Raw& r, uint32_t (&out)[4]) const {
         const float s = bf16_bits_to_f32(r.s), b = bf16_bits_to_f32(r.b);
         float q[8];
         affine_word_to_f32(r.word, q);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            out[i] = pack_bf16x2(__builtin_fmaf(q[2 * i], s, b), __builtin_fmaf(q[2 * i + 1], s, b));
+            out[i] = pack_f16x2(__builtin_fmaf(q[2 * i], s, b), __builtin_fmaf(q[2 * i + 1], s, b));
     }
 };
 
 struct LutB {
+    static constexpr bool kAffine = false;  // x and y are binary16
     const uint8_t* packed;
     const uint16_t* scales;
     int K;
@@ -94,22 +157,9 @@ struct LutB {
     }
 };
 
-template <bool kF16>
-struct Mfma;
-template <>
-struct Mfma<false> {
-    __device__ __forceinline__ static f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                      0, 0, 0);
-    }
-};
-template <>
-struct Mfma<true> {
-    __device__ __forceinline__ static f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
-                                                     0, 0, 0);
-    }
-};
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------- GEMM skeleton
 // Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>).
@@ -126,7 +176,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // steps ahead in a register ring (a step has little matrix work next to
 // the latency of its loads, so the loop is bound by how many are in flight);
 // the LDS tiles are double buffered, one barrier per step.
-template <int WM, int WN, int FM, int FN, bool kF16, class BDec, int D>
+template <int WM, int WN, int FM, int FN, class BDec, int D>
 __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K,
                                              int N, const BDec& bdec, uint16_t* As, uint16_t* Bs) {
     constexpr int BM = WM * FM * 16;
@@ -179,7 +229,8 @@ __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uin
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int piece = tid + i * kGemmThreads;
-            *reinterpret_cast<u32x4*>(as + (piece / 4) * kLds + 8 * (piece % 4)) = xr[S][i];
+            *reinterpret_cast<u32x4*>(as + (piece / 4) * kLds + 8 * (piece % 4)) =
+                BDec::kAffine ? bf16x8_to_f16x8(xr[S][i]) : xr[S][i];
         }
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
@@ -202,7 +253,7 @@ __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uin
 #pragma unroll
         for (int f = 0; f < FM; ++f)
 #pragma unroll
-            for (int g = 0; g < FN; ++g) acc[f][g] = Mfma<kF16>::run(a[f], b[g], acc[f][g]);
+            for (int g = 0; g < FN; ++g) acc[f][g] = mfma16(a[f], b[g], acc[f][g]);
     };
 
     // Step kt's loads sit in slot kt % D. Writing LDS buffer kt & 1 at step kt
@@ -224,6 +275,20 @@ __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uin
         });
     }
 
+    if constexpr (BDec::kAffine) {
+        float v[FM * FN * 4];
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int g = 0; g < FN; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[(f * FN + g) * 4 + r] = acc[f][g][r];
+        if (any_nonfinite(v)) {
+            const int ml = m0 + wm * FM * 16, nl = n0 + wn * FN * 16;
+            affine_range_scan(x, bdec.w, bdec.scales, bdec.biases, M, K, N, ml, ml + FM * 16, nl, nl + FN * 16,
+                              bdec.events);
+        }
+    }
     // Epilogue: lane holds rows 4*(lane/16)+r, column lane%16 of each fragment.
 #pragma unroll
     for (int f = 0; f < FM; ++f)
@@ -234,7 +299,9 @@ __device__ __forceinline__ void gemm_w4_body(const uint16_t* __restrict__ x, uin
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * FM * 16 + f * 16 + 4 * (lane >> 4) + r;
-                if (m < M) y[(size_t)m * N + n] = kF16 ? f32_to_f16_bits(acc[f][g][r]) : f32_to_bf16_bits(acc[f][g][r]);
+                if (m < M)
+                    y[(size_t)m * N + n] =
+                        BDec::kAffine ? f32_to_bf16_bits(acc[f][g][r]) : f32_to_f16_bits(acc[f][g][r]);
             }
         }
 }
@@ -244,31 +311,29 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_affine4_kernel(const uint32_
                                                                     const uint16_t* __restrict__ scales,
                                                                     const uint16_t* __restrict__ biases,
                                                                     const uint16_t* __restrict__ x,
-                                                                    uint16_t* __restrict__ y, int M, int K, int N) {
+                                                                    uint16_t* __restrict__ y, int M, int K, int N,
+                                                                    uint32_t* __restrict__ events) {
     constexpr int BM = WM * FM * 16, BN = WN * FN * 16;
     __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * kLds];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * BN * kLds];
-    AffineB dec{w, scales, biases, K};
-    gemm_w4_body<WM, WN, FM, FN, false, AffineB, kSmallDepth>(x, y, M, K, N, dec, As, Bs);
+    AffineB dec{w, scales, biases, K, events};
+    gemm_w4_body<WM, WN, FM, FN, AffineB, kSmallDepth>(x, y, M, K, N, dec, As, Bs);
 }
 
-// ---------------------------------------------------------------- prefill GEMM (affine)
-// qmm_affine4 for the prefill shapes: a 256 x 128 output tile per workgroup
-// (one workgroup per CU at M = 2048, N = 4096) of 8 wavefronts in a 4 x 2
-// grid, two per SIMD so one's vector-ALU and LDS work fills the other's
-// matrix-core time. Each wavefront owns a 64 x 64 sub-tile as 2 x 2
-// accumulators of v_mfma_f32_32x32x16_bf16 (the full-rate matrix instruction
-// on gfx950). K advances 64 (two quantisation groups) per step. Global loads
-// run two steps ahead into registers and the LDS tiles are double buffered,
-// so a step's loads have two steps of matrix-core work to arrive. Each
-// thread decodes half a (weight row, group) per step: 16 nibbles into bf16
-// w = q s + b, via one AND-OR per nibble pair into binary16 1024 + q (or
-// 1024 + 16 q for the odd nibbles) and one v_fma_mix_f32 per weight with the
-// scale and the offset b - 1024 s (or s / 16 and b - 64 s) held in f32, then
-// v_cvt_pk_bf16_f32. LDS rows are 144 bytes (64 bf16 + 16 bytes), which keeps
-// the 16-byte operand reads of 16 consecutive rows conflict-free. Workgroups
-// are assigned to tiles so that the 32 workgroups one XCD runs share one x
-// tile in that XCD's L2.
+// ---------------------------------------------------------------- prefill GEMM (affine), register-staged
+// qmm_affine4 for prefill shapes with K % 64 == 32 (the LDS-DMA form below
+// takes K % 64 == 0): a 256 x 128 output tile per workgroup of 8 wavefronts
+// in a 4 x 2 grid, two per SIMD so one's vector-ALU and LDS work fills the
+// other's matrix-core time. Each wavefront owns a 64 x 64 sub-tile as 2 x 2
+// accumulators of v_mfma_f32_32x32x16_f16. K advances 64 (two quantisation
+// groups) per step; the last step holds one group and reads zeros for the
+// other. Global loads run two steps ahead into registers and the LDS tiles
+// are double buffered. Each thread converts its x pieces bf16 -> binary16 and
+// decodes half a (weight row, group) per step (affine_word_f16). LDS rows
+// are 144 bytes (64 operands + 16 bytes), which keeps the 16-byte operand
+// reads of 16 consecutive rows conflict-free. Workgroups are assigned to
+// tiles so that the 32 workgroups one XCD runs share one x tile in that
+// XCD's L2.
 constexpr int kPBM = 256, kPBN = 128, kPBK = 64;
 constexpr int kPThreads = 512;
 constexpr int kPLd = kPBK + 8;  // LDS row stride in 16-bit elements (144 bytes)
@@ -313,36 +378,24 @@ __device__ __forceinline__ void prefill_load(PrefillRegs& R, int kt, bool live, 
     R.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, gv ? o.s : kOob, ks, 0);
 }
 
-// Eight affine weights of one word (k = 8j .. 8j + 7) as bf16 pairs in k order.
-__device__ __forceinline__ u32x4 affine_word_bf16(uint32_t word, float s, float c, float s16, float c16,
-                                                  uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
-    const uint32_t w8 = word >> 8;
-    const f16x2 p0 = as_f16x2(and_or_u32(word, m_lo, magic));  // 1024 + n0, 1024 + n4
-    const f16x2 p1 = as_f16x2(and_or_u32(word, m_hi, magic));  // 1024 + 16 n1, 1024 + 16 n5
-    const f16x2 p2 = as_f16x2(and_or_u32(w8, m_lo, magic));    // 1024 + n2, 1024 + n6
-    const f16x2 p3 = as_f16x2(and_or_u32(w8, m_hi, magic));    // 1024 + 16 n3, 1024 + 16 n7
-    const float f0 = __builtin_fmaf((float)p0[0], s, c), f4 = __builtin_fmaf((float)p0[1], s, c);
-    const float f1 = __builtin_fmaf((float)p1[0], s16, c16), f5 = __builtin_fmaf((float)p1[1], s16, c16);
-    const float f2 = __builtin_fmaf((float)p2[0], s, c), f6 = __builtin_fmaf((float)p2[1], s, c);
-    const float f3 = __builtin_fmaf((float)p3[0], s16, c16), f7 = __builtin_fmaf((float)p3[1], s16, c16);
-    return u32x4{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3), pack_bf16x2(f4, f5), pack_bf16x2(f6, f7)};
-}
-
 __device__ __forceinline__ void prefill_store(const PrefillRegs& R, int tid, uint16_t* As, uint16_t* Bs,
                                               uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
     uint16_t* xa = As + (tid >> 3) * kPLd + 8 * (tid & 7);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xa + 64 * i * kPLd) = R.x[i];
-    const float s = bf16_bits_to_f32(R.s), b = bf16_bits_to_f32(R.b);
-    const float c = __builtin_fmaf(-1024.f, s, b), s16 = 0.0625f * s, c16 = __builtin_fmaf(-64.f, s, b);
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xa + 64 * i * kPLd) = bf16x8_to_f16x8(R.x[i]);
+    const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(R.s), bf16_bits_to_f32(R.b));
     uint16_t* dst = Bs + (tid >> 2) * kPLd + 16 * (tid & 3);
-    *reinterpret_cast<u32x4*>(dst) = affine_word_bf16(R.w[0], s, c, s16, c16, m_lo, m_hi, magic);
-    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_bf16(R.w[1], s, c, s16, c16, m_lo, m_hi, magic);
+    *reinterpret_cast<u32x4*>(dst) = affine_word_f16(R.w[0], grp, m_lo, m_hi, magic);
+    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_f16(R.w[1], grp, m_lo, m_hi, magic);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 // One step (64 of K) of the wavefront's 64 x 64 sub-tile: per 16 of K, two
 // A fragments (rows lane % 32 of each 32-row tile, k = 8 (lane / 32) .. +7)
-// and two B fragments, four v_mfma_f32_32x32x16_bf16.
+// and two B fragments, four v_mfma_f32_32x32x16_f16.
 __device__ __forceinline__ void prefill_mma(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
                                             f32x16 (&acc)[kPTM][kPTN]) {
     const uint16_t* ab = As + (wm * 64 + (lane & 31)) * kPLd + 8 * (lane >> 5);
@@ -358,15 +411,32 @@ __device__ __forceinline__ void prefill_mma(const uint16_t* As, const uint16_t* 
         for (int f = 0; f < kPTM; ++f)
 #pragma unroll
             for (int g = 0; g < kPTN; ++g)
-                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[f]),
-                                                                   __builtin_bit_cast(bf16x8, b[g]), acc[f][g], 0, 0, 0);
+                acc[f][g] = mfma32(a[f], b[g], acc[f][g]);
     }
+}
+
+// Affine epilogue range check for a wavefront's MT x NT grid of 32 x 32
+// accumulators covering x rows [m_lo, m_lo + 32 MT) and weight rows
+// [n_lo, n_lo + 32 NT).
+template <int MT, int NT>
+__device__ __forceinline__ void check_range32(const f32x16 (&acc)[MT][NT], const uint16_t* x, const uint32_t* w,
+                                              const uint16_t* scales, const uint16_t* biases, int M, int K, int N,
+                                              int m_lo, int n_lo, uint32_t* events) {
+    float v[MT * NT * 16];
+#pragma unroll
+    for (int f = 0; f < MT; ++f)
+#pragma unroll
+        for (int g = 0; g < NT; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[(f * NT + g) * 16 + e] = acc[f][g][e];
+    if (any_nonfinite(v))
+        affine_range_scan(x, w, scales, biases, M, K, N, m_lo, m_lo + 32 * MT, n_lo, n_lo + 32 * NT, events);
 }
 
 template <bool kTail>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N, uint32_t* __restrict__ events) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kPBM * kPLd];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -422,6 +492,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         __syncthreads();
     }
 
+    check_range32(acc, x, w, scales, biases, M, K, N, m0 + wm * 64, n0 + wn * 64, events);
     // Epilogue. Lane holds column lane % 32 of each 32 x 32 tile and, in
     // register e, row 8 (e / 4) + 4 (lane / 32) + e % 4. Stores go through a
     // buffer resource over the tile's rows, so rows past M are dropped by the
@@ -441,38 +512,31 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
 }
 
-// ---------------------------------------------------------------- prefill GEMM, LDS-DMA form
+// ---------------------------------------------------------------- prefill GEMM, specialised wavefronts
 // The same 256 x 128 tile and K step of 64 for K % 64 == 0, with the work
 // split by role so that the matrix pipe, the memory pipe and the vector ALU
 // run at the same time: of the 8 wavefronts (two per SIMD), 4 consumers (a
 // 2 x 2 grid of 128 x 64 sub-tiles, 8 accumulator tiles each) only read
-// operands from LDS and issue v_mfma_f32_32x32x16_bf16; 4 producers stream
-// the next steps in and decode the weights. One barrier per step hands the
-// buffers over. Data paths:
-//   x       buffer-to-LDS DMA (buffer_load_dwordx4 ... lds: 8 rows x 128 B per
-//           instruction, two steps ahead) into a 3-slot ring of
-//           [256 rows x 128 B]; row r's 16-byte chunk c sits at slot
-//           c ^ ((r / 2) % 8), which keeps the A-operand reads (32 rows x 2
-//           chunks per instruction) conflict-free. DMA'd data occupies no
-//           registers, and LDS-DMA moves these rows faster than loads into
-//           registers do.
-//   packed W, scales, biases
-//           plain loads into producer registers three steps ahead (a 3-deep
-//           register ring, the producer loop unrolled by 3): lane l of
-//           producer p holds row 32 p + l / 2, group l % 2 of the step
-//           (16 bytes of nibbles and the group's scale and bias), which is
-//           exactly what it decodes.
-//   W tile  2 x [128 rows x 144 B] decoded bf16 operands (the 144-byte row
-//           keeps 16 consecutive rows' operand reads conflict-free).
-// All producer memory instructions are inline asm with explicit waits: the
-// compiler does not count asm-issued loads, and its own waits would stall on
-// the DMA in flight. Every producer issues the same number (kWsPerIter) per
-// iteration, so one s_waitcnt covers the data two iterations old; the
-// barrier carries no memory fence, which would wait for all DMA in flight.
+// binary16 operands from LDS and issue v_mfma_f32_32x32x16_f16; 4 producers
+// load the next steps, convert x and decode the weights. One barrier per
+// step hands the buffers over. Producer p, lane l, per step:
+//   x       8 buffer loads of 16 bytes (rows 64 p + 8 i + l / 8, chunk l % 8
+//           of the step's 128 bytes), converted bf16 -> binary16 and written
+//           to a 2-slot LDS ring of [256 rows x 128 B], row r's chunk c at
+//           position c ^ ((r / 2) % 8), which keeps the A-operand reads
+//           (32 rows x 2 chunks per instruction) conflict-free;
+//   W       16 bytes of nibbles (row 32 p + l / 2, group l % 2: exactly one
+//           quantisation group) and the group's scale and bias, decoded
+//           (affine_word_f16) into one of 2 binary16 W tiles [128 rows x
+//           144 B] (the 144-byte row keeps 16 consecutive rows' operand reads
+//           conflict-free).
+// Loads run three steps ahead through a 3-deep register ring (the producer
+// loop unrolled by 3), so a step's data has two steps of matrix work to
+// arrive; the x of the 32 workgroups that one XCD runs (one row-block) stays
+// in that XCD's L2.
 constexpr int kWsThreads = 512;
-constexpr int kWsXb = 8;                // x DMA instructions (1 KB each) per producer per step
-constexpr int kWsPerIter = kWsXb + 3;   // + packed W, scale, bias loads
-constexpr int kDXBytes = kPBM * 128;    // x ring slot
+constexpr int kWsXp = 8;                // 16-byte x pieces per producer lane per step
+constexpr int kDXBytes = kPBM * 128;    // x ring slot (also the LUT GEMM's)
 
 // Byte address of an LDS object, for inline-asm LDS instructions.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -505,24 +569,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
 
-// One producer lane's share of a step's weights: 4 words (32 nibbles, one
-// quantisation group of one row) with the group's scale and bias bits.
-struct WsWeights {
+// One producer lane's share of a step: its 8 x pieces, 4 words (32 nibbles,
+// one quantisation group of one row) and the group's scale and bias bits.
+struct WsStep {
+    u32x4 x[kWsXp];
     u32x4 words;
     uint32_t s, b;
 };
-// Makes the registers of a ring entry opaque to the compiler after the wait
-// that covers their loads, so that no use is scheduled before that wait.
-__device__ __forceinline__ void ws_fence(WsWeights& e) { asm volatile("" : "+v"(e.words), "+v"(e.s), "+v"(e.b)); }
-
-// Decodes one ring entry into its 32 bf16 operands (row r, k 32 g .. 32 g + 31).
-__device__ __forceinline__ void ws_decode(const WsWeights& e, uint16_t* dst, uint32_t m_lo, uint32_t m_hi,
-                                          uint32_t magic) {
-    const float s = bf16_bits_to_f32(e.s), b = bf16_bits_to_f32(e.b);
-    const float c = __builtin_fmaf(-1024.f, s, b), s16 = 0.0625f * s, c16 = __builtin_fmaf(-64.f, s, b);
+// Makes a ring entry's registers opaque at this point, so that no work on
+// them is scheduled before it (the conversions and decode of a step must not
+// be hoisted above the barrier that frees the buffers they are written to).
+__device__ __forceinline__ void ws_fence(WsStep& e) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(dst + 8 * i) = affine_word_bf16(e.words[i], s, c, s16, c16, m_lo, m_hi, magic);
+    for (int i = 0; i < kWsXp; ++i) asm volatile("" : "+v"(e.x[i]));
+    asm volatile("" : "+v"(e.words), "+v"(e.s), "+v"(e.b));
 }
 
 // Step j's matrix work for a consumer: 4 sub-steps of k16, each 4 A reads
@@ -544,16 +604,14 @@ __device__ __forceinline__ void ws_mma(const uint8_t* xslot, const uint16_t* Bs,
 #pragma unroll
         for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
-                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[f]),
-                                                                   __builtin_bit_cast(bf16x8, b[g]), acc[f][g], 0, 0, 0);
+            for (int g = 0; g < 2; ++g) acc[f][g] = mfma32(a[f], b[g], acc[f][g]);
     }
 }
 
 __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_ws_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
-    __shared__ __attribute__((aligned(1024))) uint8_t xring[3][kDXBytes];
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N, uint32_t* __restrict__ events) {
+    __shared__ __attribute__((aligned(1024))) uint8_t xring[2][kDXBytes];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -568,8 +626,8 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // The two roles run separate loops (so neither holds the other's
     // registers) with the same sequence of barriers, one per step: at barrier
-    // j, x(j) has landed and W(j) is decoded, and the consumers are done with
-    // the buffers of step j - 1.
+    // j, x(j) and W(j) are in LDS, and the consumers are done with the buffers
+    // of step j - 1.
     if (wave >= 4) {
         const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
         const __amdgpu_buffer_rsrc_t wsrc =
@@ -577,47 +635,60 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
         const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
         const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
-        uint32_t xo[kWsXb];  // x rows 64 p .. 64 p + 63, 8 per instruction, swizzled chunk order
+        uint32_t xo[kWsXp];  // source offsets of the lane's x pieces (step 0)
+        uint16_t* xd[kWsXp];  // their places in slot 0 of the ring
 #pragma unroll
-        for (int i = 0; i < kWsXb; ++i) {
-            const int row = 8 * (kWsXb * role_wave + i) + (lane >> 3);
-            xo[i] = (uint32_t)(row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7)));
+        for (int i = 0; i < kWsXp; ++i) {
+            const int row = 64 * role_wave + 8 * i + (lane >> 3), c = lane & 7;
+            xo[i] = (uint32_t)(row * K * 2 + 16 * c);
+            xd[i] = reinterpret_cast<uint16_t*>(xring[0] + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
         }
         const int r = 32 * role_wave + (lane >> 1), g = lane & 1;
         const uint32_t wo = (uint32_t)(r * (K / 2) + 16 * g), so = (uint32_t)((r * G + g) * 2);
         uint16_t* const bdst = Bs[0] + r * kPLd + 32 * g;
-        WsWeights ring[3];
-        // x of step kt into xslot, the weights of step kw into e (past the end: zeros).
-        auto issue = [&](int kt, int kw, uint8_t* xslot, WsWeights& e) {
-            const bool xl = kt < steps, wl = kw < steps;
+        WsStep ring[3];
+        // Loads of step kt (past the end: out of range, zeros).
+        auto issue = [&](int kt, WsStep& e) {
+            const bool live = kt < steps;
             const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
 #pragma unroll
-            for (int i = 0; i < kWsXb; ++i)
-                lds_dma16(xsrc, xslot + (kWsXb * role_wave + i) * 1024, xl ? xo[i] : kOob, kx);
-            asm_load_b128(e.words, wsrc, wl ? wo : kOob, __builtin_amdgcn_readfirstlane(kw * 32));
-            asm_load_u16(e.s, ssrc, wl ? so : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
-            asm_load_u16(e.b, bsrc, wl ? so : kOob, __builtin_amdgcn_readfirstlane(kw * 4));
+            for (int i = 0; i < kWsXp; ++i) e.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, live ? xo[i] : kOob, kx, 0);
+            e.words = __builtin_amdgcn_raw_buffer_load_b128(wsrc, live ? wo : kOob, __builtin_amdgcn_readfirstlane(kt * 32), 0);
+            e.s = __builtin_amdgcn_raw_buffer_load_b16(ssrc, live ? so : kOob, __builtin_amdgcn_readfirstlane(kt * 4), 0);
+            e.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, live ? so : kOob, __builtin_amdgcn_readfirstlane(kt * 4), 0);
         };
-        // Prologue: W(0) (with x of a nonexistent step, so every batch has the
-        // same instruction count), then (x(0), W(1)) and (x(1), W(2)).
-        issue(steps, 0, xring[2], ring[0]);
-        issue(0, 1, xring[0], ring[1]);
-        issue(1, 2, xring[1], ring[2]);
-        wait_vmcnt<2 * kWsPerIter>();
-        ws_fence(ring[0]);
-        ws_decode(ring[0], bdst, m_lo, m_hi, magic);
-        // Iteration j (j mod 3 == S0): wait for the batch of iteration j - 2
-        // (x(j), W(j + 1)), barrier, decode W(j + 1) into the free W tile,
-        // then issue x(j + 2) into the slot the consumers left in iteration
-        // j - 1 and W(j + 3) into the ring entry decoded in iteration j - 1.
+        // Step data into LDS buffer `buf`: x converted, W decoded.
+        auto publish = [&](const WsStep& e, int buf) {
+#pragma unroll
+            for (int i = 0; i < kWsXp; ++i)
+                *reinterpret_cast<u32x4*>(xd[i] + buf * (kDXBytes / 2)) = bf16x8_to_f16x8(e.x[i]);
+            const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(e.s), bf16_bits_to_f32(e.b));
+            uint16_t* dst = bdst + buf * (kPBN * kPLd);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(dst + 8 * i) = affine_word_f16(e.words[i], grp, m_lo, m_hi, magic);
+        };
+        // The prologue issues steps 0, 1, 2 in the loop's order (the
+        // scheduling barriers keep the compiler from interleaving them, so its
+        // wait counts at the loop head stay exact).
+        issue(0, ring[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(1, ring[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(2, ring[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        publish(ring[0], 0);
+        // Iteration j (j mod 3 == S0): barrier j (this wavefront's LDS writes
+        // of step j are complete), publish step j + 1 into the free buffers
+        // (past the last step: zeros into buffers no consumer reads again),
+        // then load step j + 3 into the ring entry step j used.
         auto body = [&](auto slot, int j) {
-            constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
-            wait_vmcnt<kWsPerIter>();
-            wait_lgkmcnt0();  // this wavefront's decode of W(j)
-            ws_fence(ring[S1]);
+            constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3;
+            wait_lgkmcnt0();
             raw_barrier();
-            ws_decode(ring[S1], bdst + ((j + 1) & 1) * (kPBN * kPLd), m_lo, m_hi, magic);
-            issue(j + 2, j + 3, xring[S2], ring[S0]);
+            ws_fence(ring[S1]);
+            publish(ring[S1], (j + 1) & 1);
+            issue(j + 3, ring[S0]);
         };
         int j = 0;
         for (; j + 3 <= steps; j += 3) {
@@ -627,7 +698,6 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         }
         if (j < steps) body(std::integral_constant<int, 0>{}, j);
         if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
-        wait_vmcnt<0>();  // the trailing (all-zero) DMA lands before this wavefront ends
         return;
     }
 
@@ -641,9 +711,10 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int e = 0; e < 16; ++e) acc[f][g][e] = 0.f;
     for (int j = 0; j < steps; ++j) {
         raw_barrier();
-        ws_mma(xring[j % 3], Bs[j & 1], wm, wn, lane, acc);
+        ws_mma(xring[j & 1], Bs[j & 1], wm, wn, lane, acc);
     }
 
+    check_range32(acc, x, w, scales, biases, M, K, N, m0 + wm * 128, n0 + wn * 64, events);
     const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -659,10 +730,6 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 }
 
-struct Book16 {
-    float v[16];
-};
-
 template <int WM, int WN, int FM, int FN, int D>
 __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* __restrict__ x,
                                                                  const uint8_t* __restrict__ packed,
@@ -676,7 +743,7 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* 
     if (threadIdx.x < 16) book_s[threadIdx.x] = book.v[threadIdx.x];
     __syncthreads();
     LutB dec{packed, scales, K, block, book_s};
-    gemm_w4_body<WM, WN, FM, FN, true, LutB, D>(x, y, M, K, N, dec, As, Bs);
+    gemm_w4_body<WM, WN, FM, FN, LutB, D>(x, y, M, K, N, dec, As, Bs);
 }
 
 // ---------------------------------------------------------------- LUT GEMM, specialised wavefronts
@@ -699,46 +766,6 @@ constexpr int kLConsumers = 4, kLProducers = 8;
 constexpr int kLThreads = (kLConsumers + kLProducers) * 64;
 constexpr int kLXb = 32 / kLProducers;              // x DMA instructions per producer per step
 constexpr int kLDecodeWaves = kLBN * 4 / 64;        // producers that decode (one lane per row quarter)
-
-// The 16 table entries of one row's block as byte planes: lo[j] holds the low
-// bytes of entries 4j .. 4j + 3, hi[j] the high bytes.
-struct LutPlanes {
-    uint32_t lo[4], hi[4];
-};
-__device__ __forceinline__ LutPlanes lut_planes(const Book16& book, float s) {
-    uint32_t t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = pack_f16x2(book.v[2 * i] * s, book.v[2 * i + 1] * s);
-    LutPlanes P;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        P.lo[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x06040200u);
-        P.hi[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x07050301u);
-    }
-    return P;
-}
-// Looks up four codes (one per byte, 0..15): returns the low and high bytes
-// of their table entries. Selector byte 12 reads 0x00 and 13 reads 0xFF,
-// which turns bit 3 of each code into a byte mask.
-__device__ __forceinline__ void lut_lookup4(uint32_t codes, const LutPlanes& P, uint32_t& lo, uint32_t& hi) {
-    const uint32_t sel = codes & 0x07070707u;
-    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, ((codes >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
-    const uint32_t lo_a = __builtin_amdgcn_perm(P.lo[1], P.lo[0], sel), lo_b = __builtin_amdgcn_perm(P.lo[3], P.lo[2], sel);
-    const uint32_t hi_a = __builtin_amdgcn_perm(P.hi[1], P.hi[0], sel), hi_b = __builtin_amdgcn_perm(P.hi[3], P.hi[2], sel);
-    lo = (mask & lo_b) | (~mask & lo_a);
-    hi = (mask & hi_b) | (~mask & hi_a);
-}
-// Eight weights k .. k + 7 from one packed dword (byte j: code of k + 2j in
-// the high nibble, of k + 2j + 1 in the low one) as four fp16 pairs.
-__device__ __forceinline__ u32x4 lut_decode8(uint32_t word, const LutPlanes& P) {
-    uint32_t elo, ehi, olo, ohi;
-    lut_lookup4((word >> 4) & 0x0F0F0F0Fu, P, elo, ehi);  // k, k + 2, k + 4, k + 6
-    lut_lookup4(word & 0x0F0F0F0Fu, P, olo, ohi);         // k + 1, k + 3, k + 5, k + 7
-    const uint32_t a0 = __builtin_amdgcn_perm(olo, elo, 0x05010400u), b0 = __builtin_amdgcn_perm(ohi, ehi, 0x05010400u);
-    const uint32_t a1 = __builtin_amdgcn_perm(olo, elo, 0x07030602u), b1 = __builtin_amdgcn_perm(ohi, ehi, 0x07030602u);
-    return u32x4{__builtin_amdgcn_perm(b0, a0, 0x05010400u), __builtin_amdgcn_perm(b0, a0, 0x07030602u),
-                 __builtin_amdgcn_perm(b1, a1, 0x05010400u), __builtin_amdgcn_perm(b1, a1, 0x07030602u)};
-}
 
 struct LutWeights {
     u32x2 words;  // 16 codes: the lane's K quarter of its row
@@ -884,12 +911,13 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
 // group p) of each 256-wide K window, against all M rows (MT 32-row tiles of
 // x); at the end each of a tile's eight wavefronts sums two of the 16
 // accumulator registers over the eight partial sums (through LDS) and stores
-// them. Each lane decodes its own
-// weight word straight into a matrix-core operand (affine_word_bf16: bf16
-// q s + b in k order). Weights (128 packed bytes, 16 bytes of scales and 16 of
-// biases per row per window) and x (M rows x 512 bytes per window, from L2)
-// stream through one LDS ring (6 slots for up to 32 rows of x, 3 for up to
-// 64) by buffer-to-LDS DMA that all 16 wavefronts issue.
+// them. Each lane decodes its own weight word straight into a binary16
+// matrix-core operand (affine_word_f16: q s + b rounded once, in k order) and
+// converts its x operands bf16 -> binary16 as it reads them. Weights (128
+// packed bytes, 16 bytes of scales and 16 of biases per row per window) and x
+// (M rows x 512 bytes per window, from L2) stream through one LDS ring (6
+// slots for up to 32 rows of x, 3 for up to 64) by buffer-to-LDS DMA that all
+// 16 wavefronts issue.
 constexpr int kTlWaves = 16, kTlThreads = kTlWaves * 64;
 constexpr int kTlMinM = 6;                           // fewer rows take the shared-x GEMV form
 constexpr int kTlTiles = 2;                          // 32-row weight tiles per workgroup
@@ -967,7 +995,7 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
 template <int MT>
 __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N) {
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N, uint32_t* __restrict__ events) {
     using Sh = TlShape<MT>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Sh::kLds];
     constexpr int kS = Sh::kStages;
@@ -1076,17 +1104,14 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
             for (int mt = 0; mt < MT; ++mt)
                 aop[u][mt] = (MT > 1 && XS == 2) ? lds_ld<u32x4>(xa2[u][mt]) : lds_ld<u32x4>(xa[u][mt] + XS * Sh::kXSlot);
         }
-        const float sc = bf16_bits_to_f32(sraw), bi = bf16_bits_to_f32(braw);
-        const float c = __builtin_fmaf(-1024.f, sc, bi), s16 = 0.0625f * sc, c16 = __builtin_fmaf(-64.f, sc, bi);
+        const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(sraw), bf16_bits_to_f32(braw));
         u32x4 bop[kTlSteps];
 #pragma unroll
-        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_bf16(word[u], sc, c, s16, c16, m_lo, m_hi, magic);
+        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_f16(word[u], grp, m_lo, m_hi, magic);
 #pragma unroll
         for (int u = 0; u < kTlSteps; ++u)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aop[u][mt]),
-                                                                  __builtin_bit_cast(bf16x8, bop[u]), acc[mt], 0, 0, 0);
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32(bf16x8_to_f16x8(aop[u][mt]), bop[u], acc[mt]);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -1136,6 +1161,7 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
                 red[(((t * kTlParts + part) * MT + mt) * 14 + (i < 2 * part ? i : i - 2)) * 64 + lane] = acc[mt][i];
     raw_barrier();
     const int col = n0 + row;
+    float fin[MT][2];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -1148,9 +1174,23 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
 #pragma unroll
             for (int q = 0; q < kTlParts; ++q)
                 if (q != part) v += red[(((t * kTlParts + q) * MT + mt) * 14 + (i < 2 * q ? i : i - 2)) * 64 + lane];
+            fin[mt][e] = v;
+        }
+    // Range check over the finished sums (every x row, the tile's weight rows).
+    float fl[MT * 2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) fl[mt * 2 + e] = fin[mt][e];
+    if (any_nonfinite(fl)) affine_range_scan(x, w, scales, biases, M, K, N, 0, M, n0 + 32 * t, n0 + 32 * t + 32, events);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
             // Lane (n, h) holds x rows 8 (i / 4) + 4 h + i % 4 of the tile, weight row n.
+            const int i = 2 * part + e;
             const int m = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (m < M && col < N) y[(size_t)m * N + col] = f32_to_bf16_bits(v);
+            if (m < M && col < N) y[(size_t)m * N + col] = f32_to_bf16_bits(fin[mt][e]);
         }
 }
 
@@ -1159,6 +1199,42 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
 using namespace w4mi;
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device address of g_range_events on the current device, looked up once per
+// device (each GPU holds its own copy of the variable).
+static constexpr int kMaxDevices = 64;
+static std::atomic<uint32_t*> g_range_ptr[kMaxDevices];
+
+static w4_status range_counter(uint32_t** out, const char* fn) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(W4_ELAUNCH, "%s: no usable current device", fn);
+    uint32_t* p = g_range_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_range_events));
+        if (e != hipSuccess || !a)
+            return fail(W4_ELAUNCH, "%s: cannot locate the range-event counter: %s", fn, hipGetErrorString(e));
+        p = static_cast<uint32_t*>(a);
+        g_range_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return W4_OK;
+}
+
+extern "C" w4_status w4_range_events(uint32_t* count, int32_t reset) {
+    if (!count) return fail(W4_EINVAL, "w4_range_events: count is null");
+    uint32_t* p = nullptr;
+    const w4_status st = range_counter(&p, "w4_range_events");
+    if (st != W4_OK) return st;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(count, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && reset) e = hipMemset(p, 0, sizeof(uint32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(W4_ELAUNCH, "w4_range_events: %s", hipGetErrorString(e));
+    clear_error();
+    return W4_OK;
+}
 
 extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
                                  const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
@@ -1172,6 +1248,9 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
     if (K > (1 << 21) || N > (1 << 21))
         return fail(W4_EUNSUPPORTED, "qmm_affine4: implemented for K and N up to 2097152 (K=%lld N=%lld)", (long long)K,
                     (long long)N);
+    uint32_t* events = nullptr;
+    st = range_counter(&events, "qmm_affine4");
+    if (st != W4_OK) return st;
     hipStream_t s = as_stream(stream);
     const bool tiles_ok = K % kTlWinK == 0 && ((uintptr_t)scales & 3u) == 0 && ((uintptr_t)biases & 3u) == 0;
     if (M < kTlMinM && K <= kAffineBatchMaxK) {
@@ -1182,25 +1261,25 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
         const dim3 grid((unsigned)((N + kTlRows - 1) / kTlRows));
         if (M <= 32)
             hipLaunchKernelGGL(qmm_affine4_tiles_kernel<1>, grid, dim3(kTlThreads), 0, s, w, scales, biases, x, y, (int)M,
-                               (int)K, (int)N);
+                               (int)K, (int)N, events);
         else
             hipLaunchKernelGGL(qmm_affine4_tiles_kernel<2>, grid, dim3(kTlThreads), 0, s, w, scales, biases, x, y, (int)M,
-                               (int)K, (int)N);
+                               (int)K, (int)N, events);
     } else if (M <= kAffineBatchRows && K <= kAffineBatchMaxK) {
         launch_xlds(w, scales, biases, x, y, (int)M, (int)K, (int)N, s);
     } else if (M <= 64) {
         constexpr int BM = 64, BN = 128;
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
         hipLaunchKernelGGL((qmm_affine4_kernel<1, 4, 4, 2>), dim3(tiles), dim3(kGemmThreads), 0, s, w, scales, biases,
-                           x, y, (int)M, (int)K, (int)N);
+                           x, y, (int)M, (int)K, (int)N, events);
     } else {
         const unsigned tiles = (unsigned)(((M + kPBM - 1) / kPBM) * ((N + kPBN - 1) / kPBN));
         if (K % kPBK == 0)
             hipLaunchKernelGGL(qmm_affine4_prefill_ws_kernel, dim3(tiles), dim3(kWsThreads), 0, s, w, scales, biases,
-                               x, y, (int)M, (int)K, (int)N);
+                               x, y, (int)M, (int)K, (int)N, events);
         else
             hipLaunchKernelGGL(qmm_affine4_prefill_kernel<true>, dim3(tiles), dim3(kPThreads), 0, s, w, scales, biases,
-                               x, y, (int)M, (int)K, (int)N);
+                               x, y, (int)M, (int)K, (int)N, events);
     }
     return launch_status("qmm_affine4");
 }

@@ -96,8 +96,7 @@ template <bool H = false>
 __device__ __forceinline__ float lut_weight(const uint8_t* __restrict__ packed,
                                             const typename LutIO<H>::S* __restrict__ scales, const float* book_s,
                                             int64_t flat, int64_t scale_index) {
-    const uint32_t byte = packed[flat >> 1];
-    const uint32_t code = (flat & 1) ? (byte & 15u) : (byte >> 4);
+    const uint32_t code = lut_code(packed[flat >> 1], (uint32_t)(flat & 1));
     return LutIO<H>::w(book_s[code] * LutIO<H>::s(scales[scale_index]));
 }
 
@@ -225,22 +224,7 @@ __global__ __launch_bounds__(kF32ColWaves * 64) void lut4_f32_cols_kernel(const 
 // When each 8 consecutive codes along the contiguous axis share one block
 // (block % 8 == 0 and the contiguous length a multiple of block), a lane reads
 // 8 codes (one dword) and one scale at a time and looks the codes up in an LDS
-// copy of the codebook. Byte t of the dword holds flat indices 2t (high
-// nibble) and 2t + 1 (low nibble); the lookup offsets are taken as bytes of two
-// masked copies of the dword, (word >> 2) and (word << 2) masked to 4 x code,
-// hidden from the compiler, which would otherwise fold each pick back into a
-// shift and a mask of the word.
-__device__ __forceinline__ void lut_offsets(uint32_t word, uint32_t& hi4, uint32_t& lo4) {
-    hi4 = (word >> 2) & 0x3C3C3C3Cu;
-    lo4 = (word << 2) & 0x3C3C3C3Cu;
-    asm("" : "+v"(hi4), "+v"(lo4));
-}
-// Codebook entry of column c (0..7) of a dword whose offsets are hi4 / lo4.
-__device__ __forceinline__ float lut_entry(const float* book_s, uint32_t hi4, uint32_t lo4, int c) {
-    const uint32_t off = (((c & 1) ? lo4 : hi4) >> (8 * (c / 2))) & 0xFFu;
-    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(book_s) + off);
-}
-
+// copy of the codebook (lut_offsets / lut_entry).
 // [N, K], K % block == 0, block % 8 == 0: a wavefront owns 4 weight rows, lane
 // l takes the 8-wide K groups l, l + 64, ... (one dword of codes per row).
 // Steps of 64 whole groups run without checks, a last partial step reads the

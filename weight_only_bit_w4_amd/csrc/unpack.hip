@@ -1,6 +1,6 @@
 // Unpack exports: write out, one byte per weight, the 4-bit codes the hot
-// kernels decode, through the same device decode routines they use, so the
-// decode can be checked bit for bit.
+// kernels decode, through the same device decode routines they use
+// (w4mi_device.hpp), so the decode can be checked bit for bit.
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
@@ -8,9 +8,13 @@ namespace w4mi {
 
 constexpr int kUnpackThreads = 256;
 
-// One thread per affine word. Both decoders in use are applied: the nibble
-// extraction of the GEMM (affine_nibble) and the biased bf16 pairs of the
-// GEMV; a disagreement is written as 0xFF so it cannot pass a bit-exact check.
+// One thread per affine word. Every affine decoder the kernels run is
+// applied and must agree, else the code is written as 0xFF (which cannot
+// pass a bit-exact check): the nibble extraction of the small-shape GEMM
+// (affine_nibble), the biased bf16 pairs of the GEMV forms
+// (affine_pair_biased_bf16) and the binary16 word decode of the prefill and
+// weight-tile kernels (affine_word_f16 with scale 1 and bias 0, which gives
+// q exactly).
 __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __restrict__ q, int64_t words) {
     const int64_t i = (int64_t)blockIdx.x * kUnpackThreads + threadIdx.x;
     if (i >= words) return;
@@ -23,14 +27,49 @@ __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __
         out[p] = (uint8_t)(pair & 0xFu);
         out[p + 4] = (uint8_t)((pair >> 16) & 0xFu);
     }
+    const u32x4 h = affine_word_f16(word, affine_group_f16(1.f, 0.f), vreg(0x000F000Fu), vreg(0x00F000F0u),
+                                    vreg(0x64006400u));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[i * 8 + j] = (out[j] == affine_nibble(word, j)) ? out[j] : (uint8_t)0xFF;
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t bits = (j & 1) ? (h[j / 2] >> 16) : (h[j / 2] & 0xFFFFu);
+        const float v = f16_bits_to_f32(bits);
+        const bool same = out[j] == affine_nibble(word, j) && v == (float)out[j];
+        q[i * 8 + j] = same ? out[j] : (uint8_t)0xFF;
+    }
 }
 
+// One thread per 8 codes (flat indices 8 t .. 8 t + 7, the bytes 4 t ..
+// 4 t + 3). Every lookup decoder the kernels run is applied and must agree,
+// else 0xFF: the per-element code (lut_code), the half-precision matrix-core
+// decode (lut_decode8 on the byte-plane table of book[c] = c, scale 1, whose
+// binary16 entries are the codes exactly) and the single-precision path's
+// dword lookup in an LDS codebook (lut_offsets / lut_entry, book[c] = c).
 __global__ void unpack_lut_kernel(const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes, int64_t count) {
-    const int64_t i = (int64_t)blockIdx.x * kUnpackThreads + threadIdx.x;
-    if (i >= count) return;
-    codes[i] = (uint8_t)lut_code(packed[i / 2], (uint32_t)(i & 1));
+    __shared__ float book_s[16];
+    if (threadIdx.x < 16) book_s[threadIdx.x] = (float)threadIdx.x;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kUnpackThreads + threadIdx.x;
+    const int64_t base = 8 * t;
+    if (base >= count) return;
+    const int64_t nbytes = (count + 1) / 2;
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        if (4 * t + b < nbytes) word |= (uint32_t)packed[4 * t + b] << (8 * b);
+    Book16 ident;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ident.v[c] = (float)c;
+    const u32x4 h = lut_decode8(word, lut_planes(ident, 1.f));
+    uint32_t hi4, lo4;
+    lut_offsets(word, hi4, lo4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (base + j >= count) break;
+        const uint32_t c = lut_code((word >> (8 * (j / 2))) & 0xFFu, (uint32_t)j);
+        const uint32_t bits = (j & 1) ? (h[j / 2] >> 16) : (h[j / 2] & 0xFFFFu);
+        const bool same = f16_bits_to_f32(bits) == (float)c && lut_entry(book_s, hi4, lo4, j) == (float)c;
+        codes[base + j] = same ? (uint8_t)c : (uint8_t)0xFF;
+    }
 }
 
 // One thread per block pair (64 weights), reading the nine dwords the
@@ -91,8 +130,8 @@ extern "C" w4_status w4_unpack_lut(const uint8_t* packed, uint8_t* codes, int64_
     if (count < 0) return fail(W4_EINVAL, "w4_unpack_lut: count must be >= 0");
     if (count == 0) return W4_OK;
     if (!packed || !codes) return fail(W4_EINVAL, "w4_unpack_lut: null pointer argument");
-    hipLaunchKernelGGL(unpack_lut_kernel, dim3(blocks_for(count)), dim3(kUnpackThreads), 0, as_stream(stream), packed,
-                       codes, count);
+    hipLaunchKernelGGL(unpack_lut_kernel, dim3(blocks_for((count + 7) / 8)), dim3(kUnpackThreads), 0, as_stream(stream),
+                       packed, codes, count);
     return launch_status("w4_unpack_lut");
 }
 

@@ -63,14 +63,6 @@ __device__ __forceinline__ void affine_word_to_f32(uint32_t word, float (&q)[8])
     for (int j = 0; j < 8; ++j) q[j] = (float)affine_nibble(word, j);
 }
 
-// ---------------------------------------------------------------- buffer resources
-// Raw buffer resource over [base, base + bytes): loads through it take a
-// scalar offset per instruction and a 32-bit lane offset, and return zero
-// past the end. The third descriptor word is the gfx9 raw-buffer setting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // ---------------------------------------------------------------- integer helpers
 // A 32-bit constant held in a vector register (gfx9 VOP3 encodings take no
 // literal and read at most one scalar register, so a three-operand integer
@@ -84,6 +76,131 @@ __device__ __forceinline__ uint32_t vreg(uint32_t c) {
 // (a & m) | c; with m and c in vector registers (vreg) the compiler selects
 // one v_and_or_b32.
 __device__ __forceinline__ uint32_t and_or_u32(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
+
+// ---------------------------------------------------------------- binary16 matrix-core operands
+// The affine matrix-core kernels multiply in binary16, as the INT4
+// MatMulNBits page's kernel does (module doc "Algorithm": bf16 activations
+// cast to half, weights dequantized into half tiles, float accumulation).
+
+// A bf16 pair (one dword, element 0 in the low half) as a binary16 pair,
+// round to nearest even. Exact for magnitudes in [2^-14, 65504] and zero;
+// smaller ones keep binary16's subnormal step (2^-24); 65520 and above
+// become infinity.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d) {
+    return pack_f16x2(__uint_as_float(d << 16), __uint_as_float(d & 0xFFFF0000u));
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& v) {
+    return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
+}
+
+// Per-group constants of affine_word_f16: with s, b the group's scale and
+// bias, c = b - 1024 s, s16 = s / 16, c16 = b - 64 s.
+struct AffineGroupF16 {
+    float s, c, s16, c16;
+};
+__device__ __forceinline__ AffineGroupF16 affine_group_f16(float s, float b) {
+    return AffineGroupF16{s, __builtin_fmaf(-1024.f, s, b), 0.0625f * s, __builtin_fmaf(-64.f, s, b)};
+}
+// Eight affine weights of one word (k = 8j .. 8j + 7) as binary16 pairs in k
+// order, w = q s + b rounded once to binary16. One AND-OR per nibble pair
+// places the nibble in a binary16 mantissa under the exponent of 1024
+// (magic 0x6400): the even nibbles of a byte read as 1024 + q, the odd ones
+// (bits 4..7) as 1024 + 16 q; v_fma_mix then forms (1024 + q) s + (b - 1024 s)
+// or (1024 + 16 q) s/16 + (b - 64 s) in f32 and rounds to binary16.
+// m_lo = 0x000F000F, m_hi = 0x00F000F0, magic = 0x64006400 in vector
+// registers (vreg).
+__device__ __forceinline__ u32x4 affine_word_f16(uint32_t word, const AffineGroupF16& g, uint32_t m_lo, uint32_t m_hi,
+                                                 uint32_t magic) {
+    const uint32_t w8 = word >> 8;
+    const f16x2 p0 = as_f16x2(and_or_u32(word, m_lo, magic));  // 1024 + n0, 1024 + n4
+    const f16x2 p1 = as_f16x2(and_or_u32(word, m_hi, magic));  // 1024 + 16 n1, 1024 + 16 n5
+    const f16x2 p2 = as_f16x2(and_or_u32(w8, m_lo, magic));    // 1024 + n2, 1024 + n6
+    const f16x2 p3 = as_f16x2(and_or_u32(w8, m_hi, magic));    // 1024 + 16 n3, 1024 + 16 n7
+    f16x2 r0, r1, r2, r3;
+    r0[0] = (_Float16)__builtin_fmaf((float)p0[0], g.s, g.c);
+    r0[1] = (_Float16)__builtin_fmaf((float)p1[0], g.s16, g.c16);
+    r1[0] = (_Float16)__builtin_fmaf((float)p2[0], g.s, g.c);
+    r1[1] = (_Float16)__builtin_fmaf((float)p3[0], g.s16, g.c16);
+    r2[0] = (_Float16)__builtin_fmaf((float)p0[1], g.s, g.c);
+    r2[1] = (_Float16)__builtin_fmaf((float)p1[1], g.s16, g.c16);
+    r3[0] = (_Float16)__builtin_fmaf((float)p2[1], g.s, g.c);
+    r3[1] = (_Float16)__builtin_fmaf((float)p3[1], g.s16, g.c16);
+    return u32x4{as_u32(r0), as_u32(r1), as_u32(r2), as_u32(r3)};
+}
+
+// ---------------------------------------------------------------- lookup-codebook table decode
+// The half-precision lookup matmul's weight decode (lut4 page: value =
+// fp16(book[code] * scale), code of flat index i = high nibble of byte i / 2
+// for even i, low nibble for odd i). A lane builds its block's 16 table
+// entries T[c] = fp16(book[c] * s) as byte planes and looks codes up four at
+// a time with v_perm_b32.
+struct Book16 {
+    float v[16];
+};
+// The 16 table entries as byte planes: lo[j] holds the low bytes of entries
+// 4j .. 4j + 3, hi[j] the high bytes.
+struct LutPlanes {
+    uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ LutPlanes lut_planes(const Book16& book, float s) {
+    uint32_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = pack_f16x2(book.v[2 * i] * s, book.v[2 * i + 1] * s);
+    LutPlanes P;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        P.lo[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x06040200u);
+        P.hi[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x07050301u);
+    }
+    return P;
+}
+// Looks up four codes (one per byte, 0..15): returns the low and high bytes
+// of their table entries. Selector byte 12 reads 0x00 and 13 reads 0xFF,
+// which turns bit 3 of each code into a byte mask.
+__device__ __forceinline__ void lut_lookup4(uint32_t codes, const LutPlanes& P, uint32_t& lo, uint32_t& hi) {
+    const uint32_t sel = codes & 0x07070707u;
+    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, ((codes >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+    const uint32_t lo_a = __builtin_amdgcn_perm(P.lo[1], P.lo[0], sel), lo_b = __builtin_amdgcn_perm(P.lo[3], P.lo[2], sel);
+    const uint32_t hi_a = __builtin_amdgcn_perm(P.hi[1], P.hi[0], sel), hi_b = __builtin_amdgcn_perm(P.hi[3], P.hi[2], sel);
+    lo = (mask & lo_b) | (~mask & lo_a);
+    hi = (mask & hi_b) | (~mask & hi_a);
+}
+// Eight weights k .. k + 7 from one packed dword (byte j: code of k + 2j in
+// the high nibble, of k + 2j + 1 in the low one) as four fp16 pairs.
+__device__ __forceinline__ u32x4 lut_decode8(uint32_t word, const LutPlanes& P) {
+    uint32_t elo, ehi, olo, ohi;
+    lut_lookup4((word >> 4) & 0x0F0F0F0Fu, P, elo, ehi);  // k, k + 2, k + 4, k + 6
+    lut_lookup4(word & 0x0F0F0F0Fu, P, olo, ohi);         // k + 1, k + 3, k + 5, k + 7
+    const uint32_t a0 = __builtin_amdgcn_perm(olo, elo, 0x05010400u), b0 = __builtin_amdgcn_perm(ohi, ehi, 0x05010400u);
+    const uint32_t a1 = __builtin_amdgcn_perm(olo, elo, 0x07030602u), b1 = __builtin_amdgcn_perm(ohi, ehi, 0x07030602u);
+    return u32x4{__builtin_amdgcn_perm(b0, a0, 0x05010400u), __builtin_amdgcn_perm(b0, a0, 0x07030602u),
+                 __builtin_amdgcn_perm(b1, a1, 0x05010400u), __builtin_amdgcn_perm(b1, a1, 0x07030602u)};
+}
+
+// The single-precision lookup path's dword decode: a lane reads 8 codes (one
+// dword) and looks them up in an LDS copy of the codebook. Byte t of the dword holds flat indices 2t (high
+// nibble) and 2t + 1 (low nibble); the lookup offsets are taken as bytes of two
+// masked copies of the dword, (word >> 2) and (word << 2) masked to 4 x code,
+// hidden from the compiler, which would otherwise fold each pick back into a
+// shift and a mask of the word.
+__device__ __forceinline__ void lut_offsets(uint32_t word, uint32_t& hi4, uint32_t& lo4) {
+    hi4 = (word >> 2) & 0x3C3C3C3Cu;
+    lo4 = (word << 2) & 0x3C3C3C3Cu;
+    asm("" : "+v"(hi4), "+v"(lo4));
+}
+// Codebook entry of column c (0..7) of a dword whose offsets are hi4 / lo4.
+__device__ __forceinline__ float lut_entry(const float* book_s, uint32_t hi4, uint32_t lo4, int c) {
+    const uint32_t off = (((c & 1) ? lo4 : hi4) >> (8 * (c / 2))) & 0xFFu;
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(book_s) + off);
+}
+
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer resource over [base, base + bytes): loads through it take a
+// scalar offset per instruction and a 32-bit lane offset, and return zero
+// past the end. The third descriptor word is the gfx9 raw-buffer setting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // Pair form used by the decode GEMV: bf16 pairs holding 128 + q for nibbles
 // (i, i + 4), i = 0..3, of an affine word. 128 + q (q <= 15) is exact in bf16
