@@ -6,7 +6,11 @@
  * caller owns (a hipMalloc'd buffer, e.g. a torch-ROCm tensor's data_ptr);
  * "host" pointers are read during the call only. All tensors are dense and
  * row-major. Every entry point validates its arguments on the host before it
- * touches the GPU, enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * touches the GPU (shapes, alignment, and for the expert-routed calls the
+ * byte length of every buffer; the affine and lookup calls take no buffer
+ * lengths, so each buffer must hold what its stated shape needs - the Python
+ * binding checks tensor shapes before calling), enqueues its kernels on
+ * `stream` (a hipStream_t; NULL is
  * the default stream) and returns without synchronising; the library never
  * allocates device memory. On failure nothing is enqueued (W4_EINVAL,
  * W4_EUNSUPPORTED) or the launch error is reported (W4_ELAUNCH); the message

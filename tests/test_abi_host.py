@@ -89,16 +89,16 @@ def _params(**kw):
 
 @pytest.mark.parametrize("kw,status,needle", [
     ({}, B.W4_OK, ""),
-    ({"n_tokens": 0}, B.W4_EINVAL, "must all be > 0"),
-    ({"top_k": 0}, B.W4_EINVAL, "top_k"),
-    ({"n_experts": 0}, B.W4_EINVAL, "n_experts"),
-    ({"k": 2047}, B.W4_EINVAL, "divisible"),
-    ({"expert_stride": 1000}, B.W4_EINVAL, "expert_stride"),
-    ({"x_bytes": 16}, B.W4_EINVAL, "input buffer too small"),
-    ({"w_bytes": 1}, B.W4_EINVAL, "weight buffer too small"),
-    ({"ids_bytes": 4}, B.W4_EINVAL, "ids buffer too small"),
-    ({"out_bytes": 4}, B.W4_EINVAL, "output buffer too small"),
-    ({"reserved": 1}, B.W4_EINVAL, "reserved"),
+    ({"n_tokens": 0}, B.W4_EINVAL, "every size must be positive"),
+    ({"top_k": 0}, B.W4_EINVAL, "top_k=0"),
+    ({"n_experts": 0}, B.W4_EINVAL, "n_experts=0"),
+    ({"k": 2047}, B.W4_EINVAL, "whole number of 32-weight"),
+    ({"expert_stride": 1000}, B.W4_EINVAL, "experts are 1000 bytes apart"),
+    ({"x_bytes": 16}, B.W4_EINVAL, "x holds 16 bytes"),
+    ({"w_bytes": 1}, B.W4_EINVAL, "w holds 1 bytes"),
+    ({"ids_bytes": 4}, B.W4_EINVAL, "ids holds 4 bytes"),
+    ({"out_bytes": 4}, B.W4_EINVAL, "out holds 4 bytes"),
+    ({"reserved": 1}, B.W4_EINVAL, "reserved field"),
 ])
 def test_id_contract(kw, status, needle):
     p, scratch = _params(**kw)
@@ -155,16 +155,16 @@ def _swiglu_params(**kw):
 
 @pytest.mark.parametrize("kw,status,needle", [
     ({"n_tokens": 1}, B.W4_OK, ""),
-    ({"n_tokens": 0}, B.W4_EINVAL, "must all be > 0"),
-    ({"n_tokens": 1, "top_k": 0}, B.W4_EINVAL, "top_k"),
-    ({"n_tokens": 1, "n_experts": 0}, B.W4_EINVAL, "n_experts"),
-    ({"n_tokens": 1, "k": 2047}, B.W4_EINVAL, "divisible"),
-    ({"n_tokens": 1, "expert_stride": 1000}, B.W4_EINVAL, "expert_stride"),
-    ({"n_tokens": 1, "x_bytes": 1 * 8 * 2048 * 4 - 1}, B.W4_EINVAL, "gate/up buffer too small"),
-    ({"n_tokens": 1, "w_bytes": 1}, B.W4_EINVAL, "weight buffer too small"),
-    ({"n_tokens": 1, "ids_bytes": 4}, B.W4_EINVAL, "ids buffer too small"),
-    ({"n_tokens": 1, "out_bytes": 4}, B.W4_EINVAL, "output buffer too small"),
-    ({"n_tokens": 1, "reserved": 1}, B.W4_EINVAL, "reserved"),
+    ({"n_tokens": 0}, B.W4_EINVAL, "every size must be positive"),
+    ({"n_tokens": 1, "top_k": 0}, B.W4_EINVAL, "top_k=0"),
+    ({"n_tokens": 1, "n_experts": 0}, B.W4_EINVAL, "n_experts=0"),
+    ({"n_tokens": 1, "k": 2047}, B.W4_EINVAL, "whole number of 32-weight"),
+    ({"n_tokens": 1, "expert_stride": 1000}, B.W4_EINVAL, "1000 bytes apart"),
+    ({"n_tokens": 1, "x_bytes": 1 * 8 * 2048 * 4 - 1}, B.W4_EINVAL, "gate/up holds 65535 bytes"),
+    ({"n_tokens": 1, "w_bytes": 1}, B.W4_EINVAL, "w holds 1 bytes"),
+    ({"n_tokens": 1, "ids_bytes": 4}, B.W4_EINVAL, "ids holds 4 bytes"),
+    ({"n_tokens": 1, "out_bytes": 4}, B.W4_EINVAL, "out holds 4 bytes"),
+    ({"n_tokens": 1, "reserved": 1}, B.W4_EINVAL, "reserved field"),
 ])
 def test_id_swiglu_contract(kw, status, needle):
     p = _swiglu_params(**kw)
@@ -198,3 +198,51 @@ def test_id_swiglu_limits_are_reported_before_any_launch(kw):
 ])
 def test_lut_f32_contract(args, status):
     assert B.w4_check_lut_f32(*args) == status
+
+
+# ---------------------------------------------------------------- binding shape checks
+# The binding checks every tensor's shape against (M, K, N, block) before it touches a device, so a
+# wrong shape raises here even with host tensors (no kernel could read or write past a buffer).
+import torch
+
+
+def _affine_host(M=4, K=64, N=32):
+    return (torch.zeros((N, K // 8), dtype=torch.int32), torch.zeros((N, K // 32), dtype=torch.bfloat16),
+            torch.zeros((N, K // 32), dtype=torch.bfloat16), torch.zeros((M, K), dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("bad", ["w", "scales", "biases", "y"])
+def test_binding_rejects_affine_shape_mismatch(bad):
+    w, s, b, x = _affine_host()
+    y = torch.zeros((4, 32), dtype=torch.bfloat16)
+    if bad == "w":
+        w = torch.zeros((32, 4), dtype=torch.int32)
+    elif bad == "scales":
+        s = torch.zeros((32, 1), dtype=torch.bfloat16)
+    elif bad == "biases":
+        b = torch.zeros((31, 2), dtype=torch.bfloat16)
+    else:
+        y = torch.zeros((4, 31), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=bad):
+        B.qmm_affine4(w, s, b, x, y)
+
+
+def test_binding_affine_right_shapes_reach_the_device_check():
+    w, s, b, x = _affine_host()
+    with pytest.raises(TypeError, match="device tensor"):
+        B.qmm_affine4(w, s, b, x)
+
+
+@pytest.mark.parametrize("bad", ["packed", "scales", "y", "book"])
+def test_binding_rejects_lut_size_mismatch(bad):
+    M, K, N, block = 3, 64, 20, 16
+    x = torch.zeros((M, K), dtype=torch.float16)
+    packed = torch.zeros(N * K // 2 - (1 if bad == "packed" else 0), dtype=torch.uint8)
+    scales = torch.zeros(N * K // block - (1 if bad == "scales" else 0), dtype=torch.float16)
+    y = torch.zeros((M, N + (1 if bad == "y" else 0)), dtype=torch.float16)
+    book = [0.0] * (15 if bad == "book" else 16)
+    with pytest.raises(ValueError, match=bad):
+        B.qmm_lut4(x, packed, scales, book, N, block, y=y)
+    with pytest.raises(ValueError, match=bad):
+        B.qmm_lut4_f32(x.float(), packed, scales.float(), book, N, block, y=None if bad == "y" else y.float()) \
+            if bad != "y" else B.qmm_lut4_f32(x.float(), packed, scales.float(), book, N, block, y=y.float())

@@ -96,6 +96,27 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _shape(t, name: str, shape) -> None:
+    """Raises unless tensor t has exactly `shape` (checked before any device work)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _numel_at_least(t, name: str, count: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, expected at least {count}")
+
+
+def _same_device(ref: torch.Tensor, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {ref.device}")
+
+
 def _dev(t: torch.Tensor, name: str, dtypes) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
@@ -119,8 +140,17 @@ def version() -> str:
 
 # ---------------------------------------------------------------- affine INT4
 def _affine(fn_name, w, scales, biases, x, y, group_size, bits):
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [M, K] and w [N, K/8]")
     M, K = x.shape
     N = w.shape[0]
+    if group_size > 0 and K % group_size == 0 and K % 8 == 0:
+        _shape(w, "w", (N, K // 8))
+        _shape(scales, "scales", (N, K // group_size))
+        _shape(biases, "biases", (N, K // group_size))
+    if y is not None:
+        _shape(y, "y", (M, N))
+    _same_device(x, w=w, scales=scales, biases=biases, y=y)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     fn = getattr(lib(), fn_name)
@@ -140,8 +170,24 @@ def qmv_affine4(w, scales, biases, x, y=None, group_size: int = 32, bits: int = 
 
 
 # ---------------------------------------------------------------- lookup codebook
+def _lut_shapes(x, packed, scales, book, N, block, y):
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if len(book) != 16:
+        raise ValueError(f"book holds {len(book)} values, expected 16")
+    if N > 0 and K > 0 and block > 0:
+        count = N * K
+        _numel_at_least(packed, "packed", (count + 1) // 2)
+        _numel_at_least(scales, "scales", -(-count // block))
+    if y is not None:
+        _shape(y, "y", (M, N))
+    _same_device(x, packed=packed, scales=scales, y=y)
+
+
 def qmm_lut4(x, packed, scales, book, N: int, block: int, y=None, transpose: int = 1):
     """y [M, N] fp16 = x [M, K] fp16 . fp16(book[code] * scale)^T; book: 16 host floats."""
+    _lut_shapes(x, packed, scales, book, N, block, y)
     M, K = x.shape
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
@@ -155,6 +201,7 @@ def qmm_lut4(x, packed, scales, book, N: int, block: int, y=None, transpose: int
 def qmm_lut4_f32(x, packed, scales, book, N: int, block: int, y=None, transpose: int = 1):
     """y [M, N] f32 = x [M, K] f32 . W, W = book[code] * scale (f32, unrounded); W is [N, K]
     when transpose else [K, N]; book: 16 host floats."""
+    _lut_shapes(x, packed, scales, book, N, block, y)
     M, K = x.shape
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
@@ -179,6 +226,7 @@ def id_params(x, w, ids, out, n_tokens, top_k, n, k, n_experts, expert_stride) -
 def qmm_id_q4_0(x, w, ids, n_tokens: int, top_k: int, n: int, k: int, n_experts: int, expert_stride: int,
                 out=None, scratch=None):
     """out [n_tokens*top_k, n] f32: routed rows through their experts' Q4_0 weights."""
+    _same_device(x, w=w, ids=ids, out=out, scratch=scratch)
     if out is None:
         out = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=x.device)
     if scratch is None:
@@ -196,8 +244,9 @@ def qmm_id_swiglu_q4_0(gate, up, w, ids, n_tokens: int, top_k: int, n: int, k: i
     bad_ids: optional device uint32 tensor [1] receiving the out-of-range id count."""
     if out is None:
         out = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=gate.device)
-    if up.numel() != gate.numel():
+    if up.shape != gate.shape:
         raise ValueError("gate and up must have the same shape")
+    _same_device(gate, up=up, w=w, ids=ids, out=out, bad_ids=bad_ids)
     p = id_params(gate, w, ids, out, n_tokens, top_k, n, k, n_experts, expert_stride)
     bad = None if bad_ids is None else _dev(bad_ids, "bad_ids", U32)
     _check(lib().qmm_id_swiglu_q4_0(_dev(gate, "gate", F32), _dev(up, "up", F32), _dev(w, "w", U8),

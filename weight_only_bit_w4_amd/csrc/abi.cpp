@@ -123,78 +123,57 @@ w4_status w4_check_lut_f32(int64_t M, int64_t K, int64_t N, int32_t block, int32
     return W4_OK;
 }
 
-// mlx-native MoE page, quantized_matmul_id_ggml: every dimension positive,
-// K a multiple of the block size, expert stride and buffer lengths large
-// enough; plus the scratch the grouping needs.
+// Shared validation of the expert-routed calls (mlx-native MoE page,
+// quantized_matmul_id_ggml: the contraction's sizes must be positive, K whole
+// Q4_0 blocks, the expert stride at least one expert's blocks, and every
+// buffer long enough for the shapes). `act_rows` is the number of activation
+// rows the call reads: one per token for qmm_id_q4_0, one per routed row for
+// the fused SwiGLU form (gate and up each).
+static w4_status check_routed(const char* fn, const w4_id_params* p, uint64_t act_rows_per_token, const char* act_name) {
+    if (!p) return fail(W4_EINVAL, "%s: no parameter block given", fn);
+    if (!p->n_tokens || !p->top_k || !p->n || !p->k || !p->n_experts)
+        return fail(W4_EINVAL, "%s: every size must be positive (n_tokens=%u top_k=%u n=%u k=%u n_experts=%u)", fn,
+                    p->n_tokens, p->top_k, p->n, p->k, p->n_experts);
+    if (p->reserved) return fail(W4_EINVAL, "%s: the reserved field is %u, not 0", fn, p->reserved);
+    if (p->k % 32) return fail(W4_EINVAL, "%s: k=%u is not a whole number of 32-weight Q4_0 blocks", fn, p->k);
+    const uint64_t routed = (uint64_t)p->n_tokens * p->top_k;
+    if (routed > INT32_MAX) return fail(W4_EINVAL, "%s: %llu routed rows exceed int32", fn, (unsigned long long)routed);
+    const uint64_t expert_bytes = (uint64_t)p->n * (p->k / 32) * 18u;
+    if (p->expert_stride < expert_bytes)
+        return fail(W4_EINVAL, "%s: experts are %llu bytes apart but each holds %llu bytes of blocks", fn,
+                    (unsigned long long)p->expert_stride, (unsigned long long)expert_bytes);
+    struct {
+        const char* buffer;
+        uint64_t have, need;
+    } const lengths[] = {
+        {act_name, p->x_bytes, (uint64_t)p->n_tokens * act_rows_per_token * p->k * 4u},
+        {"w", p->w_bytes, (uint64_t)(p->n_experts - 1) * p->expert_stride + expert_bytes},
+        {"ids", p->ids_bytes, routed * 4u},
+        {"out", p->out_bytes, routed * p->n * 4u},
+    };
+    for (const auto& l : lengths)
+        if (l.have < l.need)
+            return fail(W4_EINVAL, "%s: %s holds %llu bytes; the shapes need %llu", fn, l.buffer,
+                        (unsigned long long)l.have, (unsigned long long)l.need);
+    return W4_OK;
+}
+
 w4_status w4_check_id(const w4_id_params* p, size_t scratch_bytes) {
-    if (!p) return fail(W4_EINVAL, "qmm_id_q4_0: params is null");
-    if (p->n_tokens == 0 || p->k == 0 || p->n == 0)
-        return fail(W4_EINVAL, "qmm_id_q4_0: n_tokens, K, and N must all be > 0");
-    if (p->top_k == 0) return fail(W4_EINVAL, "qmm_id_q4_0: top_k must be > 0");
-    if (p->n_experts == 0) return fail(W4_EINVAL, "qmm_id_q4_0: n_experts must be > 0");
-    if (p->reserved != 0) return fail(W4_EINVAL, "qmm_id_q4_0: reserved field must be 0");
-    if (p->k % 32 != 0) return fail(W4_EINVAL, "qmm_id_q4_0: K (%u) must be divisible by block QK (32)", p->k);
-    const uint64_t row_bytes = (uint64_t)(p->k / 32) * 18u;
-    const uint64_t per_expert = (uint64_t)p->n * row_bytes;
-    if (p->expert_stride < per_expert)
-        return fail(W4_EINVAL, "qmm_id_q4_0: expert_stride (%llu) < per_expert_bytes (%llu)",
-                    (unsigned long long)p->expert_stride, (unsigned long long)per_expert);
-    const uint64_t need_x = (uint64_t)p->n_tokens * p->k * 4u;
-    if (p->x_bytes < need_x)
-        return fail(W4_EINVAL, "qmm_id_q4_0: input buffer too small: expected %llu bytes for [%u x %u] f32, got %llu",
-                    (unsigned long long)need_x, p->n_tokens, p->k, (unsigned long long)p->x_bytes);
-    const uint64_t need_w = (uint64_t)(p->n_experts - 1) * p->expert_stride + per_expert;
-    if (p->w_bytes < need_w)
-        return fail(W4_EINVAL, "qmm_id_q4_0: weight buffer too small: expected %llu bytes for %u experts, got %llu",
-                    (unsigned long long)need_w, p->n_experts, (unsigned long long)p->w_bytes);
-    const uint64_t rows = (uint64_t)p->n_tokens * p->top_k;
-    if (rows > INT32_MAX) return fail(W4_EINVAL, "qmm_id_q4_0: n_tokens * top_k must fit in int32");
-    if (p->ids_bytes < rows * 4u)
-        return fail(W4_EINVAL, "qmm_id_q4_0: ids buffer too small: expected %llu bytes for [%u * %u] u32, got %llu",
-                    (unsigned long long)(rows * 4u), p->n_tokens, p->top_k, (unsigned long long)p->ids_bytes);
-    if (p->out_bytes < rows * p->n * 4u)
-        return fail(W4_EINVAL, "qmm_id_q4_0: output buffer too small: expected %llu bytes for [%llu x %u] f32, got %llu",
-                    (unsigned long long)(rows * p->n * 4u), (unsigned long long)rows, p->n,
-                    (unsigned long long)p->out_bytes);
+    w4_status st = check_routed("qmm_id_q4_0", p, 1, "x");
+    if (st != W4_OK) return st;
     if (p->n_experts > kMaxExperts)
-        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: at most %u experts are supported, got %u", kMaxExperts,
+        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: this library groups at most %u experts (asked for %u)", kMaxExperts,
                     p->n_experts);
     const size_t need_s = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k).total;
     if (scratch_bytes < need_s)
-        return fail(W4_EINVAL, "qmm_id_q4_0: scratch too small: expected %zu bytes, got %zu", need_s, scratch_bytes);
+        return fail(W4_EINVAL, "qmm_id_q4_0: scratch holds %zu bytes; the shapes need %zu", scratch_bytes, need_s);
     clear_error();
     return W4_OK;
 }
 
 w4_status w4_check_id_swiglu(const w4_id_params* p) {
-    if (!p) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: params is null");
-    if (p->n_tokens == 0 || p->k == 0 || p->n == 0)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: n_tokens, K, and N must all be > 0");
-    if (p->top_k == 0) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: top_k must be > 0");
-    if (p->n_experts == 0) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: n_experts must be > 0");
-    if (p->reserved != 0) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: reserved field must be 0");
-    if (p->k % 32 != 0)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: K (%u) must be divisible by block QK (32)", p->k);
-    const uint64_t per_expert = (uint64_t)p->n * (p->k / 32) * 18u;
-    if (p->expert_stride < per_expert)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: expert_stride (%llu) < per_expert_bytes (%llu)",
-                    (unsigned long long)p->expert_stride, (unsigned long long)per_expert);
-    const uint64_t rows = (uint64_t)p->n_tokens * p->top_k;
-    if (rows > INT32_MAX) return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: n_tokens * top_k must fit in int32");
-    const uint64_t need_in = rows * p->k * 4u;
-    if (p->x_bytes < need_in)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: gate/up buffer too small: expected %llu bytes, got %llu",
-                    (unsigned long long)need_in, (unsigned long long)p->x_bytes);
-    const uint64_t need_w = (uint64_t)(p->n_experts - 1) * p->expert_stride + per_expert;
-    if (p->w_bytes < need_w)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: weight buffer too small: expected %llu bytes for %u experts, got %llu",
-                    (unsigned long long)need_w, p->n_experts, (unsigned long long)p->w_bytes);
-    if (p->ids_bytes < rows * 4u)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: ids buffer too small: expected %llu bytes, got %llu",
-                    (unsigned long long)(rows * 4u), (unsigned long long)p->ids_bytes);
-    if (p->out_bytes < rows * p->n * 4u)
-        return fail(W4_EINVAL, "qmm_id_swiglu_q4_0: output buffer too small: expected %llu bytes, got %llu",
-                    (unsigned long long)(rows * p->n * 4u), (unsigned long long)p->out_bytes);
+    w4_status st = check_routed("qmm_id_swiglu_q4_0", p, p ? p->top_k : 0, "gate/up");
+    if (st != W4_OK) return st;
     clear_error();
     return W4_OK;
 }
