@@ -263,6 +263,21 @@ w4_status w4_unpack_lut(const uint8_t* packed, uint8_t* codes, int64_t count, vo
 w4_status w4_unpack_q4_0(const uint8_t* w, uint8_t* q, uint16_t* d, int64_t rows, int64_t K,
                          void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement entry points: achievable ceilings of this GPU, for reporting
+ * the kernels above against measured limits as well as published peaks.
+ *   w4_ceiling_stream_read: reads `bytes` (a multiple of 16) of the 16-byte
+ *       aligned device buffer `buf` once, with the 16-byte non-temporal loads
+ *       the bandwidth-bound kernels use; bytes / time is the streaming-read
+ *       rate. `sink` is a device uint32 [1024] the kernel may write.
+ *   w4_ceiling_mfma: every SIMD issues `iters` x 4 back-to-back
+ *       v_mfma_f32_32x32x16_f16 (32,768 flop each) on 2 x 256 workgroups of 4
+ *       wavefronts (no memory traffic): 2 * 256 * 4 * 4 * iters * 32768 flop.
+ * Both are asynchronous on `stream` and return W4_EINVAL on bad arguments.
+ * ---------------------------------------------------------------------- */
+w4_status w4_ceiling_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+w4_status w4_ceiling_mfma(uint32_t* sink, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -272,6 +272,21 @@ def test_qmm_affine4_prefill_full_size_sampled():
     assert torch.isfinite(y.float()).all()
 
 
+def test_qmm_affine4_prefill_full_size_every_output():
+    """The prefill workload (M=2048, K=N=4096) in the launch configuration the benchmark times, every one
+    of its 8.39 M outputs against the oracle (the XCD-aware tile order is only taken at this size)."""
+    c = synth.prefill_affine()
+    M, K, N = c["M"], c["K"], c["N"]
+    w, s, b, x = _affine_dev(c)
+    B.w4_range_events(reset=True)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    msc, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, msc, "qmm prefill every output")
+    assert B.w4_range_events(reset=True) == 0
+
+
 def test_affine_m_zero_is_noop():
     c = synth.affine_case(2, 64, 32, seed=5)
     w, s, b, _ = _affine_dev(c)
@@ -337,6 +352,19 @@ def test_qmm_lut4_full_size_sampled():
     got = y.float().cpu().numpy().astype(np.float64)[ms, ns]
     _assert_within(got, acc, K, float(np.abs(oracle.f16_to_f32(c["x"])).max()),
                    float(np.abs(oracle.f16_to_f32(c["scales"])).max()), "lut full sampled")
+
+
+def test_qmm_lut4_full_size_every_output():
+    """The lookup workload (M=512, K=4096, N=11008, block 64), every output against the oracle."""
+    c = synth.lut_matmul_case()
+    M, K, N, block = c["M"], c["K"], c["N"], c["block"]
+    x, p, s = _lut_dev(c)
+    y = B.qmm_lut4(x, p, s, c["book"], N, block)
+    torch.cuda.synchronize()
+    acc, _ = oracle.lut4(c["x"], c["packed"], c["scales"], c["book"], M, K, N, block)
+    got = y.float().cpu().numpy().astype(np.float64)
+    _assert_within(got, acc, K, float(np.abs(oracle.f16_to_f32(c["x"])).max()),
+                   float(np.abs(oracle.f16_to_f32(c["scales"])).max()), "lut every output")
 
 
 # ---------------------------------------------------------------- expert-routed Q4_0
@@ -419,6 +447,17 @@ def test_qmm_id_q4_0_full_size_sampled():
                                  rs, ns)
     _assert_within(got[rs, ns], acc, c["K"], float(np.abs(c["x"]).max()), _max_d(c), "moe full sampled")
     assert np.isfinite(got).all()
+
+
+def test_qmm_id_q4_0_full_size_every_output():
+    """The MoE workload (64 experts, N=1408, K=2048, 128 tokens, top-8), every routed row's outputs
+    against the oracle, and no out-of-range id counted."""
+    c = synth.moe_q4_0_case()
+    got, scratch = _moe_run(c)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], c["n_tokens"], c["top_k"], c["N"], c["K"], c["n_experts"],
+                             c["expert_stride"])
+    _assert_within(got, acc, c["K"], float(np.abs(c["x"]).max()), _max_d(c), "moe every output")
+    assert int(scratch[:4].cpu().numpy().view(np.uint32)[0]) == 0
 
 
 # ---------------------------------------------------------------- fused SwiGLU routed mat-vec

@@ -65,6 +65,8 @@ SIGNATURES = {
     "w4_unpack_lut": ([_P, _P, _I64, _P], ctypes.c_int),
     "w4_unpack_q4_0": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "w4_range_events": ([_P, _I32], ctypes.c_int),
+    "w4_ceiling_stream_read": ([_P, ctypes.c_uint64, _P, _P], ctypes.c_int),
+    "w4_ceiling_mfma": ([_P, _I32, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -281,6 +283,19 @@ def w4_range_events(reset: bool = False) -> int:
     n = ctypes.c_uint32(0)
     _check(lib().w4_range_events(ctypes.byref(n), int(reset)))
     return int(n.value)
+
+
+def w4_ceiling_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Reads every byte of buf once (streaming-read ceiling); sink: device int32 [1024]."""
+    _numel_at_least(sink, "sink", 1024)
+    _check(lib().w4_ceiling_stream_read(_dev(buf, "buf", (buf.dtype,)), buf.numel() * buf.element_size(),
+                                        _dev(sink, "sink", U32), _stream(buf)))
+
+
+def w4_ceiling_mfma(sink: torch.Tensor, iters: int) -> None:
+    """Back-to-back f16 matrix-core instructions on every SIMD (MFMA ceiling); sink: device int32 [1024]."""
+    _numel_at_least(sink, "sink", 1024)
+    _check(lib().w4_ceiling_mfma(_dev(sink, "sink", U32), iters, _stream(sink)))
 
 
 def last_error() -> str:

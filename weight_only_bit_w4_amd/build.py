@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw4mi.so")
 OBJ = os.path.join(ROOT, "_build", "w4mi")
-SOURCES = ["abi.cpp", "affine_gemv.hip", "gemm_w4.hip", "lut_f32.hip", "moe_q4_0.hip", "unpack.hip"]
+SOURCES = ["abi.cpp", "affine_gemv.hip", "ceiling.hip", "gemm_w4.hip", "lut_f32.hip", "moe_q4_0.hip", "unpack.hip"]
 ARCH = "gfx950"
 
 
