@@ -396,6 +396,18 @@ def main():
         log(f"ceiling: streaming read of {wbytes2} B, {nview} rotated views, 1000 launches")
         ms2, med2 = timer.run_stats(lambda i: B.w4_ceiling_stream_read(views[i % nview], sink), 1000, 50,
                                     chunk=nview * 4)
+        # The vendor library's plain half-precision GEMM of the prefill and lookup shapes (no
+        # dequantization): what a tuned GEMM reaches on these shapes on this GPU.
+        lib_gemm = {}
+        for tag, (Mg, Kg, Ng) in (("prefill shape", (2048, 4096, 4096)), ("lookup shape", (512, 4096, 11008))):
+            ga = torch.randn((Mg, Kg), device=dev).to(torch.float16)
+            gb = torch.randn((Kg, Ng), device=dev).to(torch.float16)   # [K, N] contiguous
+            gc = torch.empty((Mg, Ng), dtype=torch.float16, device=dev)
+            log(f"ceiling: torch.matmul fp16 {Mg}x{Kg}x{Ng} (hipBLASLt), 100 launches")
+            msg, medg = timer.run_stats(lambda i: torch.matmul(ga, gb, out=gc), 100, 10, chunk=10)
+            lib_gemm[tag] = {"M": Mg, "K": Kg, "N": Ng, "us": round(msg * 1e3, 2),
+                             "TFLOPs": round(2.0 * Mg * Kg * Ng / (msg * 1e-3) / 1e12, 1)}
+            del ga, gb, gc
         iters = 4096
         log(f"ceiling: f16 matrix-core loop, {iters} x 4 MFMA per wavefront, 20 launches")
         ms3, med3 = timer.run_stats(lambda i: B.w4_ceiling_mfma(sink, iters), 20, 3, chunk=2)
@@ -405,6 +417,7 @@ def main():
             "hbm_stream_read_decode_footprint": {"GBps": round(wbytes2 / (ms2 * 1e-3) / 1e9, 1), "bytes": wbytes2,
                                                  "us": round(ms2 * 1e3, 3), "us_median": round(med2 * 1e3, 3)},
             "mfma_f16": {"TFLOPs": round(mfma_flop / (ms3 * 1e-3) / 1e12, 1), "ms": round(ms3, 4)},
+            "library_fp16_gemm": lib_gemm,
         }
         del big, views, sink
 

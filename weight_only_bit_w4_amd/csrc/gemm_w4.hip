@@ -515,27 +515,29 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // ---------------------------------------------------------------- prefill GEMM, specialised wavefronts
 // The same 256 x 128 tile and K step of 64 for K % 64 == 0, with the work
 // split by role so that the matrix pipe, the memory pipe and the vector ALU
-// run at the same time: of the 8 wavefronts (two per SIMD), 4 consumers (a
+// run at the same time: of the 12 wavefronts (three per SIMD), 4 consumers (a
 // 2 x 2 grid of 128 x 64 sub-tiles, 8 accumulator tiles each) only read
-// binary16 operands from LDS and issue v_mfma_f32_32x32x16_f16; 4 producers
-// load the next steps, convert x and decode the weights. One barrier per
-// step hands the buffers over. Producer p, lane l, per step:
-//   x       8 buffer loads of 16 bytes (rows 64 p + 8 i + l / 8, chunk l % 8
+// binary16 operands from LDS and issue v_mfma_f32_32x32x16_f16; 8 producers
+// (two per SIMD, so that the vector ALU work of a step is issued by two
+// wavefronts) load the next steps, convert x and decode the weights. One
+// barrier per step hands the buffers over. Producer p, lane l, per step:
+//   x       4 buffer loads of 16 bytes (rows 32 p + 8 i + l / 8, chunk l % 8
 //           of the step's 128 bytes), converted bf16 -> binary16 and written
 //           to a 2-slot LDS ring of [256 rows x 128 B], row r's chunk c at
 //           position c ^ ((r / 2) % 8), which keeps the A-operand reads
 //           (32 rows x 2 chunks per instruction) conflict-free;
-//   W       16 bytes of nibbles (row 32 p + l / 2, group l % 2: exactly one
-//           quantisation group) and the group's scale and bias, decoded
-//           (affine_word_f16) into one of 2 binary16 W tiles [128 rows x
-//           144 B] (the 144-byte row keeps 16 consecutive rows' operand reads
-//           conflict-free).
+//   W       8 bytes of nibbles (item 64 p + l: row item / 4, group
+//           (item / 2) % 2, half item % 2: 16 of the group's 32 weights) and
+//           the group's scale and bias, decoded (affine_word_f16) into one of
+//           2 binary16 W tiles [128 rows x 144 B] (the 144-byte row keeps 16
+//           consecutive rows' operand reads conflict-free).
 // Loads run three steps ahead through a 3-deep register ring (the producer
 // loop unrolled by 3), so a step's data has two steps of matrix work to
 // arrive; the x of the 32 workgroups that one XCD runs (one row-block) stays
 // in that XCD's L2.
-constexpr int kWsThreads = 512;
-constexpr int kWsXp = 8;                // 16-byte x pieces per producer lane per step
+constexpr int kWsConsumers = 4, kWsProducers = 8;
+constexpr int kWsThreads = (kWsConsumers + kWsProducers) * 64;
+constexpr int kWsXp = kPBM * 8 / (kWsProducers * 64);   // 16-byte x pieces per producer lane per step (4)
 constexpr int kDXBytes = kPBM * 128;    // x ring slot (also the LUT GEMM's)
 
 // Byte address of an LDS object, for inline-asm LDS instructions.
@@ -569,11 +571,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
 
-// One producer lane's share of a step: its 8 x pieces, 4 words (32 nibbles,
-// one quantisation group of one row) and the group's scale and bias bits.
+// A store to an LDS byte address.
+template <typename T>
+__device__ __forceinline__ void lds_st(uint32_t addr, const T& v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T*>((uintptr_t)addr) = v;
+}
+
+// One producer lane's share of a step: its x pieces, 2 words (16 nibbles,
+// half a quantisation group of one row) and the group's scale and bias bits.
 struct WsStep {
     u32x4 x[kWsXp];
-    u32x4 words;
+    u32x2 words;
     uint32_t s, b;
 };
 // Makes a ring entry's registers opaque at this point, so that no work on
@@ -608,14 +616,13 @@ __device__ __forceinline__ void ws_mma(const uint8_t* xslot, const uint16_t* Bs,
     }
 }
 
-__global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void qmm_affine4_prefill_ws_kernel(
+__global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void qmm_affine4_prefill_ws_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N, uint32_t* __restrict__ events) {
     __shared__ __attribute__((aligned(1024))) uint8_t xring[2][kDXBytes];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPBN * kPLd];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int role_wave = wave & 3;     // index within the role
     const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
     const int tiles = tiles_m * tiles_n;
     int t = blockIdx.x;
@@ -628,45 +635,48 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // registers) with the same sequence of barriers, one per step: at barrier
     // j, x(j) and W(j) are in LDS, and the consumers are done with the buffers
     // of step j - 1.
-    if (wave >= 4) {
+    if (wave >= kWsConsumers) {
+        const int pw = wave - kWsConsumers;
         const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
         const __amdgpu_buffer_rsrc_t wsrc =
             make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * (K / 2), (uint32_t)(nrows * (K / 2)));
         const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(scales + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
         const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(biases + (size_t)n0 * G, (uint32_t)(nrows * G * 2));
         const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
-        uint32_t xo[kWsXp];  // source offsets of the lane's x pieces (step 0)
-        uint16_t* xd[kWsXp];  // their places in slot 0 of the ring
+        uint32_t xo[kWsXp];   // source offsets of the lane's x pieces (step 0)
+        uint32_t xd[kWsXp];   // LDS byte addresses of their places in slot 0 of the ring
 #pragma unroll
         for (int i = 0; i < kWsXp; ++i) {
-            const int row = 64 * role_wave + 8 * i + (lane >> 3), c = lane & 7;
+            const int row = 8 * (kWsXp * pw + i) + (lane >> 3), c = lane & 7;
             xo[i] = (uint32_t)(row * K * 2 + 16 * c);
-            xd[i] = reinterpret_cast<uint16_t*>(xring[0] + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
+            xd[i] = lds_addr(xring[0] + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
         }
-        const int r = 32 * role_wave + (lane >> 1), g = lane & 1;
-        const uint32_t wo = (uint32_t)(r * (K / 2) + 16 * g), so = (uint32_t)((r * G + g) * 2);
-        uint16_t* const bdst = Bs[0] + r * kPLd + 32 * g;
+        const int item = 64 * pw + lane, r = item >> 2, g = (item >> 1) & 1, h = item & 1;
+        const uint32_t wo = (uint32_t)(r * (K / 2) + 16 * g + 8 * h), so = (uint32_t)((r * G + g) * 2);
+        const uint32_t bdst = lds_addr(Bs[0] + r * kPLd + 32 * g + 16 * h);
         WsStep ring[3];
-        // Loads of step kt (past the end: out of range, zeros).
+        // Loads of step kt. Past the last step the wave-uniform offset is sent
+        // past every buffer's end (the loads return zeros), which keeps the
+        // per-lane offsets fixed.
         auto issue = [&](int kt, WsStep& e) {
             const bool live = kt < steps;
-            const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
+            const int kx = __builtin_amdgcn_readfirstlane(live ? kt * 2 * kPBK : (int)kOob);
+            const int kw = __builtin_amdgcn_readfirstlane(live ? kt * 32 : (int)kOob);
+            const int ks = __builtin_amdgcn_readfirstlane(live ? kt * 4 : (int)kOob);
 #pragma unroll
-            for (int i = 0; i < kWsXp; ++i) e.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, live ? xo[i] : kOob, kx, 0);
-            e.words = __builtin_amdgcn_raw_buffer_load_b128(wsrc, live ? wo : kOob, __builtin_amdgcn_readfirstlane(kt * 32), 0);
-            e.s = __builtin_amdgcn_raw_buffer_load_b16(ssrc, live ? so : kOob, __builtin_amdgcn_readfirstlane(kt * 4), 0);
-            e.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, live ? so : kOob, __builtin_amdgcn_readfirstlane(kt * 4), 0);
+            for (int i = 0; i < kWsXp; ++i) e.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xo[i], kx, 0);
+            e.words = __builtin_amdgcn_raw_buffer_load_b64(wsrc, wo, kw, 0);
+            e.s = __builtin_amdgcn_raw_buffer_load_b16(ssrc, so, ks, 0);
+            e.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, so, ks, 0);
         };
         // Step data into LDS buffer `buf`: x converted, W decoded.
-        auto publish = [&](const WsStep& e, int buf) {
+        auto publish = [&](const WsStep& e, auto buf) {
+            constexpr uint32_t xb = decltype(buf)::value * kDXBytes, wb = decltype(buf)::value * (kPBN * kPLd * 2);
 #pragma unroll
-            for (int i = 0; i < kWsXp; ++i)
-                *reinterpret_cast<u32x4*>(xd[i] + buf * (kDXBytes / 2)) = bf16x8_to_f16x8(e.x[i]);
+            for (int i = 0; i < kWsXp; ++i) lds_st<u32x4>(xd[i] + xb, bf16x8_to_f16x8(e.x[i]));
             const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(e.s), bf16_bits_to_f32(e.b));
-            uint16_t* dst = bdst + buf * (kPBN * kPLd);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4*>(dst + 8 * i) = affine_word_f16(e.words[i], grp, m_lo, m_hi, magic);
+            for (int i = 0; i < 2; ++i) lds_st<u32x4>(bdst + wb + 16 * i, affine_word_f16(e.words[i], grp, m_lo, m_hi, magic));
         };
         // The prologue issues steps 0, 1, 2 in the loop's order (the
         // scheduling barriers keep the compiler from interleaving them, so its
@@ -677,31 +687,36 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         __builtin_amdgcn_sched_barrier(0);
         issue(2, ring[2]);
         __builtin_amdgcn_sched_barrier(0);
-        publish(ring[0], 0);
-        // Iteration j (j mod 3 == S0): barrier j (this wavefront's LDS writes
-        // of step j are complete), publish step j + 1 into the free buffers
-        // (past the last step: zeros into buffers no consumer reads again),
-        // then load step j + 3 into the ring entry step j used.
-        auto body = [&](auto slot, int j) {
+        publish(ring[0], std::integral_constant<int, 0>{});
+        // Iteration j (j mod 3 == S0, j mod 2 == P): barrier j (this
+        // wavefront's LDS writes of step j are complete), publish step j + 1
+        // into the free buffers (past the last step: zeros into buffers no
+        // consumer reads again), then load step j + 3 into the ring entry step
+        // j used. The loop is unrolled by 6 so that both ring positions are
+        // constants.
+        auto body = [&](auto slot, auto par, int j) {
             constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3;
             wait_lgkmcnt0();
             raw_barrier();
             ws_fence(ring[S1]);
-            publish(ring[S1], (j + 1) & 1);
+            publish(ring[S1], std::integral_constant<int, 1 - decltype(par)::value>{});
             issue(j + 3, ring[S0]);
         };
         int j = 0;
-        for (; j + 3 <= steps; j += 3) {
-            body(std::integral_constant<int, 0>{}, j);
-            body(std::integral_constant<int, 1>{}, j + 1);
-            body(std::integral_constant<int, 2>{}, j + 2);
-        }
-        if (j < steps) body(std::integral_constant<int, 0>{}, j);
-        if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
+        for (; j + 6 <= steps; j += 6)
+            static_for<6>([&](auto I) {
+                body(std::integral_constant<int, I % 3>{}, std::integral_constant<int, I % 2>{}, j + I);
+            });
+        static_for<5>([&](auto I) {
+            if (j + I < steps) body(std::integral_constant<int, I % 3>{}, std::integral_constant<int, I % 2>{}, j + I);
+        });
         return;
     }
 
-    const int wm = role_wave >> 1, wn = role_wave & 1;
+    // Consumers issue at a higher wave priority than the producers that share
+    // their SIMD, so the matrix pipe gets an instruction whenever it is free.
+    __builtin_amdgcn_s_setprio(2);
+    const int wm = wave >> 1, wn = wave & 1;
     f32x16 acc[4][2];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
@@ -713,6 +728,7 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         raw_barrier();
         ws_mma(xring[j & 1], Bs[j & 1], wm, wn, lane, acc);
     }
+    __builtin_amdgcn_s_setprio(0);
 
     check_range32(acc, x, w, scales, biases, M, K, N, m0 + wm * 128, n0 + wn * 64, events);
     const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(y + (size_t)m0 * N, (uint32_t)(mrows * N * 2));
