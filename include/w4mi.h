@@ -206,6 +206,21 @@ size_t qmm_id_q4_0_scratch_bytes(uint32_t n_experts, uint32_t n_tokens, uint32_t
 w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_t* ids, float* out,
                       const w4_id_params* p, void* scratch, size_t scratch_bytes, void* stream);
 
+/* qmm_id_q4_0 for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * same operation, routes, kernels, contract and results, with the scratch
+ * taken from a fixed 4 MiB device array the library holds on each GPU it
+ * runs on (until the process ends) instead of a caller buffer. The call
+ * allocates nothing and makes no allocating library call. Requests whose
+ * scratch (qmm_id_q4_0_scratch_bytes) exceeds 4 MiB return W4_EUNSUPPORTED
+ * before any device work. bad_ids (device uint32, optional, NULL: not
+ * reported) receives the out-of-range id count, copied on `stream`. Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or threads without ordering) race and must not be
+ * issued; calls ordered on one stream are safe. */
+w4_status qmm_id_q4_0_noalloc(const float* x, const uint8_t* w, const uint32_t* ids, float* out,
+                              const w4_id_params* p, uint32_t* bad_ids, void* stream);
+
 /* ------------------------------------------------------------------------
  * Fused SwiGLU + expert-routed Q4_0 mat-vec [P3] (quantized_matmul_id_swiglu_q4_0):
  * for every routed row r = t*top_k + s, e = ids[r] and

@@ -56,6 +56,7 @@ SIGNATURES = {
     "qmm_id_q4_0_scratch_bytes": ([_U32, _U32, _U32, _U32], _SZ),
     "qmm_id_q4_0": ([_P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _SZ, _P], ctypes.c_int),
     "qmm_id_swiglu_q4_0": ([_P, _P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _P], ctypes.c_int),
+    "qmm_id_q4_0_noalloc": ([_P, _P, _P, _P, ctypes.POINTER(IdParams), _P, _P], ctypes.c_int),
     "w4_check_affine": ([_I64, _I64, _I64, _I32, _I32, _I32], ctypes.c_int),
     "w4_check_lut": ([_I64, _I64, _I64, _I32, _I32], ctypes.c_int),
     "w4_check_lut_f32": ([_I64, _I64, _I64, _I32, _I32], ctypes.c_int),
@@ -237,6 +238,20 @@ def qmm_id_q4_0(x, w, ids, n_tokens: int, top_k: int, n: int, k: int, n_experts:
     p = id_params(x, w, ids, out, n_tokens, top_k, n, k, n_experts, expert_stride)
     _check(lib().qmm_id_q4_0(_dev(x, "x", F32), _dev(w, "w", U8), _dev(ids, "ids", U32), _dev(out, "out", F32),
                              ctypes.byref(p), _dev(scratch, "scratch", U8), scratch.numel(), _stream(x)))
+    return out
+
+
+def qmm_id_q4_0_noalloc(x, w, ids, n_tokens: int, top_k: int, n: int, k: int, n_experts: int, expert_stride: int,
+                        out=None, bad_ids=None):
+    """qmm_id_q4_0 with the library's fixed device scratch (no allocation in the library). out must be
+    passed for a call that may not allocate at all; bad_ids: optional device int32 [1]."""
+    _same_device(x, w=w, ids=ids, out=out, bad_ids=bad_ids)
+    if out is None:
+        out = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=x.device)
+    p = id_params(x, w, ids, out, n_tokens, top_k, n, k, n_experts, expert_stride)
+    bad = None if bad_ids is None else _dev(bad_ids, "bad_ids", U32)
+    _check(lib().qmm_id_q4_0_noalloc(_dev(x, "x", F32), _dev(w, "w", U8), _dev(ids, "ids", U32),
+                                     _dev(out, "out", F32), ctypes.byref(p), bad, _stream(x)))
     return out
 
 

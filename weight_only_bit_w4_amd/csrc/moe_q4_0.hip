@@ -18,6 +18,8 @@
 //     into fp16 (q - 8) d.
 #include <type_traits>
 
+#include <atomic>
+
 #include "w4mi_device.hpp"
 #include "w4mi_host.hpp"
 
@@ -809,6 +811,63 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     hipLaunchKernelGGL(moe_gemm_kernel, dim3(p->n_experts * splits), dim3(kMoeThreads), 0, s, w, (const uint8_t*)scratch,
                        out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay, (int)p->n_tokens, (int)splits);
     return launch_status("qmm_id_q4_0 (grouped GEMM)");
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// qmm_id_q4_0 for callers that cannot allocate: the grouping scratch is this
+// file-scope device array instead of a caller buffer. Each GPU the library
+// runs on holds its own copy until the process ends; calls that overlap on
+// one GPU share it and race.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace w4mi {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxScratchDevices];
+
+// The array's device address on the current device (the name itself is a
+// host-side stand-in), looked up once per device.
+w4_status noalloc_scratch(uint8_t** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return fail(W4_ELAUNCH, "qmm_id_q4_0_noalloc: no usable current device");
+    uint8_t* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        void* a = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !a)
+            return fail(W4_ELAUNCH, "qmm_id_q4_0_noalloc: cannot locate the library scratch: %s", hipGetErrorString(e));
+        ptr = static_cast<uint8_t*>(a);
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return W4_OK;
+}
+}  // namespace
+}  // namespace w4mi
+
+extern "C" w4_status qmm_id_q4_0_noalloc(const float* x, const uint8_t* w, const uint32_t* ids, float* out,
+                                         const w4_id_params* p, uint32_t* bad_ids, void* stream) {
+    // Validate everything but the scratch first (host only), then the size.
+    w4_status st = w4_check_id(p, SIZE_MAX);
+    if (st != W4_OK) return st;
+    const size_t need = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(W4_EUNSUPPORTED,
+                    "qmm_id_q4_0_noalloc: the shapes need %zu bytes of scratch; the library's fixed scratch holds %zu "
+                    "(use qmm_id_q4_0 with a caller buffer)",
+                    need, kNoAllocScratchBytes);
+    if (((uintptr_t)bad_ids & 3u)) return fail(W4_EINVAL, "qmm_id_q4_0_noalloc: bad_ids must be 4-byte aligned");
+    uint8_t* ptr = nullptr;
+    st = noalloc_scratch(&ptr);
+    if (st != W4_OK) return st;
+    st = qmm_id_q4_0(x, w, ids, out, p, ptr, kNoAllocScratchBytes, stream);
+    if (st != W4_OK || !bad_ids) return st;
+    const hipError_t e = hipMemcpyAsync(bad_ids, ptr + W4_ID_SCRATCH_BAD_IDS, sizeof(uint32_t),
+                                        hipMemcpyDeviceToDevice, as_stream(stream));
+    if (e != hipSuccess) return fail(W4_ELAUNCH, "qmm_id_q4_0_noalloc: copying the bad-id count: %s", hipGetErrorString(e));
+    return W4_OK;
 }
 
 extern "C" w4_status qmm_id_swiglu_q4_0(const float* gate, const float* up, const uint8_t* w, const uint32_t* ids,
