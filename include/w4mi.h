@@ -91,12 +91,16 @@ w4_status qmv_affine4(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       const uint16_t* x, uint16_t* y, int64_t M, int64_t K, int64_t N,
                       int32_t group_size, int32_t bits, void* stream);
 
-/* Range events of qmm_affine4's binary16 matrix-core routes on the CURRENT
- * device (each GPU counts its own): the number of output tiles, since the
- * last reset, whose x or weights held a finite value binary16 cannot hold
- * (see "Operand precision" above). *count (host) receives the count;
- * reset != 0 then clears it. The call synchronises the device first, so it
- * covers every call enqueued before it. */
+/* Operand range events on the CURRENT device (each GPU counts its own):
+ * events since the last reset in which a finite value had to be rounded to
+ * binary16 and could not be held (magnitude 65520 or more, which becomes an
+ * infinity): qmm_affine4's matrix-core routes add one per output tile whose
+ * x or weights held such a value (see "Operand precision" above);
+ * qmm_id_q4_0 and qmm_id_swiglu_q4_0 add one per wavefront that rounded such
+ * an activation (x, or silu(gate) * up). Zero means no call since the reset
+ * met one. *count (host) receives the count; reset != 0 then clears it. The
+ * call synchronises the device first, so it covers every call enqueued
+ * before it. */
 w4_status w4_range_events(uint32_t* count, int32_t reset);
 
 /* ------------------------------------------------------------------------
@@ -172,7 +176,9 @@ w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const float* scale
  *     is stored there as binary16) before a grouped matrix-core GEMM reads
  *     them ([P3] map0 + mm, caller-owned scratch as in IdMmScratch).
  * Both routes round x to binary16 (round to nearest even) before the
- * products, which bounds |x| by 65504; accumulation is f32.
+ * products: a finite |x| of 65520 or more becomes an infinity (its routed
+ * rows' outputs are not finite) and is counted by w4_range_events;
+ * accumulation is f32.
  * Contract ([P3] quantized_matmul_id_ggml): n_tokens, K, N, top_k and
  * n_experts > 0; K % 32 == 0; expert_stride >= N * (K/32) * 18; each byte
  * length in p at least what the shapes need. Ids must be < n_experts: a row
@@ -236,8 +242,9 @@ w4_status qmm_id_q4_0_noalloc(const float* x, const uint8_t* w, const uint32_t* 
  *           written as zeros.
  * One launch, no scratch: each selected expert's weights are read once and
  * applied to every routed row that selects it. The activation is formed in
- * f32 and rounded to binary16 (round to nearest even) before the products,
- * which bounds |silu(gate) * up| by 65504; accumulation is f32.
+ * f32 and rounded to binary16 (round to nearest even) before the products;
+ * a finite activation of magnitude 65520 or more becomes an infinity and is
+ * counted by w4_range_events; accumulation is f32.
  * Contract ([P3]): n_tokens, K, N, top_k, n_experts > 0; K % 32 == 0;
  * expert_stride >= N * (K/32) * 18; byte lengths at least what the shapes
  * need. This library implements n_tokens * top_k <= 256 and K <= 8192 (the

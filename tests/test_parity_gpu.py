@@ -460,6 +460,24 @@ def test_qmm_id_q4_0_full_size_every_output():
     assert int(scratch[:4].cpu().numpy().view(np.uint32)[0]) == 0
 
 
+@pytest.mark.parametrize("T", [3, 40])   # the mat-vec route and the grouped route
+def test_qmm_id_q4_0_range_events(T):
+    """A finite x beyond binary16's range is counted as a range event and its token's routed rows come out
+    non-finite; the other rows stay within the bound; clean inputs count nothing."""
+    c = synth.moe_case(8, 64, 256, T, 2, seed=50 + T)
+    B.w4_range_events(reset=True)
+    clean, _ = _moe_run(c)
+    assert B.w4_range_events(reset=True) == 0
+    c2 = dict(c, x=c["x"].copy())
+    c2["x"][1, 7] = 1.0e5
+    got, _ = _moe_run(c2)
+    assert B.w4_range_events(reset=True) >= 1
+    top_k = c["top_k"]
+    assert not np.isfinite(got[top_k * 1:top_k * 2]).any()
+    keep = np.setdiff1d(np.arange(T * top_k), np.arange(top_k, 2 * top_k))
+    assert np.array_equal(got[keep], clean[keep])
+
+
 # ---------------------------------------------------------------- fused SwiGLU routed mat-vec
 def _swiglu_run(c, ids=None, bad=False):
     ids = c["ids"] if ids is None else ids
@@ -473,6 +491,19 @@ def _swiglu_run(c, ids=None, bad=False):
 def _max_act(c):
     g, u = c["gate"].astype(np.float64), c["up"].astype(np.float64)
     return float(np.abs(g / (1 + np.exp(-g)) * u).max())
+
+
+def test_qmm_id_swiglu_q4_0_range_event():
+    c = synth.moe_swiglu_case(8, 64, 256, 2, 2, seed=60)
+    B.w4_range_events(reset=True)
+    _swiglu_run(c)
+    assert B.w4_range_events(reset=True) == 0
+    c2 = dict(c, gate=c["gate"].copy(), up=c["up"].copy())
+    c2["gate"][1, 3] = 400.0
+    c2["up"][1, 3] = 400.0      # silu(400) * 400 = 160000: beyond binary16
+    got, _ = _swiglu_run(c2)
+    assert B.w4_range_events(reset=True) >= 1
+    assert not np.isfinite(got[1]).any()
 
 
 @pytest.mark.parametrize("E,N,K,T,top_k", [

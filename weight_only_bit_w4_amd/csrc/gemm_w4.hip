@@ -46,8 +46,6 @@ constexpr int kSmallDepth = 8;   // steps of global loads in flight in the small
 // overflowed (see the top of this file). Read and reset by w4_range_events.
 __device__ uint32_t g_range_events;
 
-constexpr float kF16Overflow = 65520.f;  // smallest magnitude that rounds to infinity in binary16
-
 // True in every lane when any lane's accumulated value is not finite
 // (v * 0 is NaN exactly for infinities and NaN).
 template <int N>
@@ -56,10 +54,6 @@ __device__ __forceinline__ bool any_nonfinite(const float (&v)[N]) {
 #pragma unroll
     for (int i = 0; i < N; ++i) t = __builtin_fmaf(v[i], 0.f, t);
     return __builtin_amdgcn_ballot_w64(t != t) != 0;
-}
-__device__ __forceinline__ bool out_of_f16_range(float v) {
-    const float a = __builtin_fabsf(v);
-    return a >= kF16Overflow && a <= 3.4028235e38f;
 }
 // Run by one whole wavefront after its tile produced a non-finite output:
 // looks for a finite x in rows [m_lo, m_hi) or a finite weight q*s + b in
@@ -1218,10 +1212,11 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Device address of g_range_events on the current device, looked up once per
 // device (each GPU holds its own copy of the variable).
+namespace w4mi {
 static constexpr int kMaxDevices = 64;
 static std::atomic<uint32_t*> g_range_ptr[kMaxDevices];
 
-static w4_status range_counter(uint32_t** out, const char* fn) {
+w4_status range_counter(uint32_t** out, const char* fn) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return fail(W4_ELAUNCH, "%s: no usable current device", fn);
@@ -1237,6 +1232,7 @@ static w4_status range_counter(uint32_t** out, const char* fn) {
     *out = p;
     return W4_OK;
 }
+}  // namespace w4mi
 
 extern "C" w4_status w4_range_events(uint32_t* count, int32_t reset) {
     if (!count) return fail(W4_EINVAL, "w4_range_events: count is null");

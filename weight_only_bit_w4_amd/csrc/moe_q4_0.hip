@@ -30,8 +30,11 @@ constexpr int kGroupThreads = 1024;
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t* __restrict__ ids, const float* __restrict__ x,
                                                                   uint8_t* __restrict__ scratch, float* __restrict__ out,
                                                                   int n_rows, int n_experts, int N, int64_t x_count,
-                                                                  IdScratchLayout lay) {
+                                                                  IdScratchLayout lay, uint32_t* __restrict__ events) {
     if (blockIdx.x > 0) {
+        // A finite x beyond binary16's range becomes an infinity: each
+        // wavefront that meets one counts one range event.
+        bool oor = false;
         // x -> binary16, 8 values per thread per step: output positions
         // 8c .. 8c + 7 of a 32-wide block hold k = 4c, 4c + 2, 16 + 4c,
         // 16 + 4c + 2, 4c + 1, 4c + 3, 16 + 4c + 1, 16 + 4c + 3 (the order
@@ -45,7 +48,10 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const uint32_t
             const f32x4 b = *reinterpret_cast<const f32x4*>(x + blk + 16 + 4 * c);
             *reinterpret_cast<u32x4*>(xh + i) = u32x4{pack_f16x2(a[0], a[2]), pack_f16x2(b[0], b[2]),
                                                       pack_f16x2(a[1], a[3]), pack_f16x2(b[1], b[3])};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) oor |= out_of_f16_range(a[t]) || out_of_f16_range(b[t]);
         }
+        if (__builtin_amdgcn_ballot_w64(oor) != 0 && (threadIdx.x & 63) == 0) atomicAdd(events, 1u);
         return;
     }
     extern __shared__ uint32_t cnt[];  // [n_experts], counts then cursors
@@ -520,7 +526,8 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
                                                                const uint8_t* __restrict__ w,
                                                                const uint32_t* __restrict__ ids, float* __restrict__ out,
                                                                uint32_t* __restrict__ bad_ids, int N, int K, int top_k,
-                                                               int n_rows, int n_experts, uint64_t expert_stride) {
+                                                               int n_rows, int n_experts, uint64_t expert_stride,
+                                                               uint32_t* __restrict__ events) {
     constexpr int kThreads = kMvWaves * 64;
     constexpr int kPieces = T * kMvChunk * 4;  // (block, quarter) pieces of x
     constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
@@ -590,6 +597,10 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
         for (int t = 0; t < 4; ++t) a[t] = g[t] * u[t] * __builtin_amdgcn_rcpf(1.f + __expf(-g[t]));
         return a;
     };
+    // The first tile's workgroups check every activation they round to
+    // binary16 (each routed row is served by exactly one of them) and count
+    // a range event per wavefront that meets a finite value beyond its range.
+    bool oor = false;
     auto publish_x = [&](const f32x4 (&src_lo)[kSrc][kPer], const f32x4 (&src_hi)[kSrc][kPer]) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -602,6 +613,9 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
                 lo[0] = src_lo[0][i];
                 hi[0] = src_hi[0][i];
             }
+            if (blockIdx.x == 0 && p < kPieces)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) oor |= out_of_f16_range(lo[0][t]) || out_of_f16_range(hi[0][t]);
             f16x2 l02, h02, l13, h13;
             l02[0] = (_Float16)lo[0][0]; l02[1] = (_Float16)lo[0][2];
             h02[0] = (_Float16)hi[0][0]; h02[1] = (_Float16)hi[0][2];
@@ -735,6 +749,7 @@ __global__ __launch_bounds__(kMvWaves * 64) void moe_mv_kernel(const float* __re
         acc += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(acc), 0x121, 0xF, 0xF, false));
         if (j == 0 && n < N) out[(size_t)r2 * N + n] = acc;
     }
+    if (__builtin_amdgcn_ballot_w64(oor) != 0 && lane == 0) atomicAdd(events, 1u);
 }
 
 }  // namespace w4mi
@@ -747,7 +762,7 @@ namespace w4mi {
 // n_routed <= 64 kMvIdSlots and K <= 32 kMvChunk kMvMaxChunks).
 template <bool SWIGLU>
 void mv_launch(const float* x, const float* up, const uint8_t* w, const uint32_t* ids, float* out, uint32_t* bad,
-               const w4_id_params* p, hipStream_t s) {
+               const w4_id_params* p, hipStream_t s, uint32_t* events) {
     const uint32_t n_routed = p->n_tokens * p->top_k;
     const int chunks = (int)((p->k / 32 + kMvChunk - 1) / kMvChunk);
     const dim3 grid((unsigned)((p->n + kMvTile - 1) / kMvTile), n_routed), block(kMvWaves * 64);
@@ -755,7 +770,7 @@ void mv_launch(const float* x, const float* up, const uint8_t* w, const uint32_t
     const bool realign = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
 #define W4_MV_LAUNCH(T, RE)                                                                                      \
     hipLaunchKernelGGL((moe_mv_kernel<T, RE, SWIGLU>), grid, block, 0, s, x, up, w, ids, out, bad, (int)p->n,   \
-                       (int)p->k, (int)p->top_k, (int)n_routed, (int)p->n_experts, p->expert_stride)
+                       (int)p->k, (int)p->top_k, (int)n_routed, (int)p->n_experts, p->expert_stride, events)
     switch (chunks * 2 + (realign ? 1 : 0)) {
         case 2: W4_MV_LAUNCH(1, false); break;
         case 3: W4_MV_LAUNCH(1, true); break;
@@ -779,13 +794,16 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     if (((uintptr_t)w & 1u) || (p->expert_stride & 1u) || ((uintptr_t)x & 15u) || ((uintptr_t)scratch & 255u))
         return fail(W4_EINVAL, "qmm_id_q4_0: w and expert_stride must be 2-byte, x 16-byte, scratch 256-byte aligned");
     const IdScratchLayout lay = id_scratch_layout(p->n_experts, p->n_tokens, p->top_k, p->k);
+    uint32_t* events = nullptr;
     hipStream_t s = as_stream(stream);
     const uint64_t n_routed = (uint64_t)p->n_tokens * p->top_k;
     const int chunks = (int)((p->k / 32 + kMvChunk - 1) / kMvChunk);
     if (p->n_tokens <= kMvMaxTokens && n_routed <= 64u * kMvIdSlots && chunks <= kMvMaxChunks) {
         // Mat-vec route (the page's mv_id below its routing threshold).
         uint32_t* bad = reinterpret_cast<uint32_t*>((uint8_t*)scratch + lay.bad_ids);
-        mv_launch<false>(x, nullptr, w, ids, out, bad, p, s);
+        st = range_counter(&events, "qmm_id_q4_0");
+        if (st != W4_OK) return st;
+        mv_launch<false>(x, nullptr, w, ids, out, bad, p, s, events);
         return launch_status("qmm_id_q4_0 (mat-vec route)");
     }
     if (p->k % 64 != 0)
@@ -797,11 +815,13 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     // in 32 bits, with in-range offsets below the out-of-range marker 2^31.
     if ((uint64_t)p->n_tokens * p->k * 2u >= (1ull << 32) || (uint64_t)kMoeChunkRows * (p->k / 32) * 18u >= (1ull << 31))
         return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for n_tokens * K * 2 < 2^32 bytes and 384-row weight chunks below 2^31 bytes");
+    st = range_counter(&events, "qmm_id_q4_0");
+    if (st != W4_OK) return st;
     const int n_rows = (int)(p->n_tokens * p->top_k);
     const int64_t x_count = (int64_t)p->n_tokens * p->k;
     const int conv_blocks = (int)std::min<int64_t>(1024, (x_count / 8 + kGroupThreads - 1) / kGroupThreads);
     hipLaunchKernelGGL(moe_group_kernel, dim3(1 + conv_blocks), dim3(kGroupThreads), p->n_experts * sizeof(uint32_t), s,
-                       ids, x, (uint8_t*)scratch, out, n_rows, (int)p->n_experts, (int)p->n, x_count, lay);
+                       ids, x, (uint8_t*)scratch, out, n_rows, (int)p->n_experts, (int)p->n, x_count, lay, events);
     st = launch_status("qmm_id_q4_0 (group)");
     if (st != W4_OK) return st;
     // Each expert's 32-row tiles are split over enough workgroups that the
@@ -883,6 +903,9 @@ extern "C" w4_status qmm_id_swiglu_q4_0(const float* gate, const float* up, cons
     if (n_routed > 64u * kMvIdSlots || chunks > (uint64_t)kMvMaxChunks)
         return fail(W4_EUNSUPPORTED, "qmm_id_swiglu_q4_0: implemented for n_tokens * top_k <= %d and K <= %d",
                     64 * kMvIdSlots, 32 * kMvChunk * kMvMaxChunks);
-    mv_launch<true>(gate, up, w, ids, out, bad_ids, p, as_stream(stream));
+    uint32_t* events = nullptr;
+    st = range_counter(&events, "qmm_id_swiglu_q4_0");
+    if (st != W4_OK) return st;
+    mv_launch<true>(gate, up, w, ids, out, bad_ids, p, as_stream(stream), events);
     return launch_status("qmm_id_swiglu_q4_0");
 }

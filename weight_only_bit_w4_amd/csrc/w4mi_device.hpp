@@ -82,6 +82,15 @@ __device__ __forceinline__ uint32_t and_or_u32(uint32_t a, uint32_t m, uint32_t 
 // MatMulNBits page's kernel does (module doc "Algorithm": bf16 activations
 // cast to half, weights dequantized into half tiles, float accumulation).
 
+// Smallest magnitude that rounds to infinity in binary16 (65504 + half an ulp).
+constexpr float kF16Overflow = 65520.f;
+// True for a finite value that binary16 cannot hold (it would become an
+// infinity); infinities and NaN are not counted.
+__device__ __forceinline__ bool out_of_f16_range(float v) {
+    const float a = __builtin_fabsf(v);
+    return a >= kF16Overflow && a <= 3.4028235e38f;
+}
+
 // A bf16 pair (one dword, element 0 in the low half) as a binary16 pair,
 // round to nearest even. Exact for magnitudes in [2^-14, 65504] and zero;
 // smaller ones keep binary16's subnormal step (2^-24); 65520 and above

@@ -19,6 +19,10 @@ void clear_error();
 // Checks the HIP runtime's launch status after enqueuing `what`.
 w4_status launch_status(const char* what);
 
+// Device address of the current device's operand-range event counter
+// (w4_range_events), looked up once per device.
+w4_status range_counter(uint32_t** out, const char* fn);
+
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Internal layout of the expert-routed scratch buffer (see qmm_id_q4_0).
