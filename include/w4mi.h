@@ -185,9 +185,9 @@ w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const float* scale
  * whose id is not is written as zeros, and the number of such rows is left
  * as a uint32 at byte offset W4_ID_SCRATCH_BAD_IDS of scratch.
  * x must be 16-byte aligned, w and expert_stride 2-byte aligned. This
- * library implements the grouped route for K % 64 == 0, n_tokens * K * 2 <
- * 2^32 and 4-byte-aligned w and expert_stride; other valid requests that
- * need it return W4_EUNSUPPORTED.
+ * library implements the grouped route for n_tokens * K * 2 < 2^32 and
+ * 384 * (K/32) * 18 < 2^31; other valid requests that need it return
+ * W4_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct {
     uint32_t n_tokens;      /* input tokens */

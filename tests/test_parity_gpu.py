@@ -425,15 +425,60 @@ def test_qmm_id_q4_0_duplicate_and_out_of_range_ids(T):
     assert scratch[:4].view(torch.int32).item() == 3
 
 
-def test_qmm_id_q4_0_mat_vec_route_limits():
-    # Past 4 chunks (K > 8192) a few tokens go to the grouped GEMM, which needs K % 64 == 0.
-    c = synth.moe_case(2, 32, 8256, 2, 2, seed=5)
+@pytest.mark.parametrize("K", [8256, 8224])
+def test_qmm_id_q4_0_mat_vec_route_limits(K):
+    # Past 4 chunks (K > 8192) a few tokens go to the grouped GEMM, with an even and an odd block count.
+    c = synth.moe_case(2, 32, K, 2, 2, seed=K)
     got, _ = _moe_run(c)
-    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], 2, 2, 32, 8256, 2, c["expert_stride"])
-    _assert_within(got, acc, 8256, float(np.abs(c["x"]).max()), _max_d(c), "moe K=8256")
-    c = synth.moe_case(2, 32, 8224, 2, 2, seed=6)
-    with pytest.raises(RuntimeError, match="K % 64"):
-        _moe_run(c)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], 2, 2, 32, K, 2, c["expert_stride"])
+    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(c), f"moe K={K}")
+
+
+@pytest.mark.parametrize("E,N,K,T,top_k", [
+    (8, 96, 96, 40, 2),      # 3 blocks: one window, 3 live blocks
+    (4, 72, 160, 50, 3),     # 5 blocks: a last window of 1
+    (6, 200, 224, 64, 2),    # 7 blocks, N not a multiple of the tile
+    (3, 400, 2080, 40, 2),   # 65 blocks (17 windows), two row chunks (384 + 16)
+])
+def test_qmm_id_q4_0_grouped_odd_block_rows(E, N, K, T, top_k):
+    """Grouped route with K % 64 == 32: every other weight row starts 2 bytes past a dword."""
+    c = synth.moe_case(E, N, K, T, top_k, seed=E * K + T)
+    got, scratch = _moe_run(c)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], T, top_k, N, K, E, c["expert_stride"])
+    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(c), f"moe odd blocks E={E} N={N} K={K}")
+    assert scratch[:4].view(torch.int32).item() == 0
+
+
+def _restride(c, pad):
+    """c's weights with `pad` bytes between expert slabs (none after the last)."""
+    E, slab = c["n_experts"], c["expert_stride"]
+    w = np.zeros((E - 1) * (slab + pad) + slab, np.uint8)
+    for e in range(E):
+        w[e * (slab + pad):e * (slab + pad) + slab] = c["w"][e * slab:(e + 1) * slab]
+    return dict(c, w=w, expert_stride=slab + pad)
+
+
+@pytest.mark.parametrize("T", [5, 40])   # the mat-vec route and the grouped route
+@pytest.mark.parametrize("K,pad,offset", [
+    (128, 2, 0),    # expert stride 2 mod 4
+    (128, 0, 2),    # w itself only 2-byte aligned
+    (96, 2, 2),     # both, with an odd block count
+    (256, 6, 2),    # both, 4-byte multiples of rows
+])
+def test_qmm_id_q4_0_two_byte_aligned_weights(T, K, pad, offset):
+    E, N, top_k = 5, 72, 2
+    base = synth.moe_case(E, N, K, T, top_k, seed=K + pad + offset + T)
+    c = _restride(base, pad)
+    buf = torch.zeros(c["w"].size + 16, dtype=torch.uint8, device=DEV)
+    w = buf[offset:offset + c["w"].size]
+    w.copy_(torch.from_numpy(c["w"]).to(DEV))
+    assert w.data_ptr() % 4 == offset % 4
+    x, idt = _t(c["x"]), _t(c["ids"].view(np.int32))
+    out = B.qmm_id_q4_0(x, w, idt, T, top_k, N, K, E, c["expert_stride"])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], T, top_k, N, K, E, c["expert_stride"])
+    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(base), f"moe K={K} pad={pad} offset={offset} T={T}")
 
 
 def test_qmm_id_q4_0_full_size_sampled():

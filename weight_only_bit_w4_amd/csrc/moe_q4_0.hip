@@ -15,7 +15,9 @@
 //     Weights and the routed rows' x stream through a 3-slot LDS ring by
 //     buffer-to-LDS DMA, one 128-wide K window (4 Q4_0 blocks, 72 bytes of
 //     each weight row) per step; each lane decodes two qs dwords per block
-//     into fp16 (q - 8) d.
+//     into fp16 (q - 8) d. Rows that may start 2 bytes past a dword (an odd
+//     block count, or w or the expert stride 2 mod 4) take a realigning
+//     form of the same kernel.
 #include <type_traits>
 
 #include <atomic>
@@ -203,6 +205,17 @@ struct MoeOps {
     uint32_t we[kMoeWinBlocks / 2][4];  // even blocks: the four dwords that cover the lane's two qs dwords
     uint32_t wo[kMoeWinBlocks / 2][2];  // odd blocks: the lane's two qs dwords
 };
+// The realigning form, for rows whose windows may start 2 bytes past a dword
+// (an odd number of blocks per row, or w or the expert stride only 2-byte
+// aligned): each row is moved from the dword at or below its window, so its
+// window starts `phase` (0 or 2) bytes into its LDS image, and every block's
+// two qs dwords are read as 16-bit halves.
+typedef uint16_t u16x2 __attribute__((__vector_size__(2 * sizeof(uint16_t))));
+struct MoeOpsR {
+    u32x4 x[kMoeWinBlocks][2];
+    uint32_t d[kMoeWinBlocks];
+    uint32_t qs[kMoeWinBlocks][2];
+};
 // A lane's LDS read addresses (byte addresses) in slot 0 of the rings; slot
 // s adds s slot sizes, folded into the instructions' 16-bit offsets. The
 // register fence keeps each address whole in one register (otherwise the
@@ -212,11 +225,16 @@ struct MoeLane {
     uint32_t w;        // the lane's weight row in the window: block b's d at +18 b
     uint32_t wq;       // + 4 h: even block b's covering dwords at +18 b .. +18 b + 12, odd block b's qs at +18 b + 2, +10
     uint32_t x[kMoeWinBlocks][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
+    // Realigning form: w includes the row's phase, and the lane's qs dword
+    // 2 s + h of block b starts at wq + 18 b + 2 + 8 s, 2-byte aligned.
 };
-__device__ __forceinline__ MoeLane moe_lane(const uint8_t* wring, const uint8_t* xring, int nl, int lane) {
+template <bool RE>
+__device__ __forceinline__ MoeLane moe_lane(const uint8_t* wring, const uint8_t* xring, int nl, int lane,
+                                            uint32_t phase) {
     const int h = lane >> 5, m = lane & 31, sw = m & 15;
     MoeLane l;
-    l.w = moe_lds_addr(wring) + nl * kMoeSpan;
+    const uint32_t row = moe_lds_addr(wring) + nl * kMoeSpan;
+    l.w = row + (RE ? phase : 0u);
     l.wq = l.w + 4 * h;
     asm volatile("" : "+v"(l.w), "+v"(l.wq));
 #pragma unroll
@@ -253,6 +271,40 @@ __device__ __forceinline__ MoeOps moe_read(const MoeLane& l) {
     }
     return o;
 }
+template <int SLOT>
+__device__ __forceinline__ MoeOpsR moe_read_r(const MoeLane& l) {
+    MoeOpsR o;
+#pragma unroll
+    for (int b = 0; b < kMoeWinBlocks; ++b)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) o.x[b][s] = moe_lds_load<u32x4>(l.x[b][s] + SLOT * kMoeXSlot);
+    const uint32_t w = l.w + SLOT * kMoeWSlot, wq = l.wq + SLOT * kMoeWSlot;
+#pragma unroll
+    for (int b = 0; b < kMoeWinBlocks; ++b) {
+        o.d[b] = moe_lds_load<uint16_t>(w + 18 * b);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            u16x2 v;
+            v[0] = moe_lds_load<uint16_t>(wq + 18 * b + 2 + 8 * s);
+            v[1] = moe_lds_load<uint16_t>(wq + 18 * b + 4 + 8 * s);
+            o.qs[b][s] = __builtin_bit_cast(uint32_t, v);
+        }
+    }
+    return o;
+}
+// Blocks at or past `live` (a part last window when K % 128 != 0) get d = 0,
+// which zeroes their weights whatever the ring holds there; their x chunks
+// were loaded as zeros.
+__device__ __forceinline__ void moe_apply_r(const MoeOpsR& o, const Q4Consts& k, f32x16& acc, int live) {
+#pragma unroll
+    for (int b = 0; b < kMoeWinBlocks; ++b) {
+        const f16x2 dd = as_f16x2((b == 0 || b < live ? o.d[b] : 0u) * 0x10001u);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.x[b][s]),
+                                                         __builtin_bit_cast(f16x8, q4_0_operand(o.qs[b][s], dd, k)), acc, 0, 0, 0);
+    }
+}
 // Blocks at or past `live` (the half last window when K % 128 == 64) get
 // d = 0, which zeroes their weights whatever the ring holds there; their x
 // chunks were loaded as zeros.
@@ -286,9 +338,9 @@ __device__ __forceinline__ void moe_wait_lgkm() { asm volatile("s_waitcnt lgkmcn
 // window j - 1, which every wavefront finished reading before barrier j; each
 // wavefront waits for its own DMA of window j before barrier j, after which
 // every wavefront may read it. All DMA offsets are per-lane (no scalar
-// offset), so the descriptors' range checks cover every byte read: the 8
-// bytes read past a row's last window are the next row's (unused) or, past the
-// chunk's last row, zeros.
+// offset), so the descriptors' range checks cover every byte read: the 6 or
+// 8 bytes read past a row's last window are the next row's (unused) or, past
+// the chunk's last row, zeros.
 constexpr int kMoeLds = kMoeStages * (kMoeWSlot + kMoeXSlot) + kMoeMR * 4;
 
 template <int N>
@@ -302,6 +354,7 @@ __device__ __forceinline__ void moe_wait_window(int per_window) {
     }
 }
 
+template <bool RE>
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ scratch,
                                                                float* __restrict__ out, int N, int K, int top_k,
                                                                uint64_t expert_stride, IdScratchLayout lay, int n_tokens,
@@ -321,7 +374,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = K / 32;
     const int nwin = (nb + kMoeWinBlocks - 1) / kMoeWinBlocks;
-    const int last_live = nb - kMoeWinBlocks * (nwin - 1);  // blocks in the last window (2 or 4)
+    const int last_live = nb - kMoeWinBlocks * (nwin - 1);  // blocks in the last window (1 to 4)
     const uint32_t row_bytes = (uint32_t)nb * 18u;
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(scratch + lay.xh, (uint32_t)((size_t)n_tokens * (size_t)K * 2u));
     const Q4Consts k{vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u), vreg(0x54005400u)};
@@ -344,15 +397,19 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
         for (int tc = t_begin; tc < t_end; tc += kMoeWaves) {
             const int n0 = tc * kMoeTile;
             const int crow = min(min(t_end - tc, kMoeWaves) * kMoeTile, N - n0);
+            // The realigning form reads from the dword at or below the chunk
+            // (delta bytes before it) through the dword holding its last byte.
+            const uint8_t* const chunk = w + (size_t)e * expert_stride + (size_t)n0 * row_bytes;
+            const uint32_t delta = RE ? (uint32_t)((uintptr_t)chunk & 3u) : 0u;
             const __amdgpu_buffer_rsrc_t wsrc =
-                make_rsrc(w + (size_t)e * expert_stride + (size_t)n0 * row_bytes, (uint32_t)crow * row_bytes);
+                make_rsrc(chunk - delta, RE ? ((uint32_t)crow * row_bytes + delta + 3u) & ~3u : (uint32_t)crow * row_bytes);
             const int n_wi = (crow * (kMoeSpan / 16) + 63) / 64;  // W DMA instructions per window
             const int nw = (wi0 < n_wi ? 1 : 0) + (wi0 + kMoeWaves < n_wi ? 1 : 0) + (wi0 + 2 * kMoeWaves < n_wi ? 1 : 0);
             uint32_t wo[3];
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 const int q = 64 * (wi0 + kMoeWaves * t) + lane, r = q / 5, j = q % 5;
-                wo[t] = r < crow ? (uint32_t)r * row_bytes + 16u * (uint32_t)j : kMoeOob;
+                wo[t] = r < crow ? (((uint32_t)r * row_bytes + delta) & ~3u) + 16u * (uint32_t)j : kMoeOob;
             }
             // DMA of window win into ring slot SLOT (= win % kMoeStages).
             auto issue_w = [&](auto slot_c, int win) {
@@ -365,7 +422,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
             };
             auto issue_x = [&](auto slot_c, int win) {
                 constexpr int slot = decltype(slot_c)::value;
-                // Chunks of blocks past K (a half last window) land as zeros.
+                // Chunks of blocks past K (a part last window) land as zeros.
                 if (x_dma)
                     moe_dma16(xsrc, xring + slot * kMoeXSlot + 1024 * wave,
                               kMoeWinBlocks * win + (xc >> 2) < nb ? xo + (uint32_t)(kMoeXRow * win) : kMoeOob, 0);
@@ -418,30 +475,43 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
             for (int i = 0; i < 16; ++i) acc[i] = 0.f;
             const bool busy = kMoeTile * wave < crow;
             const int nl = kMoeTile * wave + (lane & 31);  // this lane's weight row in the chunk
-            const MoeLane ln = moe_lane(wring, xring, nl, lane);
+            const MoeLane ln = moe_lane<RE>(wring, xring, nl, lane, ((uint32_t)nl * row_bytes + delta) & 3u);
             // Two operand sets alternate (the loop is unrolled by six, a multiple
             // of the ring depth, so that neither set is copied and every slot
             // offset is a constant): after barrier j a wavefront reads window j
             // into one set, then decodes and multiplies window j - 1 from the
             // other.
-            MoeOps ops[2];
+            using Ops = std::conditional_t<RE, MoeOpsR, MoeOps>;
+            auto read = [&](auto slot_c) {
+                if constexpr (RE)
+                    return moe_read_r<decltype(slot_c)::value>(ln);
+                else
+                    return moe_read<decltype(slot_c)::value>(ln);
+            };
+            auto apply = [&](const Ops& o, int live) {
+                if constexpr (RE)
+                    moe_apply_r(o, k, acc, live);
+                else
+                    moe_apply(o, k, acc, live);
+            };
+            Ops ops[2];
             wait_window(0);
             moe_wait_lgkm();  // pass_rows written
             moe_barrier();
-            if (busy) ops[0] = moe_read<0>(ln);
+            if (busy) ops[0] = read(S0{});
             if (kMoeStages - 1 < nwin) {
                 issue_w(S2{}, kMoeStages - 1);
                 issue_x(S2{}, kMoeStages - 1);
             }
-            auto step = [&](auto slot_c, int j, MoeOps& into, const MoeOps& from) {
+            auto step = [&](auto slot_c, int j, Ops& into, const Ops& from) {
                 constexpr int slot = decltype(slot_c)::value;
                 wait_window(j);
                 moe_wait_lgkm();  // this wavefront's reads of window j - 1 are done: its slot is reused below
                 moe_barrier();
                 if (busy) {
-                    into = moe_read<slot>(ln);
+                    into = read(slot_c);
                     __builtin_amdgcn_sched_barrier(0);  // the reads go out before the arithmetic below
-                    moe_apply(from, k, acc, kMoeWinBlocks);
+                    apply(from, kMoeWinBlocks);
                 }
                 if (j + kMoeStages - 1 < nwin) {
                     using Next = std::integral_constant<int, (slot + kMoeStages - 1) % kMoeStages>;
@@ -465,9 +535,9 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
             if (j + 4 < nwin) step(S2{}, j + 4, ops[1], ops[0]);
             if (busy) {
                 if ((nwin - 1) & 1)  // the last window's set
-                    moe_apply(ops[1], k, acc, last_live);
+                    apply(ops[1], last_live);
                 else
-                    moe_apply(ops[0], k, acc, last_live);
+                    apply(ops[0], last_live);
                 // Lane (n, h) holds routed rows 8 (i / 4) + 4 h + i % 4 of weight row n.
                 const int ncol = n0 + nl;
                 uint32_t pr = moe_lds_addr(pass_rows) + 16u * (uint32_t)(lane >> 5);  // row 4 h's id
@@ -806,11 +876,6 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
         mv_launch<false>(x, nullptr, w, ids, out, bad, p, s, events);
         return launch_status("qmm_id_q4_0 (mat-vec route)");
     }
-    if (p->k % 64 != 0)
-        return fail(W4_EUNSUPPORTED,
-                    "qmm_id_q4_0: above 32 tokens, implemented for K %% 64 == 0 (whole 36-byte block pairs), got %u", p->k);
-    if (((uintptr_t)w & 3u) || (p->expert_stride & 3u))
-        return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: above 32 tokens, implemented for 4-byte-aligned w and expert_stride");
     // Buffer descriptors cover the binary16 x copy and one 384-row weight chunk
     // in 32 bits, with in-range offsets below the out-of-range marker 2^31.
     if ((uint64_t)p->n_tokens * p->k * 2u >= (1ull << 32) || (uint64_t)kMoeChunkRows * (p->k / 32) * 18u >= (1ull << 31))
@@ -828,8 +893,11 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
     // experts together fill the CUs once (one workgroup per CU fits).
     const uint32_t tiles = (p->n + kMoeTile - 1) / kMoeTile;
     const uint32_t splits = std::max(1u, std::min(tiles, ((uint32_t)kCUs + p->n_experts - 1) / p->n_experts));
-    hipLaunchKernelGGL(moe_gemm_kernel, dim3(p->n_experts * splits), dim3(kMoeThreads), 0, s, w, (const uint8_t*)scratch,
-                       out, (int)p->n, (int)p->k, (int)p->top_k, p->expert_stride, lay, (int)p->n_tokens, (int)splits);
+    // Rows whose windows may start off a dword boundary take the realigning form.
+    const bool realign = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
+    hipLaunchKernelGGL(realign ? moe_gemm_kernel<true> : moe_gemm_kernel<false>, dim3(p->n_experts * splits),
+                       dim3(kMoeThreads), 0, s, w, (const uint8_t*)scratch, out, (int)p->n, (int)p->k, (int)p->top_k,
+                       p->expert_stride, lay, (int)p->n_tokens, (int)splits);
     return launch_status("qmm_id_q4_0 (grouped GEMM)");
 }
 
