@@ -172,9 +172,12 @@ w4_status qmm_lut4_f32(const float* x, const uint8_t* packed, const float* scale
  *     mat-vec launch; each selected expert's weights are read once and
  *     applied to every routed row that selects it. Scratch holds only the
  *     bad-id count.
- *   - otherwise: the routed rows are grouped by expert into scratch (and x
- *     is stored there as binary16) before a grouped matrix-core GEMM reads
- *     them ([P3] map0 + mm, caller-owned scratch as in IdMmScratch).
+ *   - otherwise a grouped matrix-core GEMM ([P3] map0 + mm): up to 4096
+ *     routed rows in one launch, whose workgroups each list their expert's
+ *     routed rows and round x to binary16 themselves (scratch holds only the
+ *     bad-id count); above that, the routed rows are first grouped by
+ *     expert into scratch, with x stored there as binary16 (caller-owned
+ *     scratch as in IdMmScratch).
  * Both routes round x to binary16 (round to nearest even) before the
  * products: a finite |x| of 65520 or more becomes an infinity (its routed
  * rows' outputs are not finite) and is counted by w4_range_events;

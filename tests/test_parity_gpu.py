@@ -394,6 +394,8 @@ def _max_d(c):
     (2500, 16, 64, 40, 2),   # more experts than grouping threads: 3 experts per scan segment
     (16, 64, 128, 288, 8),   # 2304 routed rows, 144 per expert: five passes of 32
     (5, 64, 128, 461, 5),    # 2305 routed rows over 5 experts: a last pass of 1 row for some
+    (16, 64, 128, 600, 8),   # 4800 routed rows: past the one-launch route, grouped in scratch first
+    (8, 96, 96, 700, 6),     # 4200 routed rows with 3 blocks per row: the two-launch realigning form
     # mat-vec route (at most 32 tokens)
     (4, 40, 128, 3, 2),      # tiny, N not a multiple of the 32-row tile
     (8, 200, 320, 9, 3),     # 10 blocks: a ragged first chunk

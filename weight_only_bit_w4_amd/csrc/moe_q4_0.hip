@@ -2,7 +2,9 @@
 // page): out[t*top_k + s][n] = sum_k (q - 8) d of expert ids[t*top_k + s],
 // row n, times x[t][k].
 //
-// Two launches on the caller's stream, as the page's map0 + mm pair:
+// Above the mat-vec threshold, up to 4096 routed rows take one launch
+// (moe_fused_kernel, below the grouped GEMM); more take two launches on the
+// caller's stream, as the page's map0 + mm pair:
 //  1. moe_group_kernel: workgroup 0 counts the routed rows per expert, scans
 //     the counts and scatters row indices into per-expert lists (the page's
 //     htpe / hids); the other workgroups store x as binary16 (the matrix-core
@@ -14,7 +16,7 @@
 //     v_mfma_f32_32x32x16_f16, f32 accumulation, one tile per wavefront.
 //     Weights and the routed rows' x stream through a 3-slot LDS ring by
 //     buffer-to-LDS DMA, one 128-wide K window (4 Q4_0 blocks, 72 bytes of
-//     each weight row) per step; each lane decodes two qs dwords per block
+//     each weight row) per step; each lane decodes two blocks' qs dwords
 //     into fp16 (q - 8) d. Rows that may start 2 bytes past a dword (an odd
 //     block count, or w or the expert stride 2 mod 4) take a realigning
 //     form of the same kernel.
@@ -191,30 +193,35 @@ __device__ __forceinline__ u32x4 q4_0_operand(uint32_t qs, f16x2 dd, const Q4Con
 }
 
 // One 128-wide K window for a wavefront's 32 weight rows against the pass's
-// 32 routed rows: four blocks b, two MFMA k-steps s each. Lane (n, h) =
-// (lane % 32, lane / 32) feeds step s of block b with qs dword 2 s + h of
-// weight row n; the x operand of lane (m, h) is the same eight elements of
-// routed row m, which the xh order stores as the 16-byte chunk 4 b + 2 s + h
-// of the window row (kept at slot chunk ^ (m % 16), which keeps the 32-row
-// reads conflict-free). The window's LDS reads (moe_read) are issued a window
-// ahead of its arithmetic (moe_apply), so they overlap the previous window's
-// decode and matrix work instead of following each barrier.
+// 32 routed rows: eight MFMA k-steps t. Lane (n, h) = (lane % 32, lane / 32)
+// takes blocks 2 h and 2 h + 1 of weight row n's window and in step t feeds
+// qs dword t % 4 of block 2 h + t / 4. The x operand of lane (m, h) in step t
+// is the same eight elements of routed row m: in the xh order the 16-byte
+// chunk 4 (2 h + t / 4) + t % 4 = t + 8 h of the window row, kept at slot
+// chunk ^ (m % 16) so that the 32-row reads are conflict-free. A lane reads
+// its two blocks as 40 bytes of its row's 80-byte image (h = 0: bytes
+// 0 .. 39, h = 1: bytes 32 .. 71) by two 16-byte reads, which eight lanes of
+// consecutive rows spread over all 32 banks, and one 8-byte read. Every
+// byte read is used: a dead part of a read's destination would let the
+// compiler reuse it as a temporary and wait for the whole read first. The
+// window's LDS reads (moe_read) are issued a window ahead of its arithmetic
+// (moe_apply), so they overlap the previous window's decode and matrix work
+// instead of following each barrier.
 struct MoeOps {
-    u32x4 x[kMoeWinBlocks][2];       // x operands [block][step]
-    uint32_t d[kMoeWinBlocks];       // block scales (binary16)
-    uint32_t we[kMoeWinBlocks / 2][4];  // even blocks: the four dwords that cover the lane's two qs dwords
-    uint32_t wo[kMoeWinBlocks / 2][2];  // odd blocks: the lane's two qs dwords
+    u32x4 x[8];  // x operands per step
+    u32x4 w[2];  // the lane's first 32 bytes
+    u32x2 w2;    // and the 8 after them
 };
 // The realigning form, for rows whose windows may start 2 bytes past a dword
 // (an odd number of blocks per row, or w or the expert stride only 2-byte
 // aligned): each row is moved from the dword at or below its window, so its
-// window starts `phase` (0 or 2) bytes into its LDS image, and every block's
-// two qs dwords are read as 16-bit halves.
+// window starts `phase` (0 or 2) bytes into its LDS image, and the lane's
+// scales and qs dwords are read as 16-bit halves.
 typedef uint16_t u16x2 __attribute__((__vector_size__(2 * sizeof(uint16_t))));
 struct MoeOpsR {
-    u32x4 x[kMoeWinBlocks][2];
-    uint32_t d[kMoeWinBlocks];
-    uint32_t qs[kMoeWinBlocks][2];
+    u32x4 x[8];
+    uint32_t d[2];      // the lane's blocks' scales (binary16)
+    uint32_t qs[2][4];  // and their qs dwords
 };
 // A lane's LDS read addresses (byte addresses) in slot 0 of the rings; slot
 // s adds s slot sizes, folded into the instructions' 16-bit offsets. The
@@ -222,109 +229,112 @@ struct MoeOpsR {
 // compiler folds the ring base into the offset, overflows the field and
 // adds it back per read).
 struct MoeLane {
-    uint32_t w;        // the lane's weight row in the window: block b's d at +18 b
-    uint32_t wq;       // + 4 h: even block b's covering dwords at +18 b .. +18 b + 12, odd block b's qs at +18 b + 2, +10
-    uint32_t x[kMoeWinBlocks][2];  // x chunk 4 b + 2 s + h of routed row m, at its swizzled slot
-    // Realigning form: w includes the row's phase, and the lane's qs dword
-    // 2 s + h of block b starts at wq + 18 b + 2 + 8 s, 2-byte aligned.
+    // aligned form: the lane's first piece, row image + 32 h; realigning
+    // form: its first block, row image + phase + 36 h (the second block 18
+    // bytes on; in each, d then the four qs dwords)
+    uint32_t w;
+    // step t's x chunk t + 8 h of routed row m, at its swizzled slot; in the
+    // padded x layout (rows kMoeXRowP bytes apart, chunks in order) only x[0]
+    // is set, and step t's chunk is 16 t bytes after it
+    uint32_t x[8];
 };
-template <bool RE>
+constexpr int kMoeXRowP = kMoeXRow + 16;       // padded x row: 32-row reads conflict-free without a swizzle
+constexpr int kMoeXSlotP = kMoeMR * kMoeXRowP;  // 8.5 KB
+template <bool RE, bool PAD = false>
 __device__ __forceinline__ MoeLane moe_lane(const uint8_t* wring, const uint8_t* xring, int nl, int lane,
                                             uint32_t phase) {
     const int h = lane >> 5, m = lane & 31, sw = m & 15;
     MoeLane l;
-    const uint32_t row = moe_lds_addr(wring) + nl * kMoeSpan;
-    l.w = row + (RE ? phase : 0u);
-    l.wq = l.w + 4 * h;
-    asm volatile("" : "+v"(l.w), "+v"(l.wq));
+    l.w = moe_lds_addr(wring) + nl * kMoeSpan + (RE ? phase + 36u * h : 32u * h);
+    asm volatile("" : "+v"(l.w));
+    if constexpr (PAD) {
+        l.x[0] = moe_lds_addr(xring) + m * kMoeXRowP + 128 * h;
+        asm volatile("" : "+v"(l.x[0]));
+    } else {
 #pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            l.x[b][s] = moe_lds_addr(xring) + m * kMoeXRow + 16 * ((4 * b + 2 * s + h) ^ sw);
-            asm volatile("" : "+v"(l.x[b][s]));
+        for (int t = 0; t < 8; ++t) {
+            l.x[t] = moe_lds_addr(xring) + m * kMoeXRow + 16 * ((t + 8 * h) ^ sw);
+            asm volatile("" : "+v"(l.x[t]));
         }
+    }
     return l;
+}
+template <int SLOT, bool PAD>
+__device__ __forceinline__ uint32_t moe_x_addr(const MoeLane& l, int t) {
+    return PAD ? l.x[0] + 16 * t + SLOT * kMoeXSlotP : l.x[t] + SLOT * kMoeXSlot;
 }
 template <typename T>
 __device__ __forceinline__ T moe_lds_load(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
 }
-template <int SLOT>
+template <int SLOT, bool PAD = false>
 __device__ __forceinline__ MoeOps moe_read(const MoeLane& l) {
     MoeOps o;
 #pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b)
+    for (int t = 0; t < 8; ++t) o.x[t] = moe_lds_load<u32x4>(moe_x_addr<SLOT, PAD>(l, t));
 #pragma unroll
-        for (int s = 0; s < 2; ++s) o.x[b][s] = moe_lds_load<u32x4>(l.x[b][s] + SLOT * kMoeXSlot);
-    // Block b at byte 18 b of the row's window: d, then qs, which starts two
-    // bytes past a dword boundary for even b and on one for odd b.
-    const uint32_t w = l.w + SLOT * kMoeWSlot, wq = l.wq + SLOT * kMoeWSlot;
-#pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b) o.d[b] = moe_lds_load<uint16_t>(w + 18 * b);
-#pragma unroll
-    for (int e = 0; e < kMoeWinBlocks / 2; ++e) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.we[e][i] = moe_lds_load<uint32_t>(wq + 36 * e + 4 * i);
-        o.wo[e][0] = moe_lds_load<uint32_t>(wq + 36 * e + 20);
-        o.wo[e][1] = moe_lds_load<uint32_t>(wq + 36 * e + 28);
-    }
+    for (int i = 0; i < 2; ++i) o.w[i] = moe_lds_load<u32x4>(l.w + SLOT * kMoeWSlot + 16 * i);
+    o.w2 = moe_lds_load<u32x2>(l.w + SLOT * kMoeWSlot + 32);
     return o;
 }
-template <int SLOT>
+template <int SLOT, bool PAD = false>
 __device__ __forceinline__ MoeOpsR moe_read_r(const MoeLane& l) {
     MoeOpsR o;
 #pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b)
+    for (int t = 0; t < 8; ++t) o.x[t] = moe_lds_load<u32x4>(moe_x_addr<SLOT, PAD>(l, t));
+    const uint32_t w = l.w + SLOT * kMoeWSlot;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) o.x[b][s] = moe_lds_load<u32x4>(l.x[b][s] + SLOT * kMoeXSlot);
-    const uint32_t w = l.w + SLOT * kMoeWSlot, wq = l.wq + SLOT * kMoeWSlot;
-#pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b) {
+    for (int b = 0; b < 2; ++b) {
         o.d[b] = moe_lds_load<uint16_t>(w + 18 * b);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int i = 0; i < 4; ++i) {
             u16x2 v;
-            v[0] = moe_lds_load<uint16_t>(wq + 18 * b + 2 + 8 * s);
-            v[1] = moe_lds_load<uint16_t>(wq + 18 * b + 4 + 8 * s);
-            o.qs[b][s] = __builtin_bit_cast(uint32_t, v);
+            v[0] = moe_lds_load<uint16_t>(w + 18 * b + 2 + 4 * i);
+            v[1] = moe_lds_load<uint16_t>(w + 18 * b + 4 + 4 * i);
+            o.qs[b][i] = __builtin_bit_cast(uint32_t, v);
         }
     }
     return o;
 }
-// Blocks at or past `live` (a part last window when K % 128 != 0) get d = 0,
-// which zeroes their weights whatever the ring holds there; their x chunks
-// were loaded as zeros.
-__device__ __forceinline__ void moe_apply_r(const MoeOpsR& o, const Q4Consts& k, f32x16& acc, int live) {
+// The eight steps from the lane's two blocks' scales and qs dwords. Blocks at
+// or past `live` (a part last window when K % 128 != 0) get d = 0, which
+// zeroes their weights whatever the ring holds there; their x chunks were
+// loaded as zeros.
+__device__ __forceinline__ void moe_steps(const u32x4 (&x)[8], const uint32_t (&d)[2], const uint32_t (&qs)[2][4],
+                                          int h, const Q4Consts& k, f32x16& acc, int live) {
 #pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b) {
-        const f16x2 dd = as_f16x2((b == 0 || b < live ? o.d[b] : 0u) * 0x10001u);
+    for (int b = 0; b < 2; ++b) {
+        const f16x2 dd = as_f16x2((2 * h + b < live ? d[b] & 0xFFFFu : 0u) * 0x10001u);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.x[b][s]),
-                                                         __builtin_bit_cast(f16x8, q4_0_operand(o.qs[b][s], dd, k)), acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x[4 * b + i]),
+                                                         __builtin_bit_cast(f16x8, q4_0_operand(qs[b][i], dd, k)), acc, 0, 0, 0);
     }
 }
-// Blocks at or past `live` (the half last window when K % 128 == 64) get
-// d = 0, which zeroes their weights whatever the ring holds there; their x
-// chunks were loaded as zeros.
-__device__ __forceinline__ void moe_apply(const MoeOps& o, const Q4Consts& k, f32x16& acc, int live) {
+__device__ __forceinline__ void moe_apply_r(const MoeOpsR& o, int h, const Q4Consts& k, f32x16& acc, int live) {
+    moe_steps(o.x, o.d, o.qs, h, k, acc, live);
+}
+// Aligned form: h = 0 lanes' blocks start at byte 0 of what they read, h = 1
+// lanes' at byte 4 (window byte 36); with the dwords shifted down one for
+// h = 1, block 2 h sits at bytes 0 .. 17 and block 2 h + 1 at 18 .. 35.
+__device__ __forceinline__ void moe_apply(const MoeOps& o, int h, const Q4Consts& k, f32x16& acc, int live) {
+    uint32_t r[10], s[9];
 #pragma unroll
-    for (int b = 0; b < kMoeWinBlocks; ++b) {
-        uint32_t qs[2];
-        if (b % 2 == 0) {
-            qs[0] = __builtin_amdgcn_alignbyte(o.we[b / 2][1], o.we[b / 2][0], 2);
-            qs[1] = __builtin_amdgcn_alignbyte(o.we[b / 2][3], o.we[b / 2][2], 2);
-        } else {
-            qs[0] = o.wo[b / 2][0];
-            qs[1] = o.wo[b / 2][1];
-        }
-        const f16x2 dd = as_f16x2((b < kMoeWinBlocks / 2 || b < live ? o.d[b] : 0u) * 0x10001u);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, o.x[b][s]),
-                                                         __builtin_bit_cast(f16x8, q4_0_operand(qs[s], dd, k)), acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) r[4 * i + j] = o.w[i][j];
+    r[8] = o.w2[0];
+    r[9] = o.w2[1];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) s[i] = h ? r[i + 1] : r[i];
+    const uint32_t d[2] = {s[0], s[4] >> 16};
+    uint32_t qs[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qs[0][i] = __builtin_amdgcn_alignbyte(s[i + 1], s[i], 2);
+        qs[1][i] = s[5 + i];
     }
+    moe_steps(o.x, d, qs, h, k, acc, live);
 }
 __device__ __forceinline__ void moe_wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -342,17 +352,6 @@ __device__ __forceinline__ void moe_wait_lgkm() { asm volatile("s_waitcnt lgkmcn
 // 8 bytes read past a row's last window are the next row's (unused) or, past
 // the chunk's last row, zeros.
 constexpr int kMoeLds = kMoeStages * (kMoeWSlot + kMoeXSlot) + kMoeMR * 4;
-
-template <int N>
-__device__ __forceinline__ void moe_wait_window(int per_window) {
-    // windows j + 1 .. j + N may still be in flight
-    switch (per_window) {
-        case 0: moe_wait_vmcnt<0>(); break;
-        case 1: moe_wait_vmcnt<N>(); break;
-        case 2: moe_wait_vmcnt<2 * N>(); break;
-        default: moe_wait_vmcnt<3 * N>(); break;
-    }
-}
 
 template <bool RE>
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ scratch,
@@ -488,11 +487,12 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
                 else
                     return moe_read<decltype(slot_c)::value>(ln);
             };
+            const int h = lane >> 5;
             auto apply = [&](const Ops& o, int live) {
                 if constexpr (RE)
-                    moe_apply_r(o, k, acc, live);
+                    moe_apply_r(o, h, k, acc, live);
                 else
-                    moe_apply(o, k, acc, live);
+                    moe_apply(o, h, k, acc, live);
             };
             Ops ops[2];
             wait_window(0);
@@ -556,6 +556,302 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint8_t* __
     }
 }
 
+
+// ---------------------------------------------------------------- one-launch grouped route
+// Up to kFusedMaxRows routed rows the grouping pass and the binary16 copy of
+// x move into the GEMM's workgroups, and the route is one launch:
+//  - every workgroup scans the ids for its expert and lists the matching
+//    routed rows in LDS (in any order: an output row's arithmetic does not
+//    depend on its position in the tile); workgroup 0 also counts the ids
+//    that name no expert and writes their rows as zeros.
+//  - the routed rows' f32 x is moved by buffer-to-LDS DMA into a 2-slot
+//    staging ring, a window ahead, and the wavefront that moved a row rounds
+//    it to binary16 in the xh order into the x ring that the matrix steps
+//    read; rows past the pass's count are neither moved nor rounded.
+// The weight stream, the decode and the matrix steps are the grouped GEMM's.
+constexpr int kFusedMaxRows = 4096;
+constexpr int kFxRow = 32 * kMoeWinBlocks * 4;  // 512 bytes: a routed row's f32 x per window
+constexpr int kFxSlot = kMoeMR * kFxRow;        // 16 KB
+constexpr int kFusedLds = kMoeStages * (kMoeWSlot + kMoeXSlotP) + 2 * kFxSlot + kFusedMaxRows * 2 + kMoeMR * 4 + 16;
+static_assert(kFusedLds <= 160 * 1024, "the one-launch route's LDS");
+
+__device__ __forceinline__ void moe_wait_vm(int n) {
+    switch (n) {
+        case 0: moe_wait_vmcnt<0>(); break;
+        case 1: moe_wait_vmcnt<1>(); break;
+        case 2: moe_wait_vmcnt<2>(); break;
+        case 3: moe_wait_vmcnt<3>(); break;
+        case 4: moe_wait_vmcnt<4>(); break;
+        case 5: moe_wait_vmcnt<5>(); break;
+        case 6: moe_wait_vmcnt<6>(); break;
+        case 7: moe_wait_vmcnt<7>(); break;
+        default: moe_wait_vmcnt<8>(); break;
+    }
+}
+// The lane index computed where it is used (volatile, so the compiler neither
+// hoists it nor keeps it in a register across the loops).
+__device__ __forceinline__ uint32_t moe_lane_id() {
+    uint32_t v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ void moe_lds_store(uint32_t addr, const T& v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T*>((uintptr_t)addr) = v;
+}
+
+template <bool RE>
+__global__ __launch_bounds__(kMoeThreads) void moe_fused_kernel(const float* __restrict__ x, const uint8_t* __restrict__ w,
+                                                                const uint32_t* __restrict__ ids, float* __restrict__ out,
+                                                                uint32_t* __restrict__ bad_out, int N, int K, int top_k,
+                                                                int n_rows, int n_experts, uint64_t expert_stride,
+                                                                int n_tokens, int splits, uint32_t* __restrict__ events) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kFusedLds];
+    uint8_t* const wring = lds;
+    uint8_t* const xring = wring + kMoeStages * kMoeWSlot;
+    uint8_t* const xstage = xring + kMoeStages * kMoeXSlotP;
+    uint16_t* const list = reinterpret_cast<uint16_t*>(xstage + 2 * kFxSlot);
+    uint32_t* const pass_rows = reinterpret_cast<uint32_t*>(list + kFusedMaxRows);
+    uint32_t* const counters = pass_rows + kMoeMR;  // the list's length, the ids naming no expert
+    const int e = blockIdx.x / splits, part = blockIdx.x % splits;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles = (N + kMoeTile - 1) / kMoeTile;
+    const int t_begin = (int)((int64_t)part * tiles / splits), t_end = (int)((int64_t)(part + 1) * tiles / splits);
+    const int nb = K / 32;
+    const int nwin = (nb + kMoeWinBlocks - 1) / kMoeWinBlocks;
+    const uint32_t row_bytes = (uint32_t)nb * 18u;
+    const int wi0 = (wave + kMoeWaves - kMoeXDma) % kMoeWaves;  // this wavefront's W instructions: wi0 + 12 t
+
+    // The weight chunk of tiles tc .. : its descriptor, this wavefront's DMA
+    // offsets and instruction count.
+    int n0 = 0, crow = 0, nw = 0;
+    uint32_t delta = 0u, wo[3];
+    __amdgpu_buffer_rsrc_t wsrc;
+    auto setup = [&](int tc) {
+        n0 = tc * kMoeTile;
+        crow = min(min(t_end - tc, kMoeWaves) * kMoeTile, N - n0);
+        const uint8_t* const chunk = w + (size_t)e * expert_stride + (size_t)n0 * row_bytes;
+        delta = RE ? (uint32_t)((uintptr_t)chunk & 3u) : 0u;
+        wsrc = make_rsrc(chunk - delta, RE ? ((uint32_t)crow * row_bytes + delta + 3u) & ~3u : (uint32_t)crow * row_bytes);
+        const int n_wi = (crow * (kMoeSpan / 16) + 63) / 64;
+        nw = (wi0 < n_wi ? 1 : 0) + (wi0 + kMoeWaves < n_wi ? 1 : 0) + (wi0 + 2 * kMoeWaves < n_wi ? 1 : 0);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int q = 64 * (wi0 + kMoeWaves * t) + lane, r = q / 5, j = q % 5;
+            wo[t] = r < crow ? (((uint32_t)r * row_bytes + delta) & ~3u) + 16u * (uint32_t)j : kMoeOob;
+        }
+    };
+    // Window win's weights into ring slot SLOT.
+    auto issue_w = [&](auto slot_c, int win) {
+        constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            if (t < nw)
+                moe_dma16(wsrc, wring + slot * kMoeWSlot + 1024 * (wi0 + kMoeWaves * t), wo[t] + (uint32_t)(kMoeWinBytes * win), 0);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    // The first chunk's weights of windows 0 and 1 need no routing: they go
+    // out before the scan (whose loads wait for them too).
+    const bool early = t_begin < t_end;
+    if (early) {
+        setup(t_begin);
+        issue_w(S0{}, 0);
+        if (nwin > 1) issue_w(S1{}, 1);
+    }
+
+    // This expert's routed rows.
+    if (tid < 2) counters[tid] = 0u;
+    __syncthreads();
+    for (int r0 = 0; r0 < n_rows; r0 += kMoeThreads) {
+        const int r = r0 + tid;
+        const uint32_t id = r < n_rows ? ids[r] : 0u;
+        const bool mine = r < n_rows && id == (uint32_t)e;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(mine);
+        if (bal != 0u) {
+            uint32_t base = 0u;
+            if (lane == 0) base = atomicAdd(&counters[0], (uint32_t)__popcll(bal));
+            base = (uint32_t)__builtin_amdgcn_readfirstlane(base);
+            const uint64_t below = lane == 0 ? 0u : bal & (~0ull >> (64 - lane));
+            if (mine) list[base + (uint32_t)__popcll(below)] = (uint16_t)r;
+        }
+        if (blockIdx.x == 0 && r < n_rows && id >= (uint32_t)n_experts) {
+            atomicAdd(&counters[1], 1u);
+            for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = 0.f;  // no expert to read
+        }
+    }
+    moe_wait_vmcnt<0>();  // the early weights and the zero rows' stores: the DMA waits below count only DMA
+    __syncthreads();
+    const uint32_t cnt = counters[0];
+    if (blockIdx.x == 0 && tid == 0) *bad_out = counters[1];
+    if (cnt == 0u || t_begin >= t_end) return;
+
+    const int last_live = nb - kMoeWinBlocks * (nwin - 1);  // blocks in the last window (1 to 4)
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)((size_t)n_tokens * (size_t)K * 4u));
+    // masks as constants (one scalar operand per v_and_or_b32), magic values in VGPRs
+    const Q4Consts k{0x000F000Fu, 0x00F000F0u, vreg(0x64006400u), vreg(0x54005400u)};
+    // x wavefronts 0 .. 7: wavefront v moves and rounds routed rows 4 v .. 4 v + 3
+    // (DMA instruction 2 v + s: rows 4 v + 2 s + lane / 32, f32 piece lane % 32).
+    const bool x_wave = wave < kMoeMR / 4;
+    const bool count_events = part == 0;
+    bool oor = false;
+    static_assert(kMoeStages == 3, "the slot sequences below are written for three slots");
+
+    for (uint32_t m0 = 0; m0 < cnt; m0 += kMoeMR) {
+        const uint32_t mcnt = min((uint32_t)kMoeMR, cnt - m0);
+        moe_barrier();  // the previous pass's stores have read pass_rows
+        {
+            // the thread index afresh (not held in a register across the loops)
+            const uint32_t t = 64u * (uint32_t)wave + moe_lane_id();
+            if (t < (uint32_t)kMoeMR) pass_rows[t] = t < mcnt ? (uint32_t)list[m0 + t] : 0u;
+        }
+        uint32_t xo[2];
+        int nx = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t ln = moe_lane_id();  // afresh, as above
+            const uint32_t xr = 4u * (uint32_t)wave + 2u * (uint32_t)s + (ln >> 5);
+            xo[s] = x_wave && xr < mcnt ? ((uint32_t)list[m0 + xr] / (uint32_t)top_k) * (uint32_t)K * 4u + 16u * (ln & 31u)
+                                        : kMoeOob;
+            nx += x_wave && (uint32_t)(4 * wave + 2 * s) < mcnt ? 1 : 0;
+        }
+        for (int tc = t_begin; tc < t_end; tc += kMoeWaves) {
+            // the first chunk of the first pass: set up, windows 0 and 1 of its weights landed
+            const bool pre = m0 == 0 && tc == t_begin;
+            if (!pre) setup(tc);
+            const bool events_here = count_events && tc == t_begin;  // later chunks round the same x again
+            // Window win's x into staging slot ST, then (unless already out) its
+            // weights into ring slot SLOT.
+            auto issue = [&](auto st_c, auto slot_c, int win, bool with_w) {
+                constexpr int st = decltype(st_c)::value;
+                // f32 pieces of blocks past K (a part last window) land as zeros
+                const bool in_k = kMoeWinBlocks * win + ((lane & 31) >> 3) < nb;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (x_wave && (uint32_t)(4 * wave + 2 * s) < mcnt)
+                        moe_dma16(xsrc, xstage + st * kFxSlot + 1024 * (2 * wave + s),
+                                  in_k ? xo[s] + (uint32_t)(kFxRow * win) : kMoeOob, 0);
+                if (with_w) issue_w(slot_c, win);
+            };
+            // Round the routed rows' x of a window, staging slot ST -> x ring slot
+            // SLOT: lane (r, c) writes chunk c of row r in the xh order, from the
+            // two f32 pieces that hold it.
+            auto convert = [&](auto st_c, auto slot_c) {
+                constexpr int st = decltype(st_c)::value, slot = decltype(slot_c)::value;
+                const int r = 4 * wave + (lane >> 4), c = lane & 15;
+                if (x_wave && (uint32_t)r < mcnt) {
+                    const uint32_t src = moe_lds_addr(xstage) + st * kFxSlot + r * kFxRow + 16 * (8 * (c >> 2) + (c & 3));
+                    const f32x4 a = moe_lds_load<f32x4>(src), b = moe_lds_load<f32x4>(src + 64);
+                    moe_lds_store(moe_lds_addr(xring) + slot * kMoeXSlotP + r * kMoeXRowP + 16 * c,
+                                  u32x4{pack_f16x2(a[0], a[2]), pack_f16x2(b[0], b[2]), pack_f16x2(a[1], a[3]),
+                                        pack_f16x2(b[1], b[3])});
+                    if (events_here)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) oor |= out_of_f16_range(a[t]) || out_of_f16_range(b[t]);
+                }
+            };
+            f32x16 acc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+            const bool busy = kMoeTile * wave < crow;
+            const int nl = kMoeTile * wave + (lane & 31);
+            const MoeLane ln = moe_lane<RE, true>(wring, xring, nl, lane, ((uint32_t)nl * row_bytes + delta) & 3u);
+            const int h = lane >> 5;
+            using Ops = std::conditional_t<RE, MoeOpsR, MoeOps>;
+            auto read = [&](auto slot_c) {
+                if constexpr (RE)
+                    return moe_read_r<decltype(slot_c)::value, true>(ln);
+                else
+                    return moe_read<decltype(slot_c)::value, true>(ln);
+            };
+            auto apply = [&](const Ops& o, int live) {
+                if constexpr (RE)
+                    moe_apply_r(o, h, k, acc, live);
+                else
+                    moe_apply(o, h, k, acc, live);
+            };
+            // Per window this wavefront issues nx x then nw weight DMA
+            // instructions; waits count what may stay in flight behind the one
+            // awaited, in issue order.
+            const int per_window = nx + nw;
+            // Issue order: x(0) W(0) x(1) W(1), or, for the first chunk, x(0) x(1)
+            // after the weights' windows 0 and 1 have landed.
+            Ops ops[2];
+            issue(S0{}, S0{}, 0, !pre);
+            if (nwin > 1) issue(S1{}, S1{}, 1, !pre);
+            const int after_x0 = pre ? (nwin > 1 ? nx : 0) : nw + (nwin > 1 ? per_window : 0);
+            moe_wait_vm(after_x0);                                   // x(0)
+            convert(S0{}, S0{});
+            moe_wait_vm(pre ? after_x0 : (nwin > 1 ? per_window : 0));  // W(0)
+            moe_wait_lgkm();                                         // pass_rows, x(0) written
+            moe_barrier();
+            if (nwin > 2) issue(S0{}, S2{}, 2, true);
+            if (busy) ops[0] = read(S0{});
+            if (nwin > 1) {
+                moe_wait_vm((pre ? 0 : nw) + (nwin > 2 ? per_window : 0));  // x(1)
+                convert(S1{}, S1{});
+            }
+            // Step j: ring slot j % 3, staging parity j % 2.
+            auto step = [&](auto slot_c, auto par_c, int j, Ops& into, const Ops& from) {
+                constexpr int slot = decltype(slot_c)::value, par = decltype(par_c)::value;
+                moe_wait_vm(j + 1 < nwin ? per_window : 0);  // W(j); x(j) was rounded in step j - 1
+                moe_wait_lgkm();  // this wavefront's reads of window j - 1 and writes of x(j) are done
+                moe_barrier();
+                if (j + 2 < nwin) {
+                    using Next = std::integral_constant<int, (slot + 2) % 3>;
+                    issue(par_c, Next{}, j + 2, true);
+                }
+                if (busy) {
+                    into = read(slot_c);
+                    __builtin_amdgcn_sched_barrier(0);  // the reads go out before the arithmetic below
+                    apply(from, kMoeWinBlocks);
+                }
+                if (j + 1 < nwin) {
+                    using Other = std::integral_constant<int, 1 - par>;
+                    using Next = std::integral_constant<int, (slot + 1) % 3>;
+                    __builtin_amdgcn_sched_barrier(0);  // after the arithmetic: the set it read is free
+                    moe_wait_vm(nw + (j + 2 < nwin ? per_window : 0));  // x(j + 1)
+                    convert(Other{}, Next{});
+                }
+            };
+            int j = 1;  // j % 6 == 1 at the top of each round
+            for (; j + 5 < nwin; j += 6) {
+                step(S1{}, S1{}, j, ops[1], ops[0]);
+                step(S2{}, S0{}, j + 1, ops[0], ops[1]);
+                step(S0{}, S1{}, j + 2, ops[1], ops[0]);
+                step(S1{}, S0{}, j + 3, ops[0], ops[1]);
+                step(S2{}, S1{}, j + 4, ops[1], ops[0]);
+                step(S0{}, S0{}, j + 5, ops[0], ops[1]);
+            }
+            if (j < nwin) step(S1{}, S1{}, j, ops[1], ops[0]);
+            if (j + 1 < nwin) step(S2{}, S0{}, j + 1, ops[0], ops[1]);
+            if (j + 2 < nwin) step(S0{}, S1{}, j + 2, ops[1], ops[0]);
+            if (j + 3 < nwin) step(S1{}, S0{}, j + 3, ops[0], ops[1]);
+            if (j + 4 < nwin) step(S2{}, S1{}, j + 4, ops[1], ops[0]);
+            if (busy) {
+                if ((nwin - 1) & 1)  // the last window's set
+                    apply(ops[1], last_live);
+                else
+                    apply(ops[0], last_live);
+                const int ncol = n0 + nl;
+                uint32_t pr = moe_lds_addr(pass_rows) + 16u * (uint32_t)(lane >> 5);
+                asm volatile("" : "+v"(pr));
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t mm = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    const uint32_t row = moe_lds_load<uint32_t>(pr + 4u * (8 * (i >> 2) + (i & 3)));
+                    if (mm < mcnt && ncol < N) out[(size_t)row * N + ncol] = acc[i];
+                }
+            }
+            moe_wait_vmcnt<0>();  // stores done: the next chunk's DMA waits count only DMA
+            moe_wait_lgkm();
+            moe_barrier();        // every wavefront is done with the rings before the next chunk's DMA
+        }
+    }
+    if (__builtin_amdgcn_ballot_w64(oor) != 0 && moe_lane_id() == 0) atomicAdd(events, 1u);
+}
 
 // ---------------------------------------------------------------- mat-vec route
 // Below the page's routing threshold (n_tokens <= 32) a call is a set of
@@ -882,6 +1178,20 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
         return fail(W4_EUNSUPPORTED, "qmm_id_q4_0: implemented for n_tokens * K * 2 < 2^32 bytes and 384-row weight chunks below 2^31 bytes");
     st = range_counter(&events, "qmm_id_q4_0");
     if (st != W4_OK) return st;
+    // Rows whose windows may start off a dword boundary take the realigning form.
+    const bool realign = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
+    // Each expert's 32-row tiles are split over enough workgroups that the
+    // experts together fill the CUs once (one workgroup per CU fits).
+    const uint32_t tiles = (p->n + kMoeTile - 1) / kMoeTile;
+    const uint32_t splits = std::max(1u, std::min(tiles, ((uint32_t)kCUs + p->n_experts - 1) / p->n_experts));
+    if (n_routed <= (uint64_t)kFusedMaxRows && (uint64_t)p->n_tokens * p->k * 4u < (1ull << 31)) {
+        // One launch: grouping and the binary16 copy of x inside the GEMM.
+        uint32_t* bad = reinterpret_cast<uint32_t*>((uint8_t*)scratch + lay.bad_ids);
+        hipLaunchKernelGGL(realign ? moe_fused_kernel<true> : moe_fused_kernel<false>, dim3(p->n_experts * splits),
+                           dim3(kMoeThreads), 0, s, x, w, ids, out, bad, (int)p->n, (int)p->k, (int)p->top_k,
+                           (int)n_routed, (int)p->n_experts, p->expert_stride, (int)p->n_tokens, (int)splits, events);
+        return launch_status("qmm_id_q4_0 (one-launch grouped GEMM)");
+    }
     const int n_rows = (int)(p->n_tokens * p->top_k);
     const int64_t x_count = (int64_t)p->n_tokens * p->k;
     const int conv_blocks = (int)std::min<int64_t>(1024, (x_count / 8 + kGroupThreads - 1) / kGroupThreads);
@@ -889,12 +1199,6 @@ extern "C" w4_status qmm_id_q4_0(const float* x, const uint8_t* w, const uint32_
                        ids, x, (uint8_t*)scratch, out, n_rows, (int)p->n_experts, (int)p->n, x_count, lay, events);
     st = launch_status("qmm_id_q4_0 (group)");
     if (st != W4_OK) return st;
-    // Each expert's 32-row tiles are split over enough workgroups that the
-    // experts together fill the CUs once (one workgroup per CU fits).
-    const uint32_t tiles = (p->n + kMoeTile - 1) / kMoeTile;
-    const uint32_t splits = std::max(1u, std::min(tiles, ((uint32_t)kCUs + p->n_experts - 1) / p->n_experts));
-    // Rows whose windows may start off a dword boundary take the realigning form.
-    const bool realign = ((p->k / 32) & 1u) || ((uintptr_t)w & 3u) || (p->expert_stride & 3u);
     hipLaunchKernelGGL(realign ? moe_gemm_kernel<true> : moe_gemm_kernel<false>, dim3(p->n_experts * splits),
                        dim3(kMoeThreads), 0, s, w, (const uint8_t*)scratch, out, (int)p->n, (int)p->k, (int)p->top_k,
                        p->expert_stride, lay, (int)p->n_tokens, (int)splits);
