@@ -263,6 +263,11 @@ def main():
                                   max(5, warmup // 5), chunk=10)
         flops = 2.0 * M4 * N4 * K4
         result["lut"] = {"ms": ms, "ms_median": med, "TFLOPs": flops / (ms * 1e-3) / 1e12, "launches": n4}
+        # the same bytes read as a weight stored [K, N] (transpose == 0): the matrix-core [K, N] route
+        log(f"lut [K, N]: qmm_lut4 transpose=0 M={M4} K={K4} N={N4} block {blk}, {n4} launches")
+        ms, med = timer.run_stats(lambda i: B.qmm_lut4(x4, p4, s4, c4["book"], N4, blk, y=y4, transpose=0), n4,
+                                  max(5, warmup // 5), chunk=10)
+        result["lut_kn"] = {"ms": ms, "ms_median": med, "TFLOPs": flops / (ms * 1e-3) / 1e12, "launches": n4}
         del x4, p4, s4, y4
 
     # ------------------------------------------------------------ lookup codebook, single precision, 4 rows
@@ -547,10 +552,18 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(p["TFLOPs"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic("lut")}}
+    if "lut_kn" in result:
+        p = result["lut_kn"]
+        comps["lut_gemm_kn"] = {
+            "workload": "qmm_lut4 M=512 K=4096 N=11008 block 64, W stored [K, N] (transpose=0)", "ms": round(p["ms"], 5),
+            "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(p["TFLOPs"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(p["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic("lut_kn")}}
     if "moe" in result:
         p = result["moe"]
         comps["moe_q4_0"] = {
-            "workload": "qmm_id_q4_0 E=64 N=1408 K=2048 tokens=128 top_k=8 (group + grouped GEMM)",
+            "workload": "qmm_id_q4_0 E=64 N=1408 K=2048 tokens=128 top_k=8 (one-launch grouped GEMM)",
             "ms": round(p["ms"], 5), "value": round(p["GBps"], 2), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(p["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(p["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic("moe")}}
@@ -590,7 +603,7 @@ def main():
         p = result["tiny"]
         comps["tiny_affine"] = {"workload": "qmm_affine4 M=4 K=256 N=256 (launch-latency bound)",
                                 "us": round(p["ms"] * 1e3, 3), "us_median": round(p["ms_median"] * 1e3, 3)}
-    for name, key in (("prefill_gemm", "prefill"), ("lut_gemm", "lut"), ("moe_q4_0", "moe"),
+    for name, key in (("prefill_gemm", "prefill"), ("lut_gemm", "lut"), ("lut_gemm_kn", "lut_kn"), ("moe_q4_0", "moe"),
                       ("moe_q4_0_decode", "moe_decode"), ("moe_swiglu_q4_0_decode", "moe_swiglu_decode"),
                       ("lut_f32_transpose1", "lut_f32_t1"), ("lut_f32_transpose0", "lut_f32_t0"),
                       ("small_batch_gemm", "small32")):

@@ -120,8 +120,11 @@ w4_status w4_range_events(uint32_t* count, int32_t reset);
  * Contract: M >= 0, K > 0, N > 0, block > 0 and even ([P2] recognize).
  * This library implements transpose != 0 with K % 32 == 0, K % block == 0 and
  * block % 8 == 0 (matrix cores; x 16-byte and packed 4-byte aligned), and
- * transpose == 0 for any K and N with M up to 262,140 (vector ALU, K tiles
- * added with compensation); other valid requests return W4_EUNSUPPORTED.
+ * transpose == 0 for any K and N with M up to 262,140: on the matrix cores
+ * from M = 128 (the page's decoded-weight threshold) when K % 64 == 0,
+ * N % 8 == 0, block is a power of two of at least 8, N * K < 2^32, x is
+ * 16-byte and packed 4-byte aligned; otherwise on the vector ALU (K tiles
+ * added with compensation). Other valid requests return W4_EUNSUPPORTED.
  * M == 0 is a no-op. Accumulation is f32; y is the round-to-nearest-even fp16
  * of it.
  * ---------------------------------------------------------------------- */

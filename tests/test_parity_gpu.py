@@ -320,12 +320,28 @@ def test_qmm_lut4_small(M, K, N, block):
 @pytest.mark.parametrize("M,K,N,block", [
     (4, 256, 96, 64),      # aligned column form: N a multiple of the block
     (3, 100, 70, 6),       # blocks straddle rows: element-by-element form
-    (130, 64, 256, 16),    # more than 128 rows of x: 33 row groups of 4
+    (130, 64, 250, 16),    # more than 128 rows of x but N % 8 != 0: the vector route, 33 row groups of 4
     (2, 5000, 40, 10),     # K split over 16 wavefronts with a ragged last range
     (5, 1000, 200, 8),     # dword form: a partial last 64-column group, ragged K
     (4, 4096, 11008, 64),  # dword form on the LUT workload's weights
+    # matrix-core route (M >= 128, K % 64 == 0, N % 8 == 0, power-of-two block >= 8)
+    (130, 64, 256, 16),    # one K step, ragged M
+    (128, 64, 96, 8),      # one tile, the smallest block
+    (300, 192, 200, 32),   # 3 K steps, ragged M and N (200 of 288 tile columns)
+    (257, 320, 104, 256),  # blocks longer than a row straddle rows; M one past a tile
+    (200, 192, 1000, 1024),  # a partial last block (N K / block = 187.5)
 ])
 def test_qmm_lut4_weight_stored_k_by_n(M, K, N, block):
+    _lut_kn_check(M, K, N, block)
+
+
+def test_qmm_lut4_weight_stored_k_by_n_full_size_every_output():
+    """The lookup workload's shape (M=512, K=4096, N=11008, block 64) with W stored [K, N]: the
+    matrix-core route, every output against the oracle."""
+    _lut_kn_check(512, 4096, 11008, 64)
+
+
+def _lut_kn_check(M, K, N, block):
     # Half-precision path with transpose == 0 (W stored [K, N], flat = k * N + n).
     rng = np.random.default_rng(M + K)
     count = N * K

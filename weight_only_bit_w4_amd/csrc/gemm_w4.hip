@@ -565,10 +565,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
 
-// A store to an LDS byte address.
+// A store to, and a load from, an LDS byte address.
 template <typename T>
 __device__ __forceinline__ void lds_st(uint32_t addr, const T& v) {
     *reinterpret_cast<__attribute__((address_space(3))) T*>((uintptr_t)addr) = v;
+}
+template <typename T>
+__device__ __forceinline__ T lds_ld(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
 }
 
 // One producer lane's share of a step: its x pieces, 2 words (16 nibbles,
@@ -771,26 +775,52 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* 
 //     a time with v_perm_b32.
 // The block size must be a power of two of at least 16 (one scale per lane
 // and step).
+// With the weight stored [K, N] (transpose == 0, the lut4.rs page's
+// decoded-weight route at M >= 128) a step's weights are 64 rows k of the
+// tile's 96 columns, contiguous along n, and the first 6 producers decode
+// one (2-row, 8-column) item per lane instead: a packed dword (8 codes along
+// n) and the block's scale for each of the 2 rows, each byte looked up in a
+// 256-entry table of f32 pairs (book[hi], book[lo]) kept in LDS per
+// decoding wavefront, multiplied by its row's scale in f32 and rounded to
+// binary16, and each column's 2 k values written to the [n][k] tile as one
+// 4-byte store. That needs N % 8 == 0 and a power-of-two block of at least 8
+// (a packed dword never straddles a block).
 constexpr int kLBM = 256, kLBN = 96;
 constexpr int kLConsumers = 4, kLProducers = 8;
 constexpr int kLThreads = (kLConsumers + kLProducers) * 64;
 constexpr int kLXb = 32 / kLProducers;              // x DMA instructions per producer per step
 constexpr int kLDecodeWaves = kLBN * 4 / 64;        // producers that decode (one lane per row quarter)
+constexpr int kLKnCols = kLBN / 8;                  // [K, N]: 8-column groups per tile
+constexpr int kLKnRows = 2;                         // rows of a decode item
+constexpr int kLKnDecodeWaves = kLKnCols * (kPBK / kLKnRows) / 64;  // 6: one lane per (2-row, 8-column) item
 
 struct LutWeights {
     u32x2 words;  // 16 codes: the lane's K quarter of its row
     uint32_t s;   // the block's scale (binary16 bits)
 };
 __device__ __forceinline__ void lut_fence(LutWeights& e) { asm volatile("" : "+v"(e.words), "+v"(e.s)); }
+struct LutKnWeights {
+    uint32_t w[kLKnRows];  // rows kLKnRows kq + i: codes of the item's 8 columns
+    uint32_t s[kLKnRows];  // and their blocks' scales (binary16 bits)
+};
+__device__ __forceinline__ void lut_fence(LutKnWeights& e) {
+#pragma unroll
+    for (int i = 0; i < kLKnRows; ++i) asm volatile("" : "+v"(e.w[i]), "+v"(e.s[i]));
+}
+__device__ __forceinline__ void asm_load_b32(uint32_t& d, const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int soff) {
+    asm volatile("buffer_load_dword %0, %1, %2, %3 offen" : "=v"(d) : "v"(voff), "s"(r), "s"(soff));
+}
 __device__ __forceinline__ void asm_load_b64(u32x2& d, const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int soff) {
     asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen" : "=v"(d) : "v"(voff), "s"(r), "s"(soff));
 }
 
+template <bool KN>
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void qmm_lut4_ws_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
     Book16 book, uint16_t* __restrict__ y, int M, int K, int N, int block_shift) {
     __shared__ __attribute__((aligned(1024))) uint8_t xring[3][kDXBytes];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kLBN * kPLd];
+    __shared__ __attribute__((aligned(16))) f32x2 kn_pairs[KN ? kLKnDecodeWaves * 256 : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tiles_n = (N + kLBN - 1) / kLBN;
@@ -798,7 +828,101 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
     const int steps = K / kPBK;
     const int mrows = min(kLBM, M - m0), nrows = min(kLBN, N - n0);
 
-    if (wave >= kLConsumers) {
+    if (KN && wave >= kLConsumers) {
+        const int pw = wave - kLConsumers;
+        const bool decoder = pw < kLKnDecodeWaves;
+        const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+        // the whole weight (N * K / 2 < 2^31 bytes) and its scales
+        const __amdgpu_buffer_rsrc_t psrc = make_rsrc(packed, (uint32_t)((uint64_t)N * (uint64_t)K / 2));
+        const __amdgpu_buffer_rsrc_t ssrc =
+            make_rsrc(scales, (uint32_t)((((uint64_t)N * (uint64_t)K + (1u << block_shift) - 1) >> block_shift) * 2));
+        uint32_t xo[kLXb];
+#pragma unroll
+        for (int i = 0; i < kLXb; ++i) {
+            const int row = 8 * (kLXb * pw + i) + (lane >> 3);
+            xo[i] = (uint32_t)(row * K * 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7)));
+        }
+        // item (kq, cg) = (rows kLKnRows kq .. of a step, tile columns 8 cg ..); lanes of one kq read one row's 48 bytes
+        const int item = 64 * pw + lane, kq = item / kLKnCols, cg = item % kLKnCols;
+        const uint32_t col = (uint32_t)(n0 + 8 * cg);
+        const bool live = decoder && col < (uint32_t)N;
+        const uint32_t pairs = lds_addr(&kn_pairs[decoder ? pw * 256 : 0]);
+        if (decoder) {
+            // this wavefront's pair table: entry v = (book[v >> 4], book[v & 15])
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t v = 4u * (uint32_t)lane + (uint32_t)t;
+                float hi = 0.f, lo = 0.f;
+#pragma unroll
+                for (uint32_t c = 0; c < 16; ++c) {
+                    hi = (v >> 4) == c ? book.v[c] : hi;
+                    lo = (v & 15u) == c ? book.v[c] : lo;
+                }
+                lds_st(pairs + 8u * v, f32x2{hi, lo});
+            }
+        }
+        LutKnWeights ring[3];
+        auto issue = [&](int kt, int kw, uint8_t* xslot, LutKnWeights& e) {
+            const bool xl = kt < steps, wl = live && kw < steps;
+            const int kx = __builtin_amdgcn_readfirstlane(kt * 2 * kPBK);
+#pragma unroll
+            for (int i = 0; i < kLXb; ++i) lds_dma16(xsrc, xslot + (kLXb * pw + i) * 1024, xl ? xo[i] : kOob, kx);
+            if (decoder) {
+#pragma unroll
+                for (int i = 0; i < kLKnRows; ++i) {
+                    const uint32_t flat = (uint32_t)(kPBK * kw + kLKnRows * kq + i) * (uint32_t)N + col;  // < N K < 2^32
+                    asm_load_b32(e.w[i], psrc, wl ? flat / 2 : kOob, 0);
+                    asm_load_u16(e.s[i], ssrc, wl ? (flat >> block_shift) * 2u : kOob, 0);
+                }
+            }
+        };
+        // Columns 2 b and 2 b + 1 of the item are byte b's high and low codes.
+        static_assert(kLKnRows == 2, "one 4-byte store per column");
+        auto decode = [&](const LutKnWeights& e, int buf) {
+            const float s0 = f16_bits_to_f32(e.s[0]), s1 = f16_bits_to_f32(e.s[1]);
+            const uint32_t dst = lds_addr(Bs[buf]) + 2u * (uint32_t)(8 * cg * kPLd + kLKnRows * kq);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const f32x2 p0 = lds_ld<f32x2>(pairs + 8u * ((e.w[0] >> (8 * b)) & 0xFFu));
+                const f32x2 p1 = lds_ld<f32x2>(pairs + 8u * ((e.w[1] >> (8 * b)) & 0xFFu));
+                lds_st(dst + 2u * (uint32_t)((2 * b) * kPLd), pack_f16x2(p0[0] * s0, p1[0] * s1));
+                lds_st(dst + 2u * (uint32_t)((2 * b + 1) * kPLd), pack_f16x2(p0[1] * s0, p1[1] * s1));
+            }
+        };
+        constexpr int kWl = 2 * kLKnRows;  // weight loads per decoding lane per step
+        issue(steps, 0, xring[2], ring[0]);
+        issue(0, 1, xring[0], ring[1]);
+        issue(1, 2, xring[1], ring[2]);
+        if (decoder) {
+            wait_vmcnt<2 * (kLXb + kWl)>();
+            wait_lgkmcnt0();  // the pair table written
+            lut_fence(ring[0]);
+            decode(ring[0], 0);
+        }
+        auto body = [&](auto slot, int j) {
+            constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+            if (decoder)
+                wait_vmcnt<kLXb + kWl>();
+            else
+                wait_vmcnt<kLXb>();
+            wait_lgkmcnt0();
+            lut_fence(ring[S1]);
+            raw_barrier();
+            if (decoder) decode(ring[S1], (j + 1) & 1);
+            issue(j + 2, j + 3, xring[S2], ring[S0]);
+        };
+        int j = 0;
+        for (; j + 3 <= steps; j += 3) {
+            body(std::integral_constant<int, 0>{}, j);
+            body(std::integral_constant<int, 1>{}, j + 1);
+            body(std::integral_constant<int, 2>{}, j + 2);
+        }
+        if (j < steps) body(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
+        wait_vmcnt<0>();  // the trailing (all-zero) loads land before this wavefront ends
+        return;
+    }
+    if (!KN && wave >= kLConsumers) {
         const int pw = wave - kLConsumers;
         const bool decoder = pw < kLDecodeWaves;
         const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
@@ -954,11 +1078,6 @@ template <int MT> struct TlShape {
 __device__ __forceinline__ void tl_dma16(const __amdgpu_buffer_rsrc_t& rsrc, const void* lds, uint32_t voff) {
     const uint32_t a = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(rsrc));
-}
-// A load from an LDS byte address.
-template <typename T>
-__device__ __forceinline__ T lds_ld(uint32_t addr) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
 }
 // s_waitcnt vmcnt(n) for a run-time n (0 .. 23; larger waits for everything).
 __device__ __forceinline__ void wait_vmcnt_rt(int n) {
@@ -1304,9 +1423,22 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
     if (M == 0) return W4_OK;
     if (!x || !packed || !scales || !book || !y) return fail(W4_EINVAL, "qmm_lut4: null pointer argument");
     if (!transpose) {
-        // Weight stored [K, N]: column kernels in the vector ALU (lut_f32.hip).
         if (((uintptr_t)x & 1u) || ((uintptr_t)scales & 1u) || ((uintptr_t)y & 1u))
             return fail(W4_EINVAL, "qmm_lut4: x, scales and y must be 2-byte aligned");
+        // Weight stored [K, N]. From 128 rows of x (the page's decoded-weight
+        // threshold) the matrix cores, where the shape allows; otherwise column
+        // kernels in the vector ALU (lut_f32.hip).
+        if (M >= 128 && K % kPBK == 0 && N % 8 == 0 && block >= 8 && (block & (block - 1)) == 0 &&
+            (uint64_t)N * (uint64_t)K / 2 < (1ull << 31) && aligned16(x) && ((uintptr_t)packed & 3u) == 0) {
+            Book16 b;
+            for (int i = 0; i < 16; ++i) b.v[i] = book[i];
+            int shift = 0;
+            while ((1 << shift) < block) ++shift;
+            const unsigned tiles = (unsigned)(((M + kLBM - 1) / kLBM) * ((N + kLBN - 1) / kLBN));
+            hipLaunchKernelGGL(qmm_lut4_ws_kernel<true>, dim3(tiles), dim3(kLThreads), 0, as_stream(stream), x, packed,
+                               scales, b, y, (int)M, (int)K, (int)N, shift);
+            return launch_status("qmm_lut4 ([K, N] matrix-core route)");
+        }
         launch_lut4_kn_f16(x, packed, scales, book, y, M, K, N, block, as_stream(stream));
         return launch_status("qmm_lut4");
     }
@@ -1323,8 +1455,8 @@ extern "C" w4_status qmm_lut4(const uint16_t* x, const uint8_t* packed, const ui
         int shift = 0;
         while ((1 << shift) < block) ++shift;
         const unsigned tiles = (unsigned)(((M + kLBM - 1) / kLBM) * ((N + kLBN - 1) / kLBN));
-        hipLaunchKernelGGL(qmm_lut4_ws_kernel, dim3(tiles), dim3(kLThreads), 0, s, x, packed, scales, b, y, (int)M, (int)K,
-                           (int)N, shift);
+        hipLaunchKernelGGL(qmm_lut4_ws_kernel<false>, dim3(tiles), dim3(kLThreads), 0, s, x, packed, scales, b, y, (int)M,
+                           (int)K, (int)N, shift);
     } else {
         constexpr int BM = 256, BN = 128;
         const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
