@@ -47,15 +47,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "500af2f7dc0eccda", 36831260 + 57348),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 100809736 + 16800123),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 81624874 + 11291098),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "fe1bcf1b6d8d056a", 39070400 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 123876020 + 5767168),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 13134031 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "3d12ad4899832551", 14099603 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "b7d0ed61d3475eed", 26047904 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "b7d0ed61d3475eed", 44816623 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "f305b4e4589151dd", 36831475 + 57347),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 100888133 + 16795999),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 81624988 + 11289426),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 187577012 + 11283292),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 39112599 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "205797f7bcb9c4f4", 128201404 + 5767200),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "205797f7bcb9c4f4", 13123868 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "205797f7bcb9c4f4", 14108901 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "96d9222bf08f4af7", 26048078 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "96d9222bf08f4af7", 44816806 + 176128),
 }
 
 
