@@ -878,9 +878,12 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
         };
         // Columns 2 b and 2 b + 1 of the item are byte b's high and low codes.
         static_assert(kLKnRows == 2, "one 4-byte store per column");
+        // The tile's row n keeps its 16-byte k chunk c at chunk c ^ ((n / 8) % 8): the 12 lanes of one
+        // kq (columns 8 cg ..) would otherwise all store to one bank.
+        const uint32_t kofs = 2u * (uint32_t)(8 * (((kLKnRows * kq) >> 3) ^ (cg & 7)) + ((kLKnRows * kq) & 7));
         auto decode = [&](const LutKnWeights& e, int buf) {
             const float s0 = f16_bits_to_f32(e.s[0]), s1 = f16_bits_to_f32(e.s[1]);
-            const uint32_t dst = lds_addr(Bs[buf]) + 2u * (uint32_t)(8 * cg * kPLd + kLKnRows * kq);
+            const uint32_t dst = lds_addr(Bs[buf]) + 2u * (uint32_t)(8 * cg * kPLd) + kofs;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const f32x2 p0 = lds_ld<f32x2>(pairs + 8u * ((e.w[0] >> (8 * b)) & 0xFFu));
@@ -1013,7 +1016,15 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
                 a[f] = *reinterpret_cast<const u32x4*>(xslot + row * 128 + 16 * (ch ^ ((row >> 1) & 7)));
             }
 #pragma unroll
-            for (int g = 0; g < 3; ++g) b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+            for (int g = 0; g < 3; ++g) {
+                if constexpr (KN) {
+                    // [K, N] tiles: row n's 16-byte chunk c sits at chunk c ^ ((n / 8) % 8)
+                    const int n = 32 * g + (lane & 31);
+                    b[g] = *reinterpret_cast<const u32x4*>(Bs[j & 1] + n * kPLd + 8 * (ch ^ ((n >> 3) & 7)));
+                } else {
+                    b[g] = *reinterpret_cast<const u32x4*>(bb + g * 32 * kPLd + sub * 16);
+                }
+            }
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
