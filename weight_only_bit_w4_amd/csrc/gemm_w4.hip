@@ -922,7 +922,13 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
         }
         if (j < steps) body(std::integral_constant<int, 0>{}, j);
         if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
-        wait_vmcnt<0>();  // the trailing (all-zero) loads land before this wavefront ends
+        // The trailing (all-zero) loads land before this wavefront ends; the
+        // fences keep every ring entry's registers allocated until they have
+        // (an asm load's output is otherwise free once unused, and a load
+        // still in flight would overwrite whatever took its place).
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int i = 0; i < 3; ++i) lut_fence(ring[i]);
         return;
     }
     if (!KN && wave >= kLConsumers) {
@@ -989,7 +995,13 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
         }
         if (j < steps) body(std::integral_constant<int, 0>{}, j);
         if (j + 1 < steps) body(std::integral_constant<int, 1>{}, j + 1);
-        wait_vmcnt<0>();  // the trailing (all-zero) DMA lands before this wavefront ends
+        // The trailing (all-zero) loads land before this wavefront ends; the
+        // fences keep every ring entry's registers allocated until they have
+        // (an asm load's output is otherwise free once unused, and a load
+        // still in flight would overwrite whatever took its place).
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int i = 0; i < 3; ++i) lut_fence(ring[i]);
         return;
     }
 
