@@ -70,9 +70,10 @@ __device__ __forceinline__ void x_group_from_raw(const u32x4 (&v4)[4], bool vali
 }
 
 // sum over the group of x_k * (128 + q_k), f32 accumulation. `mask` and
-// `bias` hold kAffinePairMask and kAffinePairBias in vector registers, so
-// each pair is one shift and one v_and_or_b32. NA independent partial sums
-// (word j feeds sum j % NA) shorten the chain of dependent dot products.
+// `bias` hold kAffinePairMask and kAffinePairBias in vector registers; the
+// pairs of words (0, 1) and (2, 3) come from one 64-bit shift per pair index
+// and one v_and_or_b32 each. NA independent partial sums (word j feeds sum
+// j % NA) shorten the chain of dependent dot products.
 template <int NA>
 __device__ __forceinline__ float group_dot_biased(const u32x4& words, const XGroup& xg, uint32_t mask,
                                                   uint32_t bias) {
@@ -80,12 +81,15 @@ __device__ __forceinline__ float group_dot_biased(const u32x4& words, const XGro
 #pragma unroll
     for (int a = 0; a < NA; ++a) d[a] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t word = words[j];
+    for (int jp = 0; jp < 2; ++jp) {
+        uint32_t p[2][4];
+        affine_pairs2_biased_bf16(words[2 * jp], words[2 * jp + 1], mask, bias, p);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t pair = affine_pair_biased_bf16(word, i, mask, bias);
-            d[j % NA] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pair), as_bf16x2(xg.pair[j][i]), d[j % NA], false);
+        for (int h = 0; h < 2; ++h) {
+            const int j = 2 * jp + h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                d[j % NA] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p[h][i]), as_bf16x2(xg.pair[j][i]), d[j % NA], false);
         }
     }
 #pragma unroll

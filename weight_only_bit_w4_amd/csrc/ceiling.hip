@@ -1,8 +1,11 @@
 // Measurement kernels: the achievable ceilings the benchmark reports beside
 // the MI355X's published peaks.
 //   w4_ceiling_stream_read - every byte of a buffer read once with 16-byte
-//       non-temporal loads (the access pattern of the bandwidth-bound decode
-//       kernels), folded into one word per workgroup so no load is dropped;
+//       non-temporal loads, each workgroup streaming one contiguous chunk
+//       with four loads per lane in flight (the fastest plain read pattern
+//       found for buffers of tens of MB to hundreds of MB: about 10 % faster
+//       than a grid-stride loop on a 36.7 MB buffer), folded into one word
+//       per lane so no load is dropped;
 //   w4_ceiling_mfma - v_mfma_f32_32x32x16_f16 back to back on every SIMD
 //       (four independent accumulators per wavefront, no memory traffic).
 #include "w4mi_device.hpp"
@@ -11,21 +14,26 @@
 namespace w4mi {
 
 constexpr int kReadThreads = 512;
-constexpr int kReadUnroll = 8;  // 16-byte loads in flight per lane
+constexpr int kReadUnroll = 4;     // 16-byte loads in flight per lane
+constexpr int kReadGroups = 1024;  // workgroups for large buffers (four per CU)
 
+// Workgroup b reads pieces [b * per, min((b + 1) * per, pieces)) of 16 bytes;
+// per is a multiple of 64 pieces, so every wavefront load covers one aligned
+// kilobyte.
 __global__ __launch_bounds__(kReadThreads) void ceiling_read_kernel(const u32x4* __restrict__ buf, int64_t pieces,
-                                                                    uint32_t* __restrict__ sink) {
-    const int64_t stride = (int64_t)gridDim.x * kReadThreads;
-    int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+                                                                    int64_t per, uint32_t* __restrict__ sink) {
+    const int64_t beg = (int64_t)blockIdx.x * per;
+    const int64_t end = beg + per < pieces ? beg + per : pieces;
+    int64_t i = beg + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + (kReadUnroll - 1) * stride < pieces; i += kReadUnroll * stride) {
+    for (; i + (kReadUnroll - 1) * kReadThreads < end; i += kReadUnroll * kReadThreads) {
         u32x4 v[kReadUnroll];
 #pragma unroll
-        for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+        for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * kReadThreads);
 #pragma unroll
         for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
-    for (; i < pieces; i += stride) {
+    for (; i < end; i += kReadThreads) {
         const u32x4 v = __builtin_nontemporal_load(buf + i);
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
@@ -67,11 +75,14 @@ extern "C" w4_status w4_ceiling_stream_read(const void* buf, uint64_t bytes, uin
         return fail(W4_EINVAL, "w4_ceiling_stream_read: buffer must be 16-byte aligned and a multiple of 16 bytes");
     if (bytes == 0) return W4_OK;
     const int64_t pieces = (int64_t)(bytes / 16);
-    // 8 workgroups of 8 wavefronts per CU: enough loads in flight to cover HBM latency.
-    const int64_t want = (pieces + (int64_t)kReadThreads * kReadUnroll - 1) / ((int64_t)kReadThreads * kReadUnroll);
-    const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), (int64_t)kCUs * 8);
-    hipLaunchKernelGGL(ceiling_read_kernel, dim3(grid), dim3(kReadThreads), 0, as_stream(stream),
-                       reinterpret_cast<const u32x4*>(buf), pieces, sink);
+    // Four workgroups of eight wavefronts per CU, one contiguous chunk each
+    // (fewer for a buffer under 32 KB per workgroup).
+    const int64_t step = (int64_t)kReadThreads * kReadUnroll;
+    const int64_t grid = std::min<int64_t>((pieces + step - 1) / step, kReadGroups);
+    const int64_t per = ((pieces + grid - 1) / grid + 63) / 64 * 64;
+    const unsigned launch = (unsigned)((pieces + per - 1) / per);
+    hipLaunchKernelGGL(ceiling_read_kernel, dim3(launch), dim3(kReadThreads), 0, as_stream(stream),
+                       reinterpret_cast<const u32x4*>(buf), pieces, per, sink);
     return launch_status("w4_ceiling_stream_read");
 }
 

@@ -11,19 +11,27 @@ constexpr int kUnpackThreads = 256;
 // One thread per affine word. Every affine decoder the kernels run is
 // applied and must agree, else the code is written as 0xFF (which cannot
 // pass a bit-exact check): the nibble extraction of the small-shape GEMM
-// (affine_nibble), the biased bf16 pairs of the GEMV forms
-// (affine_pair_biased_bf16) and the binary16 word decode of the prefill and
-// weight-tile kernels (affine_word_f16 with scale 1 and bias 0, which gives
-// q exactly).
+// (affine_nibble), the biased bf16 pairs of the GEMV forms, one word at a
+// time (affine_pair_biased_bf16) and two at a time with the word's real
+// neighbours (affine_pairs2_biased_bf16, as the low word ahead of the next
+// word and as the high word after the previous one), and the binary16 word
+// decode of the prefill and weight-tile kernels (affine_word_f16 with scale
+// 1 and bias 0, which gives q exactly).
 __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __restrict__ q, int64_t words) {
     const int64_t i = (int64_t)blockIdx.x * kUnpackThreads + threadIdx.x;
     if (i >= words) return;
     const uint32_t word = w[i];
+    const uint32_t next = i + 1 < words ? w[i + 1] : ~word, prev = i > 0 ? w[i - 1] : ~word;
     const uint32_t mask = vreg(kAffinePairMask), bias = vreg(kAffinePairBias);
+    uint32_t lo[2][4], hi[2][4];
+    affine_pairs2_biased_bf16(word, next, mask, bias, lo);  // word as the low word
+    affine_pairs2_biased_bf16(prev, word, mask, bias, hi);  // word as the high word
     uint8_t out[8];
+    bool pairs_agree = true;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const uint32_t pair = affine_pair_biased_bf16(word, p, mask, bias);  // nibbles p (low half) and p + 4 (high half)
+        pairs_agree = pairs_agree && lo[0][p] == pair && hi[1][p] == pair;
         out[p] = (uint8_t)(pair & 0xFu);
         out[p + 4] = (uint8_t)((pair >> 16) & 0xFu);
     }
@@ -33,7 +41,7 @@ __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __
     for (int j = 0; j < 8; ++j) {
         const uint32_t bits = (j & 1) ? (h[j / 2] >> 16) : (h[j / 2] & 0xFFFFu);
         const float v = f16_bits_to_f32(bits);
-        const bool same = out[j] == affine_nibble(word, j) && v == (float)out[j];
+        const bool same = pairs_agree && out[j] == affine_nibble(word, j) && v == (float)out[j];
         q[i * 8 + j] = same ? out[j] : (uint8_t)0xFF;
     }
 }

@@ -223,6 +223,26 @@ __device__ __forceinline__ uint32_t affine_pair_biased_bf16(uint32_t word, int i
 constexpr uint32_t kAffinePairMask = 0x000F000Fu;
 constexpr uint32_t kAffinePairBias = 0x43004300u;
 
+// The same four pairs for two words at once (p[h][i] = pair i of word h): a
+// single 64-bit shift of (w1:w0) by 4i brings nibbles i and i + 4 of both
+// words down. The bits of w1 that the shift moves into the low word land at
+// bit 28 and above (i = 1), 24 (2) or 20 (3), outside the mask. One
+// v_lshrrev_b64 in place of two 32-bit shifts; written as an instruction
+// because the compiler splits a 64-bit shift whose result is masked.
+__device__ __forceinline__ void affine_pairs2_biased_bf16(uint32_t w0, uint32_t w1, uint32_t mask, uint32_t bias,
+                                                          uint32_t (&p)[2][4]) {
+    const uint64_t v = ((uint64_t)w1 << 32) | w0;
+    p[0][0] = and_or_u32(w0, mask, bias);
+    p[1][0] = and_or_u32(w1, mask, bias);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        uint64_t s;
+        asm("v_lshrrev_b64 %0, %1, %2" : "=v"(s) : "i"(4 * i), "v"(v));
+        p[0][i] = and_or_u32((uint32_t)s, mask, bias);
+        p[1][i] = and_or_u32((uint32_t)(s >> 32), mask, bias);
+    }
+}
+
 // Lookup-codebook index order (lut4 page, decode kernel): flat index i uses
 // the HIGH nibble of byte i/2 when i is even, the LOW nibble when i is odd.
 __device__ __forceinline__ uint32_t lut_code(uint32_t byte, uint32_t i) {
