@@ -47,16 +47,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "f305b4e4589151dd", 36831475 + 57347),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 100888133 + 16795999),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 81624988 + 11289426),
-    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 187577012 + 11283292),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "e6f5a8d80c4bf1c6", 39112599 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "205797f7bcb9c4f4", 128201404 + 5767200),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "205797f7bcb9c4f4", 13123868 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "205797f7bcb9c4f4", 14108901 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "96d9222bf08f4af7", 26048078 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "96d9222bf08f4af7", 44816806 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "ad97b8ec80d770e9", 36831134 + 57348),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "a9d7a1216bdd3a94", 100887486 + 16795817),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "a9d7a1216bdd3a94", 81622127 + 11287068),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "a9d7a1216bdd3a94", 187575885 + 11276716),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "a9d7a1216bdd3a94", 39117361 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "a169c8b0ffb40afa", 127931111 + 5767200),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "a169c8b0ffb40afa", 13123794 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "a169c8b0ffb40afa", 14108816 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "3f6d4a29a837ab39", 26047921 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "3f6d4a29a837ab39", 44815662 + 176128),
 }
 
 
