@@ -528,7 +528,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // Loads run three steps ahead through a 3-deep register ring (the producer
 // loop unrolled by 3), so a step's data has two steps of matrix work to
 // arrive; the x of the 32 workgroups that one XCD runs (one row-block) stays
-// in that XCD's L2.
+// in that XCD's L2. When K % 256 == 0 (a row's scales and biases fill whole
+// 16-byte pieces), each lane loads the scales and the biases of its row for
+// four steps (8 groups) at once, a 16-byte load each, four steps ahead, into
+// a 3-deep ring of its own (loop unrolled by 12), and takes each step's pair
+// from registers: 2-byte loads scattered over 128 rows cost the address unit
+// about as much as 16-byte ones, and were a large part of its work.
 constexpr int kWsConsumers = 4, kWsProducers = 8;
 constexpr int kWsThreads = (kWsConsumers + kWsProducers) * 64;
 constexpr int kWsXp = kPBM * 8 / (kWsProducers * 64);   // 16-byte x pieces per producer lane per step (4)
@@ -614,6 +619,7 @@ __device__ __forceinline__ void ws_mma(const uint8_t* xslot, const uint16_t* Bs,
     }
 }
 
+template <bool SB4>
 __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void qmm_affine4_prefill_ws_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int K, int N, uint32_t* __restrict__ events) {
@@ -653,6 +659,17 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3
         const uint32_t wo = (uint32_t)(r * (K / 2) + 16 * g + 8 * h), so = (uint32_t)((r * G + g) * 2);
         const uint32_t bdst = lds_addr(Bs[0] + r * kPLd + 32 * g + 16 * h);
         WsStep ring[3];
+        // SB4: the row's scales and biases of steps 4 blk .. 4 blk + 3 (groups 8 blk .. 8 blk + 7)
+        struct WsSB {
+            u32x4 s, b;
+        };
+        WsSB sb[3];
+        const uint32_t sro = (uint32_t)(r * G * 2);
+        auto issue_sb = [&](int blk, WsSB& e) {
+            const int kb = __builtin_amdgcn_readfirstlane(4 * blk < steps ? blk * 16 : (int)kOob);
+            e.s = __builtin_amdgcn_raw_buffer_load_b128(ssrc, sro, kb, 0);
+            e.b = __builtin_amdgcn_raw_buffer_load_b128(bsrc, sro, kb, 0);
+        };
         // Loads of step kt. Past the last step the wave-uniform offset is sent
         // past every buffer's end (the loads return zeros), which keeps the
         // per-lane offsets fixed.
@@ -664,49 +681,74 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3
 #pragma unroll
             for (int i = 0; i < kWsXp; ++i) e.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xo[i], kx, 0);
             e.words = __builtin_amdgcn_raw_buffer_load_b64(wsrc, wo, kw, 0);
-            e.s = __builtin_amdgcn_raw_buffer_load_b16(ssrc, so, ks, 0);
-            e.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, so, ks, 0);
+            if constexpr (!SB4) {
+                e.s = __builtin_amdgcn_raw_buffer_load_b16(ssrc, so, ks, 0);
+                e.b = __builtin_amdgcn_raw_buffer_load_b16(bsrc, so, ks, 0);
+            } else {
+                e.s = e.b = 0u;
+            }
         };
-        // Step data into LDS buffer `buf`: x converted, W decoded.
-        auto publish = [&](const WsStep& e, auto buf) {
+        // Step data into LDS buffer `buf`: x converted, W decoded. SB4: the
+        // step's scale and bias are dword D of sb set Q, half g.
+        auto publish = [&](const WsStep& e, auto buf, auto q_c, auto d_c) {
             constexpr uint32_t xb = decltype(buf)::value * kDXBytes, wb = decltype(buf)::value * (kPBN * kPLd * 2);
 #pragma unroll
             for (int i = 0; i < kWsXp; ++i) lds_st<u32x4>(xd[i] + xb, bf16x8_to_f16x8(e.x[i]));
-            const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(e.s), bf16_bits_to_f32(e.b));
+            float sf, bf;
+            if constexpr (SB4) {
+                constexpr int Q = decltype(q_c)::value, D = decltype(d_c)::value;
+                const uint32_t sv = sb[Q].s[D], bv = sb[Q].b[D];
+                sf = __uint_as_float(g ? sv & 0xFFFF0000u : sv << 16);
+                bf = __uint_as_float(g ? bv & 0xFFFF0000u : bv << 16);
+            } else {
+                sf = bf16_bits_to_f32(e.s);
+                bf = bf16_bits_to_f32(e.b);
+            }
+            const AffineGroupF16 grp = affine_group_f16(sf, bf);
 #pragma unroll
             for (int i = 0; i < 2; ++i) lds_st<u32x4>(bdst + wb + 16 * i, affine_word_f16(e.words[i], grp, m_lo, m_hi, magic));
         };
         // The prologue issues steps 0, 1, 2 in the loop's order (the
         // scheduling barriers keep the compiler from interleaving them, so its
-        // wait counts at the loop head stay exact).
+        // wait counts at the loop head stay exact), after the first two
+        // scale and bias blocks.
+        using C0 = std::integral_constant<int, 0>;
+        if constexpr (SB4) {
+            issue_sb(0, sb[0]);
+            issue_sb(1, sb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         issue(0, ring[0]);
         __builtin_amdgcn_sched_barrier(0);
         issue(1, ring[1]);
         __builtin_amdgcn_sched_barrier(0);
         issue(2, ring[2]);
         __builtin_amdgcn_sched_barrier(0);
-        publish(ring[0], std::integral_constant<int, 0>{});
+        publish(ring[0], C0{}, C0{}, C0{});
         // Iteration j (j mod 3 == S0, j mod 2 == P): barrier j (this
         // wavefront's LDS writes of step j are complete), publish step j + 1
         // into the free buffers (past the last step: zeros into buffers no
         // consumer reads again), then load step j + 3 into the ring entry step
-        // j used. The loop is unrolled by 6 so that both ring positions are
-        // constants.
-        auto body = [&](auto slot, auto par, int j) {
-            constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3;
+        // j used; SB4: at j = 3 mod 4, also the scale and bias block of steps
+        // j + 5 .. j + 8, into the set that block j + 5 - 12 used. The loop is
+        // unrolled by 6 (SB4: 12) so that every ring position is a constant
+        // (I = j mod 6 or 12).
+        auto body = [&](auto i_c, int j) {
+            constexpr int I = decltype(i_c)::value, S0 = I % 3, S1 = (S0 + 1) % 3, P = I % 2;
+            constexpr int Q = ((I + 1) / 4) % 3, D = (I + 1) % 4;  // step j + 1's scale set and dword
             wait_lgkmcnt0();
             raw_barrier();
             ws_fence(ring[S1]);
-            publish(ring[S1], std::integral_constant<int, 1 - decltype(par)::value>{});
+            publish(ring[S1], std::integral_constant<int, 1 - P>{}, std::integral_constant<int, Q>{},
+                    std::integral_constant<int, D>{});
             issue(j + 3, ring[S0]);
+            if constexpr (SB4 && I % 4 == 3) issue_sb((j + 5) / 4, sb[((I + 5) / 4) % 3]);
         };
+        constexpr int U = SB4 ? 12 : 6;
         int j = 0;
-        for (; j + 6 <= steps; j += 6)
-            static_for<6>([&](auto I) {
-                body(std::integral_constant<int, I % 3>{}, std::integral_constant<int, I % 2>{}, j + I);
-            });
-        static_for<5>([&](auto I) {
-            if (j + I < steps) body(std::integral_constant<int, I % 3>{}, std::integral_constant<int, I % 2>{}, j + I);
+        for (; j + U <= steps; j += U) static_for<U>([&](auto I) { body(I, j + I); });
+        static_for<U - 1>([&](auto I) {
+            if (j + I < steps) body(I, j + I);
         });
         return;
     }
@@ -814,6 +856,17 @@ __device__ __forceinline__ void asm_load_b64(u32x2& d, const __amdgpu_buffer_rsr
     asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen" : "=v"(d) : "v"(voff), "s"(r), "s"(soff));
 }
 
+// XCD-aware tile order: workgroup b runs on XCD b % 8, and XCD x takes the
+// contiguous range of tiles u = n_tile * tiles_m + m_tile that starts after
+// the tiles of XCDs 0 .. x - 1 (XCDs below tiles % 8 get one more). The M
+// tiles of a column tile, and neighbouring column tiles, then share one L2:
+// a column tile's weights (and, for W stored [K, N], the 64-byte sectors its
+// row segments share with the neighbouring tiles) come from HBM once.
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+    const int xcd = b % 8, i = b / 8, base = tiles / 8, extra = tiles % 8;
+    return xcd * base + min(xcd, extra) + i;
+}
+
 template <bool KN>
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void qmm_lut4_ws_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -823,8 +876,9 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
     __shared__ __attribute__((aligned(16))) f32x2 kn_pairs[KN ? kLKnDecodeWaves * 256 : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tiles_n = (N + kLBN - 1) / kLBN;
-    const int m0 = (blockIdx.x / tiles_n) * kLBM, n0 = (blockIdx.x % tiles_n) * kLBN;
+    const int tiles_m = (M + kLBM - 1) / kLBM, tiles_n = (N + kLBN - 1) / kLBN;
+    const int u = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int m0 = (u % tiles_m) * kLBM, n0 = (u / tiles_m) * kLBN;
     const int steps = K / kPBK;
     const int mrows = min(kLBM, M - m0), nrows = min(kLBN, N - n0);
 
@@ -1428,9 +1482,12 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
                            x, y, (int)M, (int)K, (int)N, events);
     } else {
         const unsigned tiles = (unsigned)(((M + kPBM - 1) / kPBM) * ((N + kPBN - 1) / kPBN));
-        if (K % kPBK == 0)
-            hipLaunchKernelGGL(qmm_affine4_prefill_ws_kernel, dim3(tiles), dim3(kWsThreads), 0, s, w, scales, biases,
-                               x, y, (int)M, (int)K, (int)N, events);
+        if (K % 256 == 0)
+            hipLaunchKernelGGL(qmm_affine4_prefill_ws_kernel<true>, dim3(tiles), dim3(kWsThreads), 0, s, w, scales,
+                               biases, x, y, (int)M, (int)K, (int)N, events);
+        else if (K % kPBK == 0)
+            hipLaunchKernelGGL(qmm_affine4_prefill_ws_kernel<false>, dim3(tiles), dim3(kWsThreads), 0, s, w, scales,
+                               biases, x, y, (int)M, (int)K, (int)N, events);
         else
             hipLaunchKernelGGL(qmm_affine4_prefill_kernel<true>, dim3(tiles), dim3(kPThreads), 0, s, w, scales, biases,
                                x, y, (int)M, (int)K, (int)N, events);
