@@ -108,6 +108,10 @@ def test_qmv_affine4(K, N, seed):
     (300, 128, 256),                      # 2 K steps (producer loop tail of 2)
     (257, 256, 160),                      # 4 K steps (one unrolled round + a tail of 1)
     (384, 1024, 384),                     # 16 K steps, several tiles each way
+    # K % 256 == 0: scales and biases come four steps to a load, the producer loop unrolled by 12
+    (300, 768, 160),                      # 12 K steps: one unrolled round, no tail
+    (270, 2048, 96),                      # 32 K steps: two rounds and a tail of 8
+    (520, 5120, 224),                     # 80 K steps: six rounds and a tail of 8, three row tiles
     # the GEMV form (every weight row read once for all rows): fewer than 6 rows, or up to 16
     # rows when K % 256 != 0 (K <= 8192)
     (2, 4096, 14336),                     # the decode workload's weights, two rows (batches of 2)
