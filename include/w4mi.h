@@ -295,9 +295,12 @@ w4_status w4_unpack_q4_0(const uint8_t* w, uint8_t* q, uint16_t* d, int64_t rows
  * Measurement entry points: achievable ceilings of this GPU, for reporting
  * the kernels above against measured limits as well as published peaks.
  *   w4_ceiling_stream_read: reads `bytes` (a multiple of 16) of the 16-byte
- *       aligned device buffer `buf` once, with the 16-byte non-temporal loads
- *       the bandwidth-bound kernels use; bytes / time is the streaming-read
- *       rate. `sink` is a device uint32 [1024] the kernel may write.
+ *       aligned device buffer `buf` once, with 16-byte non-temporal loads,
+ *       each workgroup streaming one contiguous chunk (up to 1024 workgroups
+ *       of 512 lanes, four loads per lane in flight); bytes / time is the
+ *       streaming-read rate. `sink` is a device uint32 [1024] the kernel may
+ *       write: a lane whose pieces fold (XOR of all their dwords) to
+ *       0x9E3779B9 writes that value to one word, so the loads are live.
  *   w4_ceiling_mfma: every SIMD issues `iters` x 4 back-to-back
  *       v_mfma_f32_32x32x16_f16 (32,768 flop each) on 2 x 256 workgroups of 4
  *       wavefronts (no memory traffic): 2 * 256 * 4 * 4 * iters * 32768 flop.
