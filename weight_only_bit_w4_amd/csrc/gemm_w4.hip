@@ -532,8 +532,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // 16-byte pieces), each lane loads the scales and the biases of its row for
 // four steps (8 groups) at once, a 16-byte load each, four steps ahead, into
 // a 3-deep ring of its own (loop unrolled by 12), and takes each step's pair
-// from registers: 2-byte loads scattered over 128 rows cost the address unit
-// about as much as 16-byte ones, and were a large part of its work.
+// from registers, instead of two 2-byte loads per step that each touch 16
+// rows' cache lines for 128 bytes of data.
 constexpr int kWsConsumers = 4, kWsProducers = 8;
 constexpr int kWsThreads = (kWsConsumers + kWsProducers) * 64;
 constexpr int kWsXp = kPBM * 8 / (kWsProducers * 64);   // 16-byte x pieces per producer lane per step (4)
