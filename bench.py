@@ -48,10 +48,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # as null once those sources change.
 TRAFFIC = {
     "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "ad97b8ec80d770e9", 36831134 + 57348),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "03b8f08470ef62e9", 100982449 + 16810040),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "03b8f08470ef62e9", 58282926 + 11831675),
-    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "03b8f08470ef62e9", 65500602 + 11506588),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "03b8f08470ef62e9", 39102655 + 917504),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "e69793bda19f8bb9", 100982449 + 16810040),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "e69793bda19f8bb9", 58282926 + 11831675),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "e69793bda19f8bb9", 65500602 + 11506588),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "e69793bda19f8bb9", 39102655 + 917504),
     "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "a169c8b0ffb40afa", 127931111 + 5767200),
     "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "a169c8b0ffb40afa", 13123794 + 45088),
     "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "a169c8b0ffb40afa", 14108816 + 45056),
