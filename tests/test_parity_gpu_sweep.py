@@ -41,6 +41,28 @@ def test_sweep_affine(seed):
     _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"sweep affine seed={seed} M={M} K={K} N={N}")
 
 
+def _prefill_shape(seed):
+    # The matrix-core prefill tiles (M > 64, K % 64 == 0), half of them with K % 256 == 0 (scales and
+    # biases loaded four steps at a time), several row and column tiles, ragged edges.
+    rng = np.random.default_rng(1500 + seed)
+    M = int(rng.integers(65, 700))
+    K = (256 if seed % 2 == 0 else 64) * int(rng.integers(1, 11))
+    N = 32 * int(rng.integers(1, 25))
+    return M, K, N
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_prefill(seed):
+    M, K, N = _prefill_shape(seed)
+    c = synth.affine_case(M, K, N, seed=100 + seed)
+    w, s, b, x = _affine_dev(c)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"sweep prefill seed={seed} M={M} K={K} N={N}")
+
+
 def _lut_shape(seed):
     rng = np.random.default_rng(2000 + seed)
     block = int(rng.choice([8, 16, 32, 64, 128]))
