@@ -1120,7 +1120,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
 // cores. A workgroup of 16 wavefronts takes two 32-row weight tiles; wavefront
 // (t, p) = (w / 8, w % 8) owns tile t and k-steps 2 p, 2 p + 1 (quantisation
 // group p) of each 256-wide K window, against all M rows (MT 32-row tiles of
-// x); at the end each of a tile's eight wavefronts sums two of the 16
+// x); at the end each of a tile's eight wavefronts sums 2 (MT = 2: 4) of the
 // accumulator registers over the eight partial sums (through LDS) and stores
 // them. Each lane decodes its own weight word straight into a binary16
 // matrix-core operand (affine_word_f16: q s + b rounded once, in k order) and
@@ -1128,7 +1128,8 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
 // packed bytes, 16 bytes of scales and 16 of biases per row per window) and x
 // (M rows x 512 bytes per window, from L2) stream through one LDS ring (6
 // slots for up to 32 rows of x, 3 for up to 64) by buffer-to-LDS DMA that all
-// 16 wavefronts issue.
+// 16 wavefronts issue; each wavefront reads its operands of window j + 1 from
+// LDS while it decodes and multiplies window j, one barrier per window.
 constexpr int kTlWaves = 16, kTlThreads = kTlWaves * 64;
 constexpr int kTlMinM = 6;                           // fewer rows take the shared-x GEMV form
 constexpr int kTlTiles = 2;                          // 32-row weight tiles per workgroup
@@ -1150,12 +1151,6 @@ template <int MT> struct TlShape {
     static constexpr int kLds = kStages * (kTlWSlot + kXSlot);
 };
 
-// lds_dma16 with the LDS address forced into a scalar register (the compiler
-// cannot always prove the slot arithmetic wave-uniform).
-__device__ __forceinline__ void tl_dma16(const __amdgpu_buffer_rsrc_t& rsrc, const void* lds, uint32_t voff) {
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(rsrc));
-}
 // s_waitcnt vmcnt(n) for a run-time n (0 .. 23; larger waits for everything).
 __device__ __forceinline__ void wait_vmcnt_rt(int n) {
     switch (n) {
@@ -1186,18 +1181,26 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
     }
 }
 
+// One lane's LDS reads of a window: two weight words, the group's scale and
+// bias bits, and the x operands of its two k-steps (bf16, per x tile).
+template <int MT> struct TlOps {
+    uint32_t word[kTlSteps];
+    u32x4 x[kTlSteps][MT];
+    uint32_t s, b;
+};
+
 // DMA instruction i of a window (issued by wavefront i % 16), lane l:
 //   i < 8: packed weights, 16-byte piece q = 64 i + l of the slot: row q / 8,
-//          slot position q % 8 holding the row's piece (q % 8) ^ ((row / 2) % 8)
-//          (rows are 128 bytes, half the banks: with the swizzle the 32 rows'
-//          word reads of a k-step fall on 32 different banks, 2-way at most);
+//          slot position q % 8 holding the row's piece (q % 8) ^ ((row / 2) % 8);
 //   i = 8, 9: the 64 rows' 16 bytes of scales, of biases;
 //   i >= 10: x, piece q = 64 (i - 10) + l: row q / 32, slot position q % 32
 //          holding chunk (q % 32) ^ (row % 16).
 // Window j + S - 1 (S slots) goes out after barrier j into the slot of window
-// j - 1, which every wavefront finished with before barrier j; each wavefront
-// waits for its own DMA of window j before barrier j. All offsets are per-lane, so the descriptors' range checks cover every
-// byte (rows past N or M read zeros).
+// j - 1, which every wavefront finished reading before barrier j; each
+// wavefront waits for its own DMA of window j + 1 before barrier j (its LDS
+// reads run one window ahead). A lane whose row lies past N or M has an
+// offset past its descriptor's range and reads zeros; an offset in range plus
+// the window's scalar offset stays inside its own row.
 template <int MT>
 __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
     const uint32_t* __restrict__ w, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -1213,51 +1216,64 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
     const int rows = min(kTlRows, N - n0);
     const int G = K / 32, nwin = K / kTlWinK;
     const uint32_t wrow = (uint32_t)K / 2u, srow = (uint32_t)G * 2u;
-    const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * wrow, (uint32_t)rows * wrow);
-    const __amdgpu_buffer_rsrc_t ssrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow, (uint32_t)rows * srow);
-    const __amdgpu_buffer_rsrc_t bsrc =
-        make_rsrc(reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow, (uint32_t)rows * srow);
-    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-
-    // This wavefront's DMA: instructions wave + 16 u.
+    // This wavefront's DMA: instructions i = wave + 16 u, u < per_window. All
+    // but the window is fixed for the launch and chosen here once: the
+    // instruction's descriptor, its LDS position in slot 0 and the slot
+    // stride, its lane offset, and the bytes a window advances (the
+    // instruction's scalar offset; every lane offset that is in range stays in
+    // its own row of W, scales, biases or x for every window).
     constexpr int kU = (Sh::kDma + kTlWaves - 1) / kTlWaves;
     const int per_window = (Sh::kDma - wave + kTlWaves - 1) / kTlWaves;
-    uint32_t off[kU];
+    static_assert(Sh::kDma > kTlWaves * (kU - 1), "every wavefront issues kU - 1 or kU instructions");
+    __amdgpu_buffer_rsrc_t rs[kU];
+    uint32_t off[kU], lbase[kU], lstride[kU], wstep[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int i = wave + kTlWaves * u;
-        if (i < kTlWDma - 2) {
+        const bool isw = i < kTlWDma - 2, iss = i == kTlWDma - 2, isb = i == kTlWDma - 1, isx = i >= kTlWDma;
+        const uint8_t* const base = isw   ? reinterpret_cast<const uint8_t*>(w) + (size_t)n0 * wrow
+                                    : iss ? reinterpret_cast<const uint8_t*>(scales) + (size_t)n0 * srow
+                                    : isb ? reinterpret_cast<const uint8_t*>(biases) + (size_t)n0 * srow
+                                          : reinterpret_cast<const uint8_t*>(x);
+        rs[u] = make_rsrc(base, isw ? (uint32_t)rows * wrow : isx ? (uint32_t)M * (uint32_t)K * 2u : (uint32_t)rows * srow);
+        lbase[u] = isw ? lds_addr(wring) + 1024u * (uint32_t)i
+                   : isx ? lds_addr(xring) + 1024u * (uint32_t)(i - kTlWDma)
+                         : lds_addr(wring) + kTlWBytes + (isb ? kTlSBytes : 0);
+        lstride[u] = isx ? Sh::kXSlot : kTlWSlot;
+        wstep[u] = isw ? kTlWRow : isx ? kTlXRow : 16;
+        if (isw) {
             const int q = 64 * i + lane, r = q >> 3, pc = (q & 7) ^ ((r >> 1) & 7);
             off[u] = r < rows ? (uint32_t)r * wrow + 16u * (uint32_t)pc : kOob;
-        } else if (i < kTlWDma) {
+        } else if (!isx) {
             off[u] = lane < rows ? (uint32_t)lane * srow : kOob;
         } else {
             const int q = 64 * (i - kTlWDma) + lane, m = q >> 5, c = (q & 31) ^ (m & 15);
             off[u] = m < M ? (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)c : kOob;
         }
     }
-    auto issue = [&](int win) {
-        const int slot = win % kS;
-        uint8_t* const ws = wring + slot * kTlWSlot;
-        uint8_t* const xs = xring + slot * Sh::kXSlot;
+    // Window win into ring slot sl (win % S; a constant wherever the step
+    // loop below calls it).
+    auto issue = [&](int sl, int win) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int i = wave + kTlWaves * u;
-            if (i >= Sh::kDma) break;
-            if (i < kTlWDma - 2)
-                tl_dma16(wsrc, ws + 1024 * i, off[u] + (uint32_t)(kTlWRow * win));
-            else if (i == kTlWDma - 2)
-                tl_dma16(ssrc, ws + kTlWBytes, off[u] + 16u * (uint32_t)win);
-            else if (i == kTlWDma - 1)
-                tl_dma16(bsrc, ws + kTlWBytes + kTlSBytes, off[u] + 16u * (uint32_t)win);
-            else
-                tl_dma16(xsrc, xs + 1024 * (i - kTlWDma), off[u] + (uint32_t)(kTlXRow * win));
+            if (u >= per_window) break;
+            const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lbase[u] + (uint32_t)sl * lstride[u]));
+            const int soff = __builtin_amdgcn_readfirstlane(win * (int)wstep[u]);
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(off[u]), "s"(rs[u]),
+                         "s"(soff));
         }
     };
-    for (int win = 0; win < kS - 1 && win < nwin; ++win) issue(win);
+    // Window 0 from every wavefront first: the barrier puts it ahead of the
+    // later windows in the compute unit's memory queue.
+    issue(0, 0);
+    raw_barrier();
+#pragma unroll
+    for (int win = 1; win < kS - 1; ++win)
+        if (win < nwin) issue(win, win);
 
+    // Wavefront (t, p) = (w / 8, w % 8) takes weight tile t and k-steps
+    // 2 p, 2 p + 1 (quantisation group p) of each window, against all MT x
+    // tiles; every output has 8 partial sums.
     const int t = wave / kTlParts, part = wave % kTlParts;
     const int h = lane >> 5, n = lane & 31, row = 32 * t + n;
     const uint32_t m_lo = vreg(0x000F000Fu), m_hi = vreg(0x00F000F0u), magic = vreg(0x64006400u);
@@ -1290,34 +1306,64 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-    // Window j in slot j % S (a constant: the loop below is unrolled by S).
-    auto step = [&](auto ws_c, int j) {
+    using Ops = TlOps<MT>;
+    // A window's LDS reads: the lane's weight words, its group's scale and
+    // bias bits and its x operands (bf16).
+    auto read = [&](auto ws_c) {
         constexpr int WS = decltype(ws_c)::value, XS = WS;
-        // Windows j + 1 .. min(j + S - 2, nwin - 1) may still be in flight.
-        wait_vmcnt_rt(min(kS - 2, nwin - 1 - j) * per_window);
-        raw_barrier();
-        if (j + kS - 1 < nwin) issue(j + kS - 1);
-        // Every LDS read of the window first (one wait), then the decodes,
-        // then the matrix work.
-        uint32_t word[kTlSteps];
-        u32x4 aop[kTlSteps][MT];
-        const uint32_t sraw = lds_ld<uint16_t>(sa + WS * kTlWSlot);
-        const uint32_t braw = lds_ld<uint16_t>(sa + WS * kTlWSlot + kTlSBytes);
+        Ops o;
+        o.s = lds_ld<uint16_t>(sa + WS * kTlWSlot);
+        o.b = lds_ld<uint16_t>(sa + WS * kTlWSlot + kTlSBytes);
 #pragma unroll
         for (int u = 0; u < kTlSteps; ++u) {
-            word[u] = lds_ld<uint32_t>(wa[u] + WS * kTlWSlot);
+            o.word[u] = lds_ld<uint32_t>(wa[u] + WS * kTlWSlot);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                aop[u][mt] = (MT > 1 && XS == 2) ? lds_ld<u32x4>(xa2[u][mt]) : lds_ld<u32x4>(xa[u][mt] + XS * Sh::kXSlot);
+                o.x[u][mt] = (MT > 1 && XS == 2) ? lds_ld<u32x4>(xa2[u][mt]) : lds_ld<u32x4>(xa[u][mt] + XS * Sh::kXSlot);
         }
-        const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(sraw), bf16_bits_to_f32(braw));
+        return o;
+    };
+    auto compute = [&](const Ops& o) {
+        const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(o.s), bf16_bits_to_f32(o.b));
         u32x4 bop[kTlSteps];
 #pragma unroll
-        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_f16(word[u], grp, m_lo, m_hi, magic);
+        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_f16(o.word[u], grp, m_lo, m_hi, magic);
 #pragma unroll
         for (int u = 0; u < kTlSteps; ++u)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32(bf16x8_to_f16x8(aop[u][mt]), bop[u], acc[mt]);
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32(bf16x8_to_f16x8(o.x[u][mt]), bop[u], acc[mt]);
+    };
+    // The reads run one window ahead of the arithmetic, so that a window's
+    // LDS traffic overlaps the previous window's decode and matrix work.
+    // Window 0: its DMA landed for every wavefront at the barrier.
+    wait_vmcnt_rt(min(kS - 2, nwin - 1) * per_window);
+    raw_barrier();
+    Ops ops[2];
+    ops[0] = read(std::integral_constant<int, 0>{});
+    // Step j: window j (slot j % S, a constant: the loop below is unrolled by
+    // S) from registers, window j + 1's reads into the other register set.
+    auto step = [&](auto ws_c, int j, Ops& cur, Ops& next) {
+        constexpr int WS = decltype(ws_c)::value;
+        // Window j + 1 has landed; windows j + 2 .. min(j + S - 2, nwin - 1)
+        // may still be in flight. The barrier also marks every wavefront's
+        // reads of window j - 1 done (they were used in step j - 1), so its
+        // slot takes window j + S - 1.
+        if constexpr (kS == 3) {
+            wait_vmcnt<0>();
+        } else if (j + kS - 2 < nwin) {  // the usual case: windows j + 2 .. j + S - 2 exist
+            if (per_window == kU)
+                wait_vmcnt<(kS - 3) * kU>();
+            else
+                wait_vmcnt<(kS - 3) * (kU - 1)>();
+        } else {
+            wait_vmcnt_rt(max(0, nwin - 2 - j) * per_window);
+        }
+        wait_lgkmcnt0();
+        raw_barrier();
+        if (j + kS - 1 < nwin) issue((WS + kS - 1) % kS, j + kS - 1);
+        if (j + 1 < nwin) next = read(std::integral_constant<int, (WS + 1) % kS>{});
+        __builtin_amdgcn_sched_barrier(0);  // the reads go out before the arithmetic below
+        compute(cur);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -1328,76 +1374,106 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
     int j = 0;
     if constexpr (kS == 6) {
         for (; j + 5 < nwin; j += 6) {
-            step(I0{}, j);
-            step(I1{}, j + 1);
-            step(I2{}, j + 2);
-            step(I3{}, j + 3);
-            step(I4{}, j + 4);
-            step(I5{}, j + 5);
+            step(I0{}, j, ops[0], ops[1]);
+            step(I1{}, j + 1, ops[1], ops[0]);
+            step(I2{}, j + 2, ops[0], ops[1]);
+            step(I3{}, j + 3, ops[1], ops[0]);
+            step(I4{}, j + 4, ops[0], ops[1]);
+            step(I5{}, j + 5, ops[1], ops[0]);
         }
-        if (j < nwin) step(I0{}, j);
-        if (j + 1 < nwin) step(I1{}, j + 1);
-        if (j + 2 < nwin) step(I2{}, j + 2);
-        if (j + 3 < nwin) step(I3{}, j + 3);
-        if (j + 4 < nwin) step(I4{}, j + 4);
+        if (j < nwin) step(I0{}, j, ops[0], ops[1]);
+        if (j + 1 < nwin) step(I1{}, j + 1, ops[1], ops[0]);
+        if (j + 2 < nwin) step(I2{}, j + 2, ops[0], ops[1]);
+        if (j + 3 < nwin) step(I3{}, j + 3, ops[1], ops[0]);
+        if (j + 4 < nwin) step(I4{}, j + 4, ops[0], ops[1]);
     } else {
         static_assert(kS == 3, "slot sequences for 6 and 3 slots");
-        for (; j + 2 < nwin; j += 3) {
-            step(I0{}, j);
-            step(I1{}, j + 1);
-            step(I2{}, j + 2);
+        // Three slots and two register sets: the loop runs six windows a turn.
+        for (; j + 5 < nwin; j += 6) {
+            step(I0{}, j, ops[0], ops[1]);
+            step(I1{}, j + 1, ops[1], ops[0]);
+            step(I2{}, j + 2, ops[0], ops[1]);
+            step(I0{}, j + 3, ops[1], ops[0]);
+            step(I1{}, j + 4, ops[0], ops[1]);
+            step(I2{}, j + 5, ops[1], ops[0]);
         }
-        if (j < nwin) step(I0{}, j);
-        if (j + 1 < nwin) step(I1{}, j + 1);
+        if (j < nwin) step(I0{}, j, ops[0], ops[1]);
+        if (j + 1 < nwin) step(I1{}, j + 1, ops[1], ops[0]);
+        if (j + 2 < nwin) step(I2{}, j + 2, ops[0], ops[1]);
+        if (j + 3 < nwin) step(I0{}, j + 3, ops[1], ops[0]);
+        if (j + 4 < nwin) step(I1{}, j + 4, ops[0], ops[1]);
     }
     // The rings are free (every DMA landed before the last barrier, and the
-    // barrier below waits for every wavefront's last reads). Wavefront p of a
-    // tile owns accumulator registers 2 p, 2 p + 1 (of each x tile): it writes
-    // the other 14, then adds the seven partial sums of its own two.
+    // barrier below waits for every wavefront's last reads). Of a tile's 8
+    // wavefronts, wavefront p finishes the kOwn registers f = kOwn p + e
+    // (flat index f = 16 mt + i over its accumulator tiles): it writes its
+    // registers in groups of four, then adds the 7 other partial sums of its
+    // own, in order of the writer. With kOwn = 4 its own group is not written.
     raw_barrier();
-    float* const red = reinterpret_cast<float*>(lds);
-    // red[tile][writer][mt][slot][lane], 14 slots: writer q's register i (not
-    // its own 2 q, 2 q + 1) at slot i < 2 q ? i : i - 2.
-    static_assert(kTlTiles * kTlParts * MT * 14 * 64 * 4 <= Sh::kLds, "exchange area fits the rings");
+    constexpr int kRegs = 16 * MT, kOwn = kRegs / kTlParts;  // its registers, the ones it finishes
+    constexpr bool kSkipOwn = kOwn == 4;
+    constexpr int kGroups = kRegs / 4 - (kSkipOwn ? 1 : 0);  // groups a wavefront writes
+    const int grp0 = t * kTlParts;                           // the tile's first writer
+    // red[writer][group slot][lane]: writer q's group g (registers 4 g .. 4 g + 3)
+    // at slot g, or with kSkipOwn g < q ? g : g - 1.
+    u32x4* const red = reinterpret_cast<u32x4*>(lds);
+    static_assert(kTlWaves * kGroups * 64 * 16 <= Sh::kLds, "exchange area fits the rings");
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if ((i >> 1) != part)
-                red[(((t * kTlParts + part) * MT + mt) * 14 + (i < 2 * part ? i : i - 2)) * 64 + lane] = acc[mt][i];
+    for (int g = 0; g < kRegs / 4; ++g) {
+        const u32x4 v = {__float_as_uint(acc[g >> 2][4 * (g & 3)]), __float_as_uint(acc[g >> 2][4 * (g & 3) + 1]),
+                         __float_as_uint(acc[g >> 2][4 * (g & 3) + 2]), __float_as_uint(acc[g >> 2][4 * (g & 3) + 3])};
+        if (!kSkipOwn)
+            red[((grp0 + part) * kGroups + g) * 64 + lane] = v;
+        else if (g != part)
+            red[((grp0 + part) * kGroups + (g < part ? g : g - 1)) * 64 + lane] = v;
+    }
+    wait_lgkmcnt0();  // the partial sums written before another wavefront reads them
     raw_barrier();
-    const int col = n0 + row;
-    float fin[MT][2];
+    const int f0 = kOwn * part, gown = f0 >> 2;
+    // the wavefront's own partial sums (a run-time register index)
+    float fin[kOwn];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int e = 0; e < kOwn; ++e) {
+        float v = 0.f;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int i = 2 * part + e;
-            // the wavefront's own partial sum of register i (a run-time index)
-            float v = 0.f;
+        for (int r = 0; r < kRegs; ++r) v = r == f0 + e ? acc[r >> 4][r & 15] : v;
+        fin[e] = v;
+    }
+    // every writer's group read at once (the own one, q = part, at a valid
+    // position and not added), then added in order of q
+    float o[kTlParts][kOwn];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v = r == i ? acc[mt][r] : v;
+    for (int q = 0; q < kTlParts; ++q) {
+        const int slot = !kSkipOwn ? gown : gown < q ? gown : q == part ? 0 : gown - 1;
+        const float* const src = reinterpret_cast<const float*>(&red[((grp0 + q) * kGroups + slot) * 64 + lane]) + (f0 & 3);
+        if constexpr (kOwn == 4) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-            for (int q = 0; q < kTlParts; ++q)
-                if (q != part) v += red[(((t * kTlParts + q) * MT + mt) * 14 + (i < 2 * q ? i : i - 2)) * 64 + lane];
-            fin[mt][e] = v;
+            for (int e = 0; e < 4; ++e) o[q][e] = __uint_as_float(v[e]);
+        } else {
+            static_assert(kOwn == 2, "two or four registers per wavefront");
+            const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+            o[q][0] = __uint_as_float(v[0]);
+            o[q][1] = __uint_as_float(v[1]);
         }
+    }
+#pragma unroll
+    for (int q = 0; q < kTlParts; ++q)
+#pragma unroll
+        for (int e = 0; e < kOwn; ++e) fin[e] = q != part ? fin[e] + o[q][e] : fin[e];
+    // Lane (n, h) holds, of accumulator register i, x row 8 (i / 4) + 4 h + i % 4
+    // of the x tile and weight row n of the tile; the wavefront's registers
+    // lie in x tile f0 / 16.
+    static_assert(16 % kOwn == 0, "a wavefront's registers lie in one accumulator tile");
+    const int mt_own = f0 >> 4, col = n0 + row;
     // Range check over the finished sums (every x row, the tile's weight rows).
-    float fl[MT * 2];
+    if (any_nonfinite(fin)) affine_range_scan(x, w, scales, biases, M, K, N, 0, M, n0 + 32 * t, n0 + 32 * t + 32, events);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) fl[mt * 2 + e] = fin[mt][e];
-    if (any_nonfinite(fl)) affine_range_scan(x, w, scales, biases, M, K, N, 0, M, n0 + 32 * t, n0 + 32 * t + 32, events);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            // Lane (n, h) holds x rows 8 (i / 4) + 4 h + i % 4 of the tile, weight row n.
-            const int i = 2 * part + e;
-            const int m = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (m < M && col < N) y[(size_t)m * N + col] = f32_to_bf16_bits(fin[mt][e]);
-        }
+    for (int e = 0; e < kOwn; ++e) {
+        const int i = (f0 + e) & 15;
+        const int m = 32 * mt_own + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (m < M && col < N) y[(size_t)m * N + col] = f32_to_bf16_bits(fin[e]);
+    }
 }
 
 }  // namespace w4mi
