@@ -821,11 +821,11 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_lut4_kernel(const uint16_t* 
 // decoded-weight route at M >= 128) a step's weights are 64 rows k of the
 // tile's 96 columns, contiguous along n, and the first 6 producers decode
 // one (2-row, 8-column) item per lane instead: a packed dword (8 codes along
-// n) and the block's scale for each of the 2 rows, each byte looked up in a
-// 256-entry table of f32 pairs (book[hi], book[lo]) kept in LDS per
-// decoding wavefront, multiplied by its row's scale in f32 and rounded to
-// binary16, and each column's 2 k values written to the [n][k] tile as one
-// 4-byte store. That needs N % 8 == 0 and a power-of-two block of at least 8
+// n) and the block's scale for each of the 2 rows, each code looked up in
+// the 16 f32 codebook entries kept in LDS (64 lanes read at most 16
+// addresses, one per bank: no bank conflicts), multiplied by its row's scale
+// in f32 and rounded to binary16, and each column's 2 k values written to
+// the [n][k] tile as one 4-byte store. That needs N % 8 == 0 and a power-of-two block of at least 8
 // (a packed dword never straddles a block).
 constexpr int kLBM = 256, kLBN = 96;
 constexpr int kLConsumers = 4, kLProducers = 8;
@@ -873,7 +873,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
     Book16 book, uint16_t* __restrict__ y, int M, int K, int N, int block_shift) {
     __shared__ __attribute__((aligned(1024))) uint8_t xring[3][kDXBytes];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kLBN * kPLd];
-    __shared__ __attribute__((aligned(16))) f32x2 kn_pairs[KN ? kLKnDecodeWaves * 256 : 1];
+    __shared__ __attribute__((aligned(16))) float kn_book[16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tiles_m = (M + kLBM - 1) / kLBM, tiles_n = (N + kLBN - 1) / kLBN;
@@ -900,20 +900,14 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
         const int item = 64 * pw + lane, kq = item / kLKnCols, cg = item % kLKnCols;
         const uint32_t col = (uint32_t)(n0 + 8 * cg);
         const bool live = decoder && col < (uint32_t)N;
-        const uint32_t pairs = lds_addr(&kn_pairs[decoder ? pw * 256 : 0]);
-        if (decoder) {
-            // this wavefront's pair table: entry v = (book[v >> 4], book[v & 15])
+        // Every decoding wavefront writes the same 16 entries (and waits for
+        // its own writes before its first lookup: no barrier is needed).
+        const uint32_t kb = lds_addr(kn_book);
+        if (decoder && lane < 16) {
+            float v = 0.f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t v = 4u * (uint32_t)lane + (uint32_t)t;
-                float hi = 0.f, lo = 0.f;
-#pragma unroll
-                for (uint32_t c = 0; c < 16; ++c) {
-                    hi = (v >> 4) == c ? book.v[c] : hi;
-                    lo = (v & 15u) == c ? book.v[c] : lo;
-                }
-                lds_st(pairs + 8u * v, f32x2{hi, lo});
-            }
+            for (int c = 0; c < 16; ++c) v = lane == c ? book.v[c] : v;
+            lds_st(kb + 4u * (uint32_t)lane, v);
         }
         LutKnWeights ring[3];
         auto issue = [&](int kt, int kw, uint8_t* xslot, LutKnWeights& e) {
@@ -938,12 +932,22 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
         auto decode = [&](const LutKnWeights& e, int buf) {
             const float s0 = f16_bits_to_f32(e.s[0]), s1 = f16_bits_to_f32(e.s[1]);
             const uint32_t dst = lds_addr(Bs[buf]) + 2u * (uint32_t)(8 * cg * kPLd) + kofs;
+            // byte offsets 4 code of each row's codes: high nibbles (even
+            // columns) and low nibbles (odd columns), one byte per code
+            uint32_t hi4[kLKnRows], lo4[kLKnRows];
+#pragma unroll
+            for (int i = 0; i < kLKnRows; ++i) {
+                hi4[i] = (e.w[i] >> 2) & 0x3C3C3C3Cu;
+                lo4[i] = (e.w[i] << 2) & 0x3C3C3C3Cu;
+            }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const f32x2 p0 = lds_ld<f32x2>(pairs + 8u * ((e.w[0] >> (8 * b)) & 0xFFu));
-                const f32x2 p1 = lds_ld<f32x2>(pairs + 8u * ((e.w[1] >> (8 * b)) & 0xFFu));
-                lds_st(dst + 2u * (uint32_t)((2 * b) * kPLd), pack_f16x2(p0[0] * s0, p1[0] * s1));
-                lds_st(dst + 2u * (uint32_t)((2 * b + 1) * kPLd), pack_f16x2(p0[1] * s0, p1[1] * s1));
+                const float h0 = lds_ld<float>(kb + ((hi4[0] >> (8 * b)) & 0xFFu));
+                const float h1 = lds_ld<float>(kb + ((hi4[1] >> (8 * b)) & 0xFFu));
+                const float l0 = lds_ld<float>(kb + ((lo4[0] >> (8 * b)) & 0xFFu));
+                const float l1 = lds_ld<float>(kb + ((lo4[1] >> (8 * b)) & 0xFFu));
+                lds_st(dst + 2u * (uint32_t)((2 * b) * kPLd), pack_f16x2(h0 * s0, h1 * s1));
+                lds_st(dst + 2u * (uint32_t)((2 * b + 1) * kPLd), pack_f16x2(l0 * s0, l1 * s1));
             }
         };
         constexpr int kWl = 2 * kLKnRows;  // weight loads per decoding lane per step
@@ -952,7 +956,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
         issue(1, 2, xring[1], ring[2]);
         if (decoder) {
             wait_vmcnt<2 * (kLXb + kWl)>();
-            wait_lgkmcnt0();  // the pair table written
+            wait_lgkmcnt0();  // the codebook written
             lut_fence(ring[0]);
             decode(ring[0], 0);
         }
