@@ -70,10 +70,11 @@ const char* w4_version(void);
  * This library implements qmm_affine4 for K and N up to 2^21 (2,097,152);
  * larger valid shapes return W4_EUNSUPPORTED.
  *
- * Operand precision. qmv_affine4, and qmm_affine4 below 6 rows (or up to 16
- * rows when K % 256 != 0 and K <= 8192), multiply the bf16 x by the exact
- * nibbles and apply scale and bias per group in f32: no range limit beyond
- * f32's. Every other qmm_affine4 shape runs on the matrix cores in binary16,
+ * Operand precision. qmv_affine4, and qmm_affine4 with K <= 8192 and either
+ * at most 4 rows (K <= 4096) or 2 rows (K > 4096), or, when K % 256 != 0 or
+ * the scales or biases are not 4-byte aligned, at most 16 rows, multiply the
+ * bf16 x by the exact nibbles and apply scale and bias per group in f32: no
+ * range limit beyond f32's. Every other qmm_affine4 shape runs on the matrix cores in binary16,
  * as [P1]'s kernel does (module doc "Algorithm"): x is converted bf16 ->
  * binary16 (round to nearest even; exact for magnitudes 2^-14 .. 65504,
  * binary16's subnormal step below) and each weight is q * scale + bias

@@ -112,9 +112,13 @@ def test_qmv_affine4(K, N, seed):
     (300, 768, 160),                      # 12 K steps: one unrolled round, no tail
     (270, 2048, 96),                      # 32 K steps: two rounds and a tail of 8
     (520, 5120, 224),                     # 80 K steps: six rounds and a tail of 8, three row tiles
-    # the GEMV form (every weight row read once for all rows): fewer than 6 rows, or up to 16
-    # rows when K % 256 != 0 (K <= 8192)
+    # the GEMV form (every weight row read once for all rows): the rows it applies in one pass (4
+    # for K <= 4096, 2 above), or up to 16 rows when K % 256 != 0 (K <= 8192)
     (2, 4096, 14336),                     # the decode workload's weights, two rows (batches of 2)
+    (4, 4096, 256),                       # one pass of 4 rows: the GEMV form
+    (2, 8192, 64),                        # K > 4096, one pass of 2 rows: the GEMV form
+    (5, 4096, 256),                       # two passes: the weight-tile form instead
+    (3, 8192, 64),                        # K > 4096, two passes of 2: the weight-tile form
     (3, 96, 64),                          # 3 groups, one batch of 4 with a missing row
     (5, 2080, 160),                       # ragged second chunk, a 1-row second batch
     (8, 4160, 256),                       # 3 chunks: batches of 2
@@ -149,14 +153,16 @@ def test_qmm_affine4_small(M, K, N):
     _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"qmm M={M} K={K} N={N}")
 
 
-# Short K on every route of qmm_affine4, element by element: the GEMV forms (M < 6, and M <= 16 with
-# K % 256 != 0), the 64x128-tile kernel (17 <= M <= 64 with K % 256 != 0), the register-staged prefill
-# kernel (M > 64, K % 64 == 32), the specialised-wavefront prefill kernel (M > 64, K % 64 == 0) and the
-# weight-tile kernel (6 <= M <= 64, K % 256 == 0). Small K is where operand rounding weighs most against
-# the bound (few products, small |ref|).
+# Short K on every route of qmm_affine4, element by element: the GEMV forms (the rows one pass takes,
+# 4 up to K = 4096, and M <= 16 with K % 256 != 0), the 64x128-tile kernel (17 <= M <= 64 with
+# K % 256 != 0), the register-staged prefill kernel (M > 64, K % 64 == 32), the specialised-wavefront
+# prefill kernel (M > 64, K % 64 == 0) and the weight-tile kernel (past one GEMV pass up to 64 rows,
+# K % 256 == 0). Small K is where operand rounding weighs most against the bound (few products, small
+# |ref|).
 @pytest.mark.parametrize("M,K,N", [(m, k, n) for k, n in ((32, 96), (64, 128), (96, 160))
                                    for m in (2, 5, 6, 12, 16, 17, 40, 64, 65, 100, 300)]
-                         + [(6, 256, 96), (20, 256, 128), (40, 512, 64), (64, 256, 160)])
+                         + [(4, 256, 64), (5, 256, 64), (6, 256, 96), (20, 256, 128), (40, 512, 64),
+                            (64, 256, 160)])
 def test_qmm_affine4_short_k_every_route(M, K, N):
     c = synth.affine_case(M, K, N, seed=7 * M + K + N)
     w, s, b, x = _affine_dev(c)
@@ -234,10 +240,11 @@ def test_qmm_affine4_gemv_forms_hold_large_x_exactly():
 
 
 @pytest.mark.gpu
-def test_qmm_affine4_small_unaligned_scales():
+@pytest.mark.parametrize("M,K,N", [(24, 512, 96), (5, 4096, 64)])
+def test_qmm_affine4_small_unaligned_scales(M, K, N):
     """Scales and biases only 2-byte aligned: the weight-tile form (4-byte DMA offsets) is not
-    taken; the 64x128-tile matrix-core kernel gives the same result."""
-    M, K, N = 24, 512, 96
+    taken; the 64x128-tile matrix-core kernel (24 rows) or the GEMV form in two passes (5 rows)
+    gives the same result."""
     c = synth.affine_case(M, K, N, seed=5)
     w, s, b, x = _affine_dev(c)
     s2 = torch.empty(s.numel() + 1, dtype=torch.bfloat16, device="cuda")[1:].view(N, K // 32)

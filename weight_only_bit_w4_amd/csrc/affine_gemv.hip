@@ -433,11 +433,16 @@ namespace w4mi {
 // The shared-x form for M rows of x (1 <= M <= kAffineBatchRows, K <=
 // kAffineBatchMaxK = 64 * 32 * kXChunks): MB rows of x per batch (4, or 2 where 4 chunks would take 80 KB
 // of LDS), one workgroup per 16 weight rows.
+int xlds_batch_rows(int M, int K) {
+    const int chunks = (K / 32 + kWave - 1) / kWave;
+    return M == 1 ? 1 : (M == 2 || chunks > 2) ? 2 : 4;
+}
+
 void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, const uint16_t* x, uint16_t* y,
                  int M, int K, int N, hipStream_t s) {
     static_assert(kAffineBatchMaxK == 32 * kWave * kXChunks, "four chunks of 64 groups");
     const int chunks = (K / 32 + kWave - 1) / kWave;
-    const int mb = M == 1 ? 1 : (M == 2 || chunks > 2) ? 2 : 4;
+    const int mb = xlds_batch_rows(M, K);
     const dim3 grid((unsigned)(N / (kXWaves * kXRows))), block(kWave * kXWaves);
     if (mb == 1) {
         // One row of x: pick 8, 7 or 6 wavefronts per workgroup so that the

@@ -1135,7 +1135,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
 // 16 wavefronts issue; each wavefront reads its operands of window j + 1 from
 // LDS while it decodes and multiplies window j, one barrier per window.
 constexpr int kTlWaves = 16, kTlThreads = kTlWaves * 64;
-constexpr int kTlMinM = 6;                           // fewer rows take the shared-x GEMV form
+constexpr int kTlMinM = 6;                           // fewer rows may take the shared-x GEMV form
 constexpr int kTlTiles = 2;                          // 32-row weight tiles per workgroup
 constexpr int kTlParts = kTlWaves / kTlTiles;        // 8 wavefronts share a tile's K
 constexpr int kTlSteps = 16 / kTlParts;              // k-steps (16 of K) per wavefront per window
@@ -1541,8 +1541,10 @@ extern "C" w4_status qmm_affine4(const uint32_t* w, const uint16_t* scales, cons
     if (st != W4_OK) return st;
     hipStream_t s = as_stream(stream);
     const bool tiles_ok = K % kTlWinK == 0 && ((uintptr_t)scales & 3u) == 0 && ((uintptr_t)biases & 3u) == 0;
-    if (M < kTlMinM && K <= kAffineBatchMaxK) {
-        // A few rows: the GEMV form (each weight row read once for all of them).
+    if (M < kTlMinM && K <= kAffineBatchMaxK && (!tiles_ok || M <= xlds_batch_rows((int)M, (int)K))) {
+        // A few rows: the GEMV form (each weight row read once for all of
+        // them), where its rows fit one pass or the weight-tile form does not
+        // apply; a second pass costs more than the tile form's whole launch.
         launch_xlds(w, scales, biases, x, y, (int)M, (int)K, (int)N, s);
     } else if (M <= 64 && tiles_ok) {
         // Up to 64 rows: weight tiles streamed once through the matrix cores.

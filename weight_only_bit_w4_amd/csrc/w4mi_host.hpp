@@ -43,6 +43,9 @@ constexpr int kAffineBatchRows = 16;
 constexpr int64_t kAffineBatchMaxK = 8192;
 void launch_xlds(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, const uint16_t* x, uint16_t* y,
                  int M, int K, int N, hipStream_t s);
+// Rows of x the GEMV form applies per pass over its registers' weights (1, 2
+// or 4); M rows take ceil(M / that) passes, each repeating the decode.
+int xlds_batch_rows(int M, int K);
 
 // Half-precision lookup matmul with the weight stored [K, N] (lut_f32.hip),
 // any K, N and even block, M up to 4 * 65535.
