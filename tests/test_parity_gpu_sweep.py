@@ -63,6 +63,30 @@ def test_sweep_prefill(seed):
     _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"sweep prefill seed={seed} M={M} K={K} N={N}")
 
 
+def _tiles_shape(seed):
+    # The weight-tile form (K % 256 == 0, rows past one pass of the GEMV form up to 64) and its
+    # boundary (3 and 4 rows take the GEMV form up to K = 4096, the tile form above): one or two x
+    # tiles, 1 to 24 windows of K (ring wrap and tails of every length), and N an odd multiple of 32
+    # for about half the seeds (a last workgroup with one weight tile).
+    rng = np.random.default_rng(1700 + seed)
+    M = int(rng.choice([3, 4, 5, 6, 7, 11, 19, 31, 32, 33, 40, 57, 64]))
+    K = 256 * int(rng.integers(1, 25))
+    N = 32 * int(rng.integers(1, 41))
+    return M, K, N
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_sweep_weight_tiles(seed):
+    M, K, N = _tiles_shape(seed)
+    c = synth.affine_case(M, K, N, seed=200 + seed)
+    w, s, b, x = _affine_dev(c)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"sweep weight tiles seed={seed} M={M} K={K} N={N}")
+
+
 def _lut_shape(seed):
     rng = np.random.default_rng(2000 + seed)
     block = int(rng.choice([8, 16, 32, 64, 128]))
