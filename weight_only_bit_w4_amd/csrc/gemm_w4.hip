@@ -1019,8 +1019,36 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(3, 3)
                 asm_load_u16(e.s, ssrc, wl ? so : kOob, 0);
             }
         };
+        // With blocks of 64 or more the four lanes of a quad (one row's four K
+        // quarters of a step) share a scale: each builds a quarter of the
+        // table (entries 4 q .. 4 q + 3, its planes lo[q] and hi[q]) and takes
+        // the other quarters from its neighbours by quad permutes.
+        const bool quad = block_shift >= 6;
+        float bq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) v = q == qq ? book.v[4 * qq + i] : v;
+            bq[i] = v;
+        }
         auto decode = [&](const LutWeights& e, int buf) {
-            const LutPlanes P = lut_planes(book, f16_bits_to_f32(e.s));
+            const float sc = f16_bits_to_f32(e.s);
+            LutPlanes P;
+            if (quad) {
+                const uint32_t t0 = pack_f16x2(bq[0] * sc, bq[1] * sc), t1 = pack_f16x2(bq[2] * sc, bq[3] * sc);
+                const uint32_t lo = __builtin_amdgcn_perm(t1, t0, 0x06040200u), hi = __builtin_amdgcn_perm(t1, t0, 0x07050301u);
+                P.lo[0] = __builtin_amdgcn_update_dpp(0u, lo, 0x00, 0xF, 0xF, false);
+                P.lo[1] = __builtin_amdgcn_update_dpp(0u, lo, 0x55, 0xF, 0xF, false);
+                P.lo[2] = __builtin_amdgcn_update_dpp(0u, lo, 0xAA, 0xF, 0xF, false);
+                P.lo[3] = __builtin_amdgcn_update_dpp(0u, lo, 0xFF, 0xF, 0xF, false);
+                P.hi[0] = __builtin_amdgcn_update_dpp(0u, hi, 0x00, 0xF, 0xF, false);
+                P.hi[1] = __builtin_amdgcn_update_dpp(0u, hi, 0x55, 0xF, 0xF, false);
+                P.hi[2] = __builtin_amdgcn_update_dpp(0u, hi, 0xAA, 0xF, 0xF, false);
+                P.hi[3] = __builtin_amdgcn_update_dpp(0u, hi, 0xFF, 0xF, 0xF, false);
+            } else {
+                P = lut_planes(book, sc);
+            }
             uint16_t* dst = bdst + buf * (kLBN * kPLd);
             *reinterpret_cast<u32x4*>(dst) = lut_decode8(e.words[0], P);
             *reinterpret_cast<u32x4*>(dst + 8) = lut_decode8(e.words[1], P);
