@@ -78,7 +78,10 @@ const char* w4_version(void);
  * as [P1]'s kernel does (module doc "Algorithm"): x is converted bf16 ->
  * binary16 (round to nearest even; exact for magnitudes 2^-14 .. 65504,
  * binary16's subnormal step below) and each weight is q * scale + bias
- * rounded once to binary16. A finite x (or weight) of magnitude 65520 or
+ * rounded once to binary16 (exactly so when bias = 0 or |bias| lies within
+ * about 2^-6 .. 2^15 of |scale|, as it does for bias = -zero_point * scale;
+ * outside that band an f32 step can round first, by at most 2^-14 |scale|).
+ * A finite x (or weight) of magnitude 65520 or
  * more overflows binary16: the outputs of its row of x (or weight row) come
  * out as infinities or NaN, and the call adds one per affected output tile
  * to the device's range-event count (w4_range_events). Infinite or NaN

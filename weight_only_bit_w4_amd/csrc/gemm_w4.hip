@@ -706,7 +706,8 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3
             }
             const AffineGroupF16 grp = affine_group_f16(sf, bf);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) lds_st<u32x4>(bdst + wb + 16 * i, affine_word_f16(e.words[i], grp, m_lo, m_hi, magic));
+            for (int i = 0; i < 2; ++i)
+                lds_st<u32x4>(bdst + wb + 16 * i, affine_word_f16<true>(e.words[i], grp, m_lo, m_hi, magic));
         };
         // The prologue issues steps 0, 1, 2 in the loop's order (the
         // scheduling barriers keep the compiler from interleaving them, so its
@@ -1359,7 +1360,7 @@ __global__ __launch_bounds__(kTlThreads) void qmm_affine4_tiles_kernel(
         const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(o.s), bf16_bits_to_f32(o.b));
         u32x4 bop[kTlSteps];
 #pragma unroll
-        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_f16(o.word[u], grp, m_lo, m_hi, magic);
+        for (int u = 0; u < kTlSteps; ++u) bop[u] = affine_word_f16<MT == 1>(o.word[u], grp, m_lo, m_hi, magic);
 #pragma unroll
         for (int u = 0; u < kTlSteps; ++u)
 #pragma unroll

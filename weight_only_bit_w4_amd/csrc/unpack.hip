@@ -16,7 +16,8 @@ constexpr int kUnpackThreads = 256;
 // neighbours (affine_pairs2_biased_bf16, as the low word ahead of the next
 // word and as the high word after the previous one), and the binary16 word
 // decode of the prefill and weight-tile kernels (affine_word_f16 with scale
-// 1 and bias 0, which gives q exactly).
+// 1 and bias 0, which gives q exactly, in both its forms: rounded in f32
+// registers and straight into register halves).
 __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __restrict__ q, int64_t words) {
     const int64_t i = (int64_t)blockIdx.x * kUnpackThreads + threadIdx.x;
     if (i >= words) return;
@@ -35,13 +36,15 @@ __global__ void unpack_affine_kernel(const uint32_t* __restrict__ w, uint8_t* __
         out[p] = (uint8_t)(pair & 0xFu);
         out[p + 4] = (uint8_t)((pair >> 16) & 0xFu);
     }
-    const u32x4 h = affine_word_f16(word, affine_group_f16(1.f, 0.f), vreg(0x000F000Fu), vreg(0x00F000F0u),
-                                    vreg(0x64006400u));
+    const AffineGroupF16 unit = affine_group_f16(1.f, 0.f);
+    const u32x4 h = affine_word_f16<false>(word, unit, vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u));
+    const u32x4 h32 = affine_word_f16<true>(word, unit, vreg(0x000F000Fu), vreg(0x00F000F0u), vreg(0x64006400u));
+    const bool forms_agree = h[0] == h32[0] && h[1] == h32[1] && h[2] == h32[2] && h[3] == h32[3];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t bits = (j & 1) ? (h[j / 2] >> 16) : (h[j / 2] & 0xFFFFu);
         const float v = f16_bits_to_f32(bits);
-        const bool same = pairs_agree && out[j] == affine_nibble(word, j) && v == (float)out[j];
+        const bool same = pairs_agree && forms_agree && out[j] == affine_nibble(word, j) && v == (float)out[j];
         q[i * 8 + j] = same ? out[j] : (uint8_t)0xFF;
     }
 }

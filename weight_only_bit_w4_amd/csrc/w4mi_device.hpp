@@ -112,13 +112,21 @@ __device__ __forceinline__ AffineGroupF16 affine_group_f16(float s, float b) {
     return AffineGroupF16{s, __builtin_fmaf(-1024.f, s, b), 0.0625f * s, __builtin_fmaf(-64.f, s, b)};
 }
 // Eight affine weights of one word (k = 8j .. 8j + 7) as binary16 pairs in k
-// order, w = q s + b rounded once to binary16. One AND-OR per nibble pair
-// places the nibble in a binary16 mantissa under the exponent of 1024
-// (magic 0x6400): the even nibbles of a byte read as 1024 + q, the odd ones
-// (bits 4..7) as 1024 + 16 q; v_fma_mix then forms (1024 + q) s + (b - 1024 s)
-// or (1024 + 16 q) s/16 + (b - 64 s) in f32 and rounds to binary16.
-// m_lo = 0x000F000F, m_hi = 0x00F000F0, magic = 0x64006400 in vector
-// registers (vreg).
+// order, w = q s + b rounded to binary16. One AND-OR per nibble pair places
+// the nibble in a binary16 mantissa under the exponent of 1024 (magic
+// 0x6400): the even nibbles of a byte read as 1024 + q, the odd ones (bits
+// 4..7) as 1024 + 16 q; a fused multiply-add then forms (1024 + q) s +
+// (b - 1024 s) or (1024 + 16 q) s/16 + (b - 64 s) in f32 and that is rounded
+// to binary16. The f32 value is q s + b exactly when b = 0 or |b| lies within
+// about 2^-6 .. 2^15 of |s| (both terms then fit f32's 24 bits), so the
+// weight is q s + b rounded once; outside that band the f32 step rounds first
+// (by at most 2^-14 |s|). F32: the eight sums round in f32 registers and
+// v_cvt_pk_f16_f32 packs them (v_fma_mix_f32 issues in about 3.4 cycles per
+// wave64 instruction, the half-writing v_fma_mix{lo,hi}_f16 in 5.9);
+// otherwise they round straight into register halves (fewer registers). Both
+// give the same bits. m_lo = 0x000F000F, m_hi = 0x00F000F0, magic =
+// 0x64006400 in vector registers (vreg).
+template <bool F32 = false>
 __device__ __forceinline__ u32x4 affine_word_f16(uint32_t word, const AffineGroupF16& g, uint32_t m_lo, uint32_t m_hi,
                                                  uint32_t magic) {
     const uint32_t w8 = word >> 8;
@@ -126,16 +134,27 @@ __device__ __forceinline__ u32x4 affine_word_f16(uint32_t word, const AffineGrou
     const f16x2 p1 = as_f16x2(and_or_u32(word, m_hi, magic));  // 1024 + 16 n1, 1024 + 16 n5
     const f16x2 p2 = as_f16x2(and_or_u32(w8, m_lo, magic));    // 1024 + n2, 1024 + n6
     const f16x2 p3 = as_f16x2(and_or_u32(w8, m_hi, magic));    // 1024 + 16 n3, 1024 + 16 n7
-    f16x2 r0, r1, r2, r3;
-    r0[0] = (_Float16)__builtin_fmaf((float)p0[0], g.s, g.c);
-    r0[1] = (_Float16)__builtin_fmaf((float)p1[0], g.s16, g.c16);
-    r1[0] = (_Float16)__builtin_fmaf((float)p2[0], g.s, g.c);
-    r1[1] = (_Float16)__builtin_fmaf((float)p3[0], g.s16, g.c16);
-    r2[0] = (_Float16)__builtin_fmaf((float)p0[1], g.s, g.c);
-    r2[1] = (_Float16)__builtin_fmaf((float)p1[1], g.s16, g.c16);
-    r3[0] = (_Float16)__builtin_fmaf((float)p2[1], g.s, g.c);
-    r3[1] = (_Float16)__builtin_fmaf((float)p3[1], g.s16, g.c16);
-    return u32x4{as_u32(r0), as_u32(r1), as_u32(r2), as_u32(r3)};
+    if constexpr (F32) {
+        float f0 = __builtin_fmaf((float)p0[0], g.s, g.c), f1 = __builtin_fmaf((float)p1[0], g.s16, g.c16);
+        float f2 = __builtin_fmaf((float)p2[0], g.s, g.c), f3 = __builtin_fmaf((float)p3[0], g.s16, g.c16);
+        float f4 = __builtin_fmaf((float)p0[1], g.s, g.c), f5 = __builtin_fmaf((float)p1[1], g.s16, g.c16);
+        float f6 = __builtin_fmaf((float)p2[1], g.s, g.c), f7 = __builtin_fmaf((float)p3[1], g.s16, g.c16);
+        // opaque to the compiler, which would otherwise fold each rounding
+        // back into a half-writing v_fma_mix
+        asm("" : "+v"(f0), "+v"(f1), "+v"(f2), "+v"(f3), "+v"(f4), "+v"(f5), "+v"(f6), "+v"(f7));
+        return u32x4{pack_f16x2(f0, f1), pack_f16x2(f2, f3), pack_f16x2(f4, f5), pack_f16x2(f6, f7)};
+    } else {
+        f16x2 r0, r1, r2, r3;
+        r0[0] = (_Float16)__builtin_fmaf((float)p0[0], g.s, g.c);
+        r0[1] = (_Float16)__builtin_fmaf((float)p1[0], g.s16, g.c16);
+        r1[0] = (_Float16)__builtin_fmaf((float)p2[0], g.s, g.c);
+        r1[1] = (_Float16)__builtin_fmaf((float)p3[0], g.s16, g.c16);
+        r2[0] = (_Float16)__builtin_fmaf((float)p0[1], g.s, g.c);
+        r2[1] = (_Float16)__builtin_fmaf((float)p1[1], g.s16, g.c16);
+        r3[0] = (_Float16)__builtin_fmaf((float)p2[1], g.s, g.c);
+        r3[1] = (_Float16)__builtin_fmaf((float)p3[1], g.s16, g.c16);
+        return u32x4{as_u32(r0), as_u32(r1), as_u32(r2), as_u32(r3)};
+    }
 }
 
 // ---------------------------------------------------------------- lookup-codebook table decode
