@@ -379,8 +379,8 @@ __device__ __forceinline__ void prefill_store(const PrefillRegs& R, int tid, uin
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xa + 64 * i * kPLd) = bf16x8_to_f16x8(R.x[i]);
     const AffineGroupF16 grp = affine_group_f16(bf16_bits_to_f32(R.s), bf16_bits_to_f32(R.b));
     uint16_t* dst = Bs + (tid >> 2) * kPLd + 16 * (tid & 3);
-    *reinterpret_cast<u32x4*>(dst) = affine_word_f16(R.w[0], grp, m_lo, m_hi, magic);
-    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_f16(R.w[1], grp, m_lo, m_hi, magic);
+    *reinterpret_cast<u32x4*>(dst) = affine_word_f16<true>(R.w[0], grp, m_lo, m_hi, magic);
+    *reinterpret_cast<u32x4*>(dst + 8) = affine_word_f16<true>(R.w[1], grp, m_lo, m_hi, magic);
 }
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
