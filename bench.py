@@ -47,16 +47,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once those sources change.
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "e601c6aed1502add", 36831125 + 57346),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "4514e48b8f6c877d", 101006345 + 16804101),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "4514e48b8f6c877d", 58310168 + 11774851),
-    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "4514e48b8f6c877d", 65506308 + 11826852),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "4514e48b8f6c877d", 39081236 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 128084409 + 5767200),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 13123793 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 14108815 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "336e4331960d161d", 26047919 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "336e4331960d161d", 44816620 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "e601c6aed1502add", 36831323 + 57345),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 101006903 + 16802790),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 58304352 + 11759475),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 65506677 + 11851768),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 39082395 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 128216096 + 5767200),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 13123867 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 14108894 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "336e4331960d161d", 26048065 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "336e4331960d161d", 44816409 + 176128),
 }
 
 
