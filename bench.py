@@ -45,35 +45,67 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # `bench.py --eager --calib`, each counter scaled by what it reads for a plain
 # 256 MiB copy (torch.neg on f32: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0). Each entry
 # is tied to the digest of the kernel sources it was measured on and reported
-# as null once those sources change.
+# as null once their code changes (comments and layout aside: see code_digest).
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "e601c6aed1502add", 36831323 + 57345),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 101006903 + 16802790),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 58304352 + 11759475),
-    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 65506677 + 11851768),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "f2721d82890ac6a8", 39082395 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 128216096 + 5767200),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 13123867 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "db19a06851406095", 14108894 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "336e4331960d161d", 26048065 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "336e4331960d161d", 44816409 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "7e3a5a299979dcc8", 36831323 + 57345),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "6cb8236906b0fe08", 101006903 + 16802790),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "6cb8236906b0fe08", 58304352 + 11759475),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "6cb8236906b0fe08", 65506677 + 11851768),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "6cb8236906b0fe08", 39082395 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 128216096 + 5767200),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 13123867 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 14108894 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 26048065 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 44816409 + 176128),
 }
 
 
-def traffic(name: str):
-    """Measured HBM bytes per launch of `name`, or None if its sources changed since."""
+def _code_text(src: str) -> str:
+    """C++/HIP source with comments removed and every whitespace run made one space, so a change
+    to a comment or to layout leaves it unchanged. String and character literals are kept whole."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def code_digest(paths) -> str:
+    """First 16 hex of the sha256 over the comment-free code of `paths`, in order."""
     import hashlib
+
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_text(f.read()).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic(name: str):
+    """Measured HBM bytes per launch of `name`, or None if its sources' code changed since."""
     import os
 
     if name not in TRAFFIC:
         return None
     sources, digest, nbytes = TRAFFIC[name]
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_bit_w4_amd", "csrc")
-    h = hashlib.sha256()
-    for src in sources:
-        with open(os.path.join(csrc, src), "rb") as f:
-            h.update(f.read())
-    return nbytes if h.hexdigest()[:16] == digest else None
+    return nbytes if code_digest([os.path.join(csrc, s) for s in sources]) == digest else None
 
 
 def parse():

@@ -79,8 +79,9 @@ const char* w4_version(void);
  * binary16 (round to nearest even; exact for magnitudes 2^-14 .. 65504,
  * binary16's subnormal step below) and each weight is q * scale + bias
  * rounded once to binary16 (exactly so when bias = 0 or |bias| lies within
- * about 2^-6 .. 2^15 of |scale|, as it does for bias = -zero_point * scale;
- * outside that band an f32 step can round first, by at most 2^-14 |scale|).
+ * 2^-6 .. 2^15 of |scale|, as it does for bias = -zero_point * scale;
+ * outside that band an f32 step can round first, by at most 2^-14 |scale|
+ * below it and 2^-22 |bias| above it).
  * A finite x (or weight) of magnitude 65520 or
  * more overflows binary16: the outputs of its row of x (or weight row) come
  * out as infinities or NaN, and the call adds one per affected output tile

@@ -118,9 +118,9 @@ __device__ __forceinline__ AffineGroupF16 affine_group_f16(float s, float b) {
 // 4..7) as 1024 + 16 q; a fused multiply-add then forms (1024 + q) s +
 // (b - 1024 s) or (1024 + 16 q) s/16 + (b - 64 s) in f32 and that is rounded
 // to binary16. The f32 value is q s + b exactly when b = 0 or |b| lies within
-// about 2^-6 .. 2^15 of |s| (both terms then fit f32's 24 bits), so the
-// weight is q s + b rounded once; outside that band the f32 step rounds first
-// (by at most 2^-14 |s|). F32: the eight sums round in f32 registers and
+// 2^-6 .. 2^15 of |s| (both terms then fit f32's 24 bits), so the weight is
+// q s + b rounded once; outside that band the f32 step can round first (by at
+// most 2^-14 |s| below it, 2^-22 |b| above it). F32: the eight sums round in f32 registers and
 // v_cvt_pk_f16_f32 packs them (v_fma_mix_f32 issues in about 3.4 cycles per
 // wave64 instruction, the half-writing v_fma_mix{lo,hi}_f16 in 5.9);
 // otherwise they round straight into register halves (fewer registers). Both
