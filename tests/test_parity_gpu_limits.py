@@ -4,8 +4,9 @@ The affine entry points are implemented for K and N up to 2^21: the decode GEMV,
 form (also for two rows, which past K = 8192 take it), the prefill tiles and the 64x128 kernel
 are run with K = 2^21 or N = 2^21. The lookup entry points take M up to 262,140 (4 rows per
 workgroup times the 65,535 workgroups of a grid's y dimension on the `[K, N]` vector kernels);
-that M is run on those kernels and on both matrix-core routes. Shapes past these limits are
-rejected before any launch (tests/test_abi_host.py).
+that M is run on those kernels and on both matrix-core routes. The expert-routed entry point
+groups up to 8192 experts; every route runs at that count. Shapes past these limits are rejected
+before any launch (tests/test_abi_host.py).
 """
 import numpy as np
 import pytest
@@ -15,7 +16,7 @@ import oracle
 from weight_only_bit_w4_amd import binding as B
 from weight_only_bit_w4_amd import synth
 from test_parity_gpu import (_affine_dev, _affine_scales, _assert_within, _bf16_to_f64, _lut_dev, _lut_f32_case,
-                             _t)
+                             _max_d, _moe_run, _t)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,3 +75,19 @@ def test_lut4_f32_at_the_row_limit(transpose):
     acc, _ = oracle.lut4_f32(x, packed, scales, book, M, K, N, block, bool(transpose))
     _assert_within(y.astype(np.float64), acc, K, float(np.abs(x).max()), float(np.abs(scales).max()),
                    f"limits lut4_f32 M={M} transpose={transpose}")
+
+
+# (tokens, top_k) at the most experts the grouped routes take (8192): the mat-vec route, the
+# one-launch grouped GEMM (512 routed rows) and the two-launch form (4800 routed rows, the
+# grouping kernel's per-expert counters at their largest)
+@pytest.mark.parametrize("T,top_k", [(4, 8), (64, 8), (600, 8)])
+def test_moe_at_the_expert_limit(T, top_k):
+    E, N, K = 8192, 32, 64
+    print(f"limits moe E={E} N={N} K={K} T={T} top_k={top_k}", flush=True)
+    c = synth.moe_case(E, N, K, T, top_k, seed=44)
+    c["ids"][: top_k] = np.arange(E - top_k, E, dtype=np.uint32)  # the highest expert ids are used
+    got, scratch = _moe_run(c)
+    acc, _ = oracle.moe_q4_0(c["x"], c["w"], c["ids"], T, top_k, N, K, E, c["expert_stride"])
+    _assert_within(got, acc, K, float(np.abs(c["x"]).max()), _max_d(c),
+                   f"limits moe E={E} T={T} top_k={top_k}")
+    assert scratch[:4].view(torch.int32).item() == 0
