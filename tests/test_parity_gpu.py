@@ -306,6 +306,23 @@ def test_affine_m_zero_is_noop():
     assert y.shape == (0, 32)
 
 
+@pytest.mark.parametrize("transpose", [1, 0])
+@pytest.mark.parametrize("f32", [False, True])
+def test_lut_m_zero_is_noop(f32, transpose):
+    M, K, N, block = 0, 64, 48, 16
+    c = synth.lut_case(2, K, N, seed=6, block=block)
+    if f32:
+        x = torch.empty((M, K), dtype=torch.float32, device=DEV)
+        p, s = _t(c["packed"]), _t(oracle.f16_to_f32(c["scales"]))
+        y = B.qmm_lut4_f32(x, p, s, c["book"], N, block, transpose=transpose)
+    else:
+        x = torch.empty((M, K), dtype=torch.float16, device=DEV)
+        _, p, s = _lut_dev(c)
+        y = B.qmm_lut4(x, p, s, c["book"], N, block, transpose=transpose)
+    torch.cuda.synchronize()
+    assert y.shape == (0, N)
+
+
 # ---------------------------------------------------------------- lookup codebook
 def _lut_dev(c):
     return _t(c["x"].view(np.int16), torch.float16), _t(c["packed"]), _t(c["scales"].view(np.int16), torch.float16)
