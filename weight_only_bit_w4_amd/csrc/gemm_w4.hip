@@ -326,12 +326,39 @@ __global__ __launch_bounds__(kGemmThreads) void qmm_affine4_kernel(const uint32_
 // decodes half a (weight row, group) per step (affine_word_f16). LDS rows
 // are 144 bytes (64 operands + 16 bytes), which keeps the 16-byte operand
 // reads of 16 consecutive rows conflict-free. Workgroups are assigned to
-// tiles so that the 32 workgroups one XCD runs share one x tile in that
-// XCD's L2.
+// tiles so that each XCD works on one block of tiles whose x rows and weight
+// columns its L2 serves to all of them (prefill_tile).
 constexpr int kPBM = 256, kPBN = 128, kPBK = 64;
 constexpr int kPThreads = 512;
 constexpr int kPLd = kPBK + 8;  // LDS row stride in 16-bit elements (144 bytes)
 constexpr int kPTM = 2, kPTN = 2;  // 32 x 32 accumulator tiles per wavefront
+
+// XCD-blocked tile order for a grid of tm x tn tiles (index m_tile * tn +
+// n_tile). Workgroup b runs on XCD b % 8. Each XCD takes one block of
+// (tm / pm) x (tn / pn) tiles, pm * pn = 8, with pm chosen so the blocks read
+// the fewest bytes from outside the XCD: xb per row tile (its x rows), wb per
+// column tile (its packed weights, scales and biases). Within a block, tiles
+// go row by row, so the workgroups an XCD runs at once share their x rows.
+// At M=2048, K=N=4096 (8 x 32 tiles) that is 2 x 16 tiles per XCD, 9.1 MB each
+// against 12.2 MB for one row of 32 tiles. Grids that divide no such way keep
+// a contiguous run of tiles per XCD (or the launch order).
+__device__ __forceinline__ int prefill_tile(int b, int tm, int tn, uint64_t xb, uint64_t wb) {
+    int pm = 0;
+    uint64_t best = ~0ull;
+    for (int p = 1; p <= 8; p *= 2)
+        if (tm % p == 0 && tn % (8 / p) == 0) {
+            const uint64_t bytes = (uint64_t)(tm / p) * xb + (uint64_t)(tn / (8 / p)) * wb;
+            if (bytes < best) best = bytes, pm = p;
+        }
+    const int tiles = tm * tn;
+    if (pm == 0) return tiles % 8 == 0 ? (b % 8) * (tiles / 8) + b / 8 : b;
+    const int pn = 8 / pm, bm = tm / pm, bn = tn / pn, xcd = b % 8, i = b / 8;
+    return ((xcd / pn) * bm + i / bn) * tn + (xcd % pn) * bn + i % bn;
+}
+__device__ __forceinline__ int prefill_tile(int b, int tm, int tn, int K) {
+    return prefill_tile(b, tm, tn, (uint64_t)kPBM * (uint64_t)K * 2u,
+                        (uint64_t)kPBN * ((uint64_t)K / 2u + (uint64_t)(K / 32) * 4u));
+}
 
 struct PrefillRegs {
     u32x4 x[4];       // x tile pieces i: row (tid / 8) + 64 i, 16-byte chunk tid % 8
@@ -437,11 +464,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
-    const int tiles = tiles_m * tiles_n;
-    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
-    // contiguous run of tiles (n fastest), so it shares one x tile.
-    int t = blockIdx.x;
-    if (tiles % 8 == 0) t = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+    const int t = prefill_tile(blockIdx.x, tiles_m, tiles_n, K);  // XCD-blocked order
     const int m0 = (t / tiles_n) * kPBM, n0 = (t % tiles_n) * kPBN;
     const int G = K / 32, steps = (K + kPBK - 1) / kPBK;
 
@@ -628,9 +651,7 @@ __global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tiles_m = (M + kPBM - 1) / kPBM, tiles_n = (N + kPBN - 1) / kPBN;
-    const int tiles = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    if (tiles % 8 == 0) t = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+    const int t = prefill_tile(blockIdx.x, tiles_m, tiles_n, K);  // XCD-blocked order
     const int m0 = (t / tiles_n) * kPBM, n0 = (t % tiles_n) * kPBN;
     const int G = K / 32, steps = K / kPBK;
     const int mrows = min(kPBM, M - m0), nrows = min(kPBN, N - n0);
