@@ -47,16 +47,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once their code changes (comments and layout aside: see code_digest).
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "7e3a5a299979dcc8", 36831135 + 57346),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 75864641 + 16802271),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 58303017 + 11809060),
-    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 65502231 + 11778852),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 39079455 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 128042827 + 5767200),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 13123799 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 14108819 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 26047926 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 44816785 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "7e3a5a299979dcc8", 36831141 + 57347),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 75864670 + 16802440),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 58303039 + 11808364),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 65502256 + 11782584),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 39082627 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 128225971 + 5767200),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 13123802 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 14108824 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 26047936 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 44816112 + 176128),
 }
 
 
