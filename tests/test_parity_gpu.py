@@ -298,6 +298,28 @@ def test_qmm_affine4_prefill_full_size_every_output():
     assert B.w4_range_events(reset=True) == 0
 
 
+# The prefill tiles in XCD blocks: each of the 8 XCDs takes a block of (tiles_m / pm) x (tiles_n / pn)
+# tiles, pm * pn = 8, the split that reads the fewest bytes. Each split (pm = 1, 2, 4, 8) on each
+# prefill kernel (K % 256 == 0, K % 64 == 0, and the register-staged one for K % 64 == 32), with
+# blocks of one tile and of several, and ragged last row and column tiles.
+@pytest.mark.parametrize("M,K,N", [
+    (256, 64, 1024), (512, 64, 512), (1024, 64, 256), (2048, 64, 128),   # pm = 1, 2, 4, 8: one tile per XCD
+    (200, 256, 2016),                     # pm = 1, 2 tiles per XCD, K % 256 == 0
+    (500, 64, 2016), (300, 128, 4064),    # pm = 2, ragged M and N
+    (1000, 320, 992), (1000, 256, 1984),  # pm = 4, 4 and 8 tiles per XCD
+    (1800, 192, 480), (4000, 64, 96),     # pm = 8, 2 tiles per XCD
+    (130, 160, 1024), (260, 96, 992), (1020, 480, 992), (2000, 96, 224),  # register-staged: pm = 1, 2, 4, 8
+])
+def test_qmm_affine4_prefill_xcd_blocks(M, K, N):
+    c = synth.affine_case(M, K, N, seed=M + N + K)
+    w, s, b, x = _affine_dev(c)
+    y = B.qmm_affine4(w, s, b, x)
+    torch.cuda.synchronize()
+    acc, _ = oracle.affine(c["w"], c["scales"], c["biases"], c["x"], M, K, N)
+    ms, mx = _affine_scales(c)
+    _assert_within(_bf16_to_f64(y), acc, K, mx, ms, f"prefill xcd blocks M={M} K={K} N={N}")
+
+
 def test_affine_m_zero_is_noop():
     c = synth.affine_case(2, 64, 32, seed=5)
     w, s, b, _ = _affine_dev(c)
