@@ -12,7 +12,13 @@
  * binding checks tensor shapes before calling), enqueues its kernels on
  * `stream` (a hipStream_t; NULL is
  * the default stream) and returns without synchronising; the library never
- * allocates device memory. On failure nothing is enqueued (W4_EINVAL,
+ * allocates device memory. Apart from w4_range_events (which synchronises),
+ * a call enqueues only kernel launches (qmm_id_q4_0_noalloc also one
+ * device-to-device copy), so it may be recorded into a HIP graph by stream
+ * capture and replayed: each replay rewrites every output (the range-event
+ * count of w4_range_events goes on adding up). The first call on
+ * a device looks up the library's device variables (hipGetSymbolAddress):
+ * make one call per device before capturing. On failure nothing is enqueued (W4_EINVAL,
  * W4_EUNSUPPORTED) or the launch error is reported (W4_ELAUNCH); the message
  * is available from w4_last_error() on the calling thread. There is no
  * fallback path: a status other than W4_OK means no result was produced.
