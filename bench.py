@@ -47,16 +47,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores, TFLOP/s
 # is tied to the digest of the kernel sources it was measured on and reported
 # as null once their code changes (comments and layout aside: see code_digest).
 TRAFFIC = {
-    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "7e3a5a299979dcc8", 36831141 + 57347),
-    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 75864670 + 16802440),
-    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 58303039 + 11808364),
-    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 65502256 + 11782584),
-    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 39082627 + 917504),
-    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 128225971 + 5767200),
-    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 13123802 + 45088),
-    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 14108824 + 45056),
-    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 26047936 + 176128),
-    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "3f9e9f6bb7e7723a", 44816112 + 176128),
+    "decode": (("w4mi_device.hpp", "affine_gemv.hip"), "7e3a5a299979dcc8", 36831120 + 57347),
+    "prefill": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 75864647 + 16803220),
+    "lut": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 58303006 + 11816387),
+    "lut_kn": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 65502219 + 11785032),
+    "small32": (("w4mi_device.hpp", "gemm_w4.hip"), "b5587ba7bc363947", 39082079 + 917504),
+    "moe": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 128268590 + 5767200),
+    "moe_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 13123794 + 45088),
+    "moe_swiglu_decode": (("w4mi_device.hpp", "moe_q4_0.hip"), "d873f820bff023d7", 14108816 + 45056),
+    "lut_f32_t1": (("w4mi_device.hpp", "lut_f32.hip"), "2a4765550d6e3759", 26047921 + 176128),
+    "lut_f32_t0": (("w4mi_device.hpp", "lut_f32.hip"), "2a4765550d6e3759", 32674713 + 176128),
 }
 
 

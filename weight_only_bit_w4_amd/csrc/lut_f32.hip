@@ -527,15 +527,15 @@ __global__ __launch_bounds__(kKnWaves * 64, 4) void lut4_kn8_kernel(const typena
     using IO = LutIO<H>;
     constexpr int R = 64 / D;           // rows per step; lanes that share outputs
     constexpr int CH = 16 * R;          // rows per chunk
-    constexpr int S = 32 / D;           // workgroups per 128-byte line of a row
     constexpr int NO = 8 * kF32M;       // outputs per lane in a step
     constexpr int KEEP = NO / R;        // outputs each lane keeps after the reduce-scatter
     static_assert(D == 1 || D == 2 || D == 4 || D == 8, "1, 2, 4 or 8 dwords per row");
-    // Workgroup b runs on XCD b % 8; the S groups of one line get consecutive
-    // b / 8 on the same XCD.
-    const int b = blockIdx.x;
-    const int g = S * (8 * (b / (8 * S)) + b % 8) + (b / 8) % S;
-    if (g >= groups) return;  // the whole workgroup
+    // Workgroup b runs on XCD b % 8. Each XCD takes one contiguous range of
+    // column groups, so the groups that share a 128-byte line of a code row
+    // (32 / D of them) or of a scale row (up to 32) read it through one L2,
+    // apart from the lines at the ends of a range.
+    const int b = blockIdx.x, xcd = b % 8, base = groups / 8, extra = groups % 8;
+    const int g = xcd * base + min(xcd, extra) + b / 8;  // the grid has exactly `groups` columns
     __shared__ float book_s[16];
     __shared__ __attribute__((aligned(16))) float xs[kKnWaves][CH][kF32M];
     __shared__ float red[kKnWaves][2][D * NO];
@@ -674,8 +674,7 @@ void launch_lut4_kn8(const typename LutIO<H>::X* x, const uint8_t* packed, const
                      const LutBook& b, typename LutIO<H>::Y* y, int64_t M, int64_t K, int64_t N, int32_t block,
                      hipStream_t s) {
     const int groups = (int)((N + 8 * D - 1) / (8 * D));
-    const int per = 8 * (32 / D);  // the numbering works in whole sets of 8 XCDs x S groups
-    const dim3 grid((unsigned)((groups + per - 1) / per * per), (unsigned)((M + kF32M - 1) / kF32M));
+    const dim3 grid((unsigned)groups, (unsigned)((M + kF32M - 1) / kF32M));
     hipLaunchKernelGGL((lut4_kn8_kernel<H, D>), grid, dim3(kKnWaves * 64), 0, s, x, packed, scales, b, y, (int)M,
                        (int)K, (int)N, (int)block, groups);
 }
